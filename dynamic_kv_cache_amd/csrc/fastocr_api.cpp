@@ -1,0 +1,616 @@
+// Host runtime of the FastOCR decode-step attention library: handle, scratch
+// arena, per-step/per-layer state machine, warm-up profiler finalisation and
+// kernel dispatch.  The C ABI is declared in include/fastocr.h.
+//
+// Method source: "FastOCR: Dynamic Visual Fixation via KV Cache Pruning for
+// Efficient Document Parsing", technical summary, Method / 1. Focal-Guided
+// Pruning (Focal Layer Selection, Cross-Layer Propagation) and 2. Cross-Step
+// Fixation Reuse (Implementation).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "../../include/fastocr.h"
+#include "internal.h"
+
+using namespace fastocr;
+
+namespace {
+
+enum Phase : int { PHASE_WARMUP = 0, PHASE_WARMUP_DONE = 1, PHASE_PRUNED = 2, PHASE_FULL = 3 };
+
+struct EventPair {
+  int cls;
+  hipEvent_t a, b;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+// Rows per split for a pass that visits at most `rows` rows per (sequence,
+// KV head): aim for about `target` workgroups in total, with at least one
+// 64-row pass per workgroup, and at most kMaxSplits splits.
+int plan_rows_per_split(int64_t pairs, int rows, int target, const char* env) {
+  int R = env_int(env, 0);
+  if (R <= 0) {
+    int64_t want = (pairs * (int64_t)std::max(rows, 1) + target - 1) / target;
+    R = (int)align_up((size_t)std::max<int64_t>(want, 1), kRowsPerPass);
+  } else {
+    R = (int)align_up((size_t)R, kTileRows);
+  }
+  while ((rows + R - 1) / R > kMaxSplits) R += kRowsPerPass;
+  return R;
+}
+
+}  // namespace
+
+struct fastocr_handle {
+  fastocr_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int G = 0, D = 0, n_cap = 0, n_stride = 0, k_max = 0;
+  int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
+  float scale_log2 = 0.f;
+
+  int step = 0, next_layer = 0, phase = PHASE_WARMUP;
+  bool poisoned = false;
+  std::vector<int32_t> focal;
+  std::vector<char> is_focal;
+  std::vector<double> ratios;
+
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  float4* pstat = nullptr;
+  float* po = nullptr;
+  float* logits = nullptr;
+  float2* mz = nullptr;
+  float* scores = nullptr;
+  float* warm_scores = nullptr;
+  float* text_mass = nullptr;
+  int32_t* sel = nullptr;
+  int32_t* sel_cnt = nullptr;
+  int32_t* status = nullptr;
+  int32_t* lens_shadow = nullptr;  // [B, 2] lens of the last warm-up step
+
+  bool timing = false;
+  std::vector<EventPair> events;
+  size_t ev_used = 0;
+  fastocr_timing timing_acc{};
+};
+
+namespace {
+
+int fail_hip(fastocr_handle* h, hipError_t e) {
+  if (e == hipSuccess) return FASTOCR_OK;
+  if (h) h->poisoned = true;
+  return FASTOCR_ERR_HIP;
+}
+
+// Launch helper: optional event pair around the launch for kernel timing.
+template <typename F>
+int timed(fastocr_handle* h, int cls, F&& launch) {
+  EventPair* ep = nullptr;
+  if (h->timing) {
+    if (h->ev_used == h->events.size()) {
+      EventPair np{cls, nullptr, nullptr};
+      if (hipEventCreate(&np.a) != hipSuccess || hipEventCreate(&np.b) != hipSuccess)
+        return fail_hip(h, hipErrorOutOfMemory);
+      h->events.push_back(np);
+    }
+    ep = &h->events[h->ev_used++];
+    ep->cls = cls;
+    hipError_t e = hipEventRecord(ep->a, h->stream);
+    if (e != hipSuccess) return fail_hip(h, e);
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return fail_hip(h, e);
+  if (ep) {
+    e = hipEventRecord(ep->b, h->stream);
+    if (e != hipSuccess) return fail_hip(h, e);
+  }
+  return FASTOCR_OK;
+}
+
+SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const void* v,
+                         const int32_t* lens, bool sparse) {
+  SplitParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.lens = lens;
+  p.sel = h->sel;
+  p.sel_cnt = h->sel_cnt;
+  p.logits = h->logits;
+  p.pstat = h->pstat;
+  p.po = h->po;
+  p.status = h->status;
+  p.B = h->cfg.batch;
+  p.Hq = h->cfg.num_q_heads;
+  p.Hkv = h->cfg.num_kv_heads;
+  p.S = h->cfg.max_seq_len;
+  p.n_cap = h->n_cap;
+  p.n_stride = h->n_stride;
+  p.k_stride = h->k_max;
+  p.max_splits = h->max_splits;
+  p.rows_per_split = sparse ? h->sparse_R : h->full_R;
+  p.grid_splits = sparse ? h->sparse_splits : h->full_splits;
+  p.scale_log2 = h->scale_log2;
+  return p;
+}
+
+CombineParams combine_params(fastocr_handle* h, const int32_t* lens, void* out, bool sparse) {
+  CombineParams c{};
+  c.pstat = h->pstat;
+  c.po = h->po;
+  c.lens = lens;
+  c.sel_cnt = sparse ? h->sel_cnt : nullptr;
+  c.out = out;
+  c.B = h->cfg.batch;
+  c.Hq = h->cfg.num_q_heads;
+  c.S = h->cfg.max_seq_len;
+  c.n_cap = h->n_cap;
+  c.k_stride = h->k_max;
+  c.max_splits = h->max_splits;
+  c.rows_per_split = sparse ? h->sparse_R : h->full_R;
+  c.grid_splits = sparse ? h->sparse_splits : h->full_splits;
+  c.status = h->status;
+  return c;
+}
+
+int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens) {
+  TopkParams t{};
+  t.scores = scores;
+  t.score_stride = h->n_stride;
+  t.n_cap = h->n_cap;
+  t.lens = lens;
+  t.B = h->cfg.batch;
+  t.tau = h->cfg.tau;
+  t.idx = h->sel;
+  t.idx_stride = h->k_max;
+  t.cnt = h->sel_cnt;
+  t.status = h->status;
+  return timed(h, FASTOCR_KC_TOPK, [&] { return launch_topk(t, h->stream); });
+}
+
+// Full attention of one layer; optionally records per-head text mass and
+// per-image-token scores (into `scores_dst`).
+int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
+             void* out, float* text_mass_dst, float* scores_dst) {
+  const fastocr_config& c = h->cfg;
+  const bool focal = scores_dst != nullptr;
+  SplitParams sp = split_params(h, q, k, v, lens, false);
+  int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&] {
+    return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream);
+  });
+  if (rc) return rc;
+  CombineParams cp = combine_params(h, lens, out, false);
+  cp.mz = focal ? h->mz : nullptr;
+  cp.text_mass = text_mass_dst;
+  rc = timed(h, FASTOCR_KC_COMBINE, [&] { return launch_combine(c.dtype, c.head_dim, cp, h->stream); });
+  if (rc || !focal) return rc;
+  ScoreParams sc{};
+  sc.logits = h->logits;
+  sc.mz = h->mz;
+  sc.lens = lens;
+  sc.scores = scores_dst;
+  sc.B = c.batch;
+  sc.Hq = c.num_q_heads;
+  sc.S = c.max_seq_len;
+  sc.n_cap = h->n_cap;
+  sc.n_stride = h->n_stride;
+  return timed(h, FASTOCR_KC_SCORE, [&] { return launch_score(sc, h->stream); });
+}
+
+int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
+               void* out) {
+  const fastocr_config& c = h->cfg;
+  SplitParams sp = split_params(h, q, k, v, lens, true);
+  int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&] {
+    return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream);
+  });
+  if (rc) return rc;
+  CombineParams cp = combine_params(h, lens, out, true);
+  return timed(h, FASTOCR_KC_COMBINE, [&] { return launch_combine(c.dtype, c.head_dim, cp, h->stream); });
+}
+
+void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {
+  std::vector<int> idx(L);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return ratios[a] > ratios[b]; });
+  std::vector<int> pick(idx.begin(), idx.begin() + num_focal);
+  std::sort(pick.begin(), pick.end());
+  for (int i = 0; i < num_focal; ++i) out[i] = pick[i];
+}
+
+bool config_ok(const fastocr_config& c) {
+  if (c.num_layers < 1 || c.num_kv_heads < 1 || c.num_q_heads < 1 || c.batch < 1) return false;
+  if (c.num_q_heads % c.num_kv_heads != 0) return false;
+  if (c.num_q_heads / c.num_kv_heads > 16 || c.num_q_heads > 128) return false;
+  if (c.head_dim != 64 && c.head_dim != 128) return false;
+  if (c.max_seq_len < 1) return false;
+  if (c.max_img_tokens < 0 || c.max_img_tokens > c.max_seq_len) return false;
+  if (c.min_img_tokens < 0 || c.min_img_tokens > c.max_img_tokens) return false;
+  if (c.dtype != FASTOCR_DTYPE_F32 && c.dtype != FASTOCR_DTYPE_BF16) return false;
+  if (c.mode != FASTOCR_MODE_PRUNED && c.mode != FASTOCR_MODE_FULL) return false;
+  if (!(c.tau > 0.0 && c.tau <= 1.0)) return false;
+  if (!(c.sm_scale >= 0.f) || !std::isfinite(c.sm_scale)) return false;
+  if (c.mode == FASTOCR_MODE_PRUNED) {
+    if (c.num_focal < 1 || c.num_focal > c.num_layers) return false;
+    if (c.warmup_steps < 1) return false;
+  }
+  // every cache index must fit comfortably in 64-bit byte offsets
+  const double cache_elems = (double)c.batch * c.num_kv_heads * c.max_seq_len * c.head_dim;
+  if (cache_elems > 4.0e15) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fastocr_kept_count(double tau, int32_t n_img) {
+#pragma clang fp contract(off)
+  if (!(tau > 0.0 && tau <= 1.0)) return FASTOCR_ERR_INVALID_ARG;
+  if (n_img <= 0) return 0;
+  const double prod = tau * (double)n_img;
+  const double k = std::ceil(prod - 1e-9);
+  int32_t ki = (int32_t)k;
+  return std::min(std::max(ki, 1), n_img);
+}
+
+int fastocr_choose_focal_layers(const double* ratios, int32_t num_layers, int32_t num_focal,
+                                int32_t* out) {
+  if (!ratios || !out || num_layers < 1 || num_focal < 1 || num_focal > num_layers)
+    return FASTOCR_ERR_INVALID_ARG;
+  select_focal(ratios, num_layers, num_focal, out);
+  return FASTOCR_OK;
+}
+
+const char* fastocr_error_string(int32_t code) {
+  switch (code) {
+    case FASTOCR_OK: return "ok";
+    case FASTOCR_ERR_INVALID_ARG: return "invalid argument";
+    case FASTOCR_ERR_STATE: return "call out of order for the handle state";
+    case FASTOCR_ERR_HIP: return "HIP runtime error";
+    case FASTOCR_ERR_OOM: return "device allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out) {
+  if (!cfg || !out) return FASTOCR_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!config_ok(*cfg)) return FASTOCR_ERR_INVALID_ARG;
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return FASTOCR_ERR_HIP;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FASTOCR_ERR_HIP;
+  int num_cu = 256;
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+      num_cu = prop.multiProcessorCount;
+  }
+
+  fastocr_handle* h = new (std::nothrow) fastocr_handle();
+  if (!h) return FASTOCR_ERR_OOM;
+  h->cfg = *cfg;
+  h->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  h->device = dev;
+  const fastocr_config& c = h->cfg;
+  h->G = c.num_q_heads / c.num_kv_heads;
+  h->D = c.head_dim;
+  h->n_cap = c.max_img_tokens;
+  h->n_stride = (int)align_up((size_t)std::max(c.max_img_tokens, 1), 4);
+  h->k_max = std::max(fastocr_kept_count(c.tau, c.max_img_tokens), 1);
+  const float scale = c.sm_scale > 0.f ? c.sm_scale : 1.0f / std::sqrt((float)c.head_dim);
+  h->scale_log2 = scale * 1.4426950408889634f;
+  h->phase = c.mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
+
+  const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
+  const int target = 4 * num_cu;
+  h->full_R = plan_rows_per_split(pairs, c.max_seq_len, target, "FASTOCR_FULL_ROWS");
+  h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
+  int sparse_rows = c.max_seq_len;
+  if (c.min_img_tokens > 0)
+    sparse_rows = std::min(c.max_seq_len, h->k_max + c.max_seq_len - c.min_img_tokens);
+  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, target, "FASTOCR_SPARSE_ROWS");
+  h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
+  h->max_splits = std::max(h->full_splits, h->sparse_splits);
+
+  // scratch arena
+  const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers, D = c.head_dim;
+  const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_pstat = take(B * Hq * h->max_splits * sizeof(float4));
+  const size_t o_po = take(B * Hq * h->max_splits * D * sizeof(float));
+  const size_t o_logits = take(pruned ? B * Hq * h->n_stride * sizeof(float) : 0);
+  const size_t o_mz = take(B * Hq * sizeof(float2));
+  const size_t o_scores = take(pruned ? B * h->n_stride * sizeof(float) : 0);
+  const size_t o_warm = take(pruned ? L * B * h->n_stride * sizeof(float) : 0);
+  const size_t o_tm = take(pruned ? L * (size_t)c.warmup_steps * B * Hq * sizeof(float) : 0);
+  const size_t o_sel = take(B * h->k_max * sizeof(int32_t));
+  const size_t o_cnt = take(B * sizeof(int32_t));
+  const size_t o_status = take(sizeof(int32_t));
+  const size_t o_lens = take(B * 2 * sizeof(int32_t));
+  h->arena_bytes = off;
+  hipError_t e = hipMalloc(&h->arena, h->arena_bytes);
+  if (e != hipSuccess) {
+    delete h;
+    return e == hipErrorOutOfMemory ? FASTOCR_ERR_OOM : FASTOCR_ERR_HIP;
+  }
+  char* base = static_cast<char*>(h->arena);
+  h->pstat = reinterpret_cast<float4*>(base + o_pstat);
+  h->po = reinterpret_cast<float*>(base + o_po);
+  h->logits = pruned ? reinterpret_cast<float*>(base + o_logits) : nullptr;
+  h->mz = reinterpret_cast<float2*>(base + o_mz);
+  h->scores = pruned ? reinterpret_cast<float*>(base + o_scores) : nullptr;
+  h->warm_scores = pruned ? reinterpret_cast<float*>(base + o_warm) : nullptr;
+  h->text_mass = pruned ? reinterpret_cast<float*>(base + o_tm) : nullptr;
+  h->sel = reinterpret_cast<int32_t*>(base + o_sel);
+  h->sel_cnt = reinterpret_cast<int32_t*>(base + o_cnt);
+  h->status = reinterpret_cast<int32_t*>(base + o_status);
+  h->lens_shadow = reinterpret_cast<int32_t*>(base + o_lens);
+  e = hipMemsetAsync(h->arena, 0, h->arena_bytes, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) {
+    (void)hipFree(h->arena);
+    delete h;
+    return FASTOCR_ERR_HIP;
+  }
+  h->is_focal.assign(c.num_layers, 0);
+  *out = h;
+  return FASTOCR_OK;
+}
+
+int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* lens, void* out) {
+  if (!h) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned) return FASTOCR_ERR_STATE;
+  if (!q || !k_cache || !v_cache || !lens || !out) return FASTOCR_ERR_INVALID_ARG;
+  const fastocr_config& c = h->cfg;
+  if (layer < 0 || layer >= c.num_layers) return FASTOCR_ERR_INVALID_ARG;
+  if (layer != h->next_layer) return FASTOCR_ERR_STATE;
+  if (h->phase == PHASE_WARMUP_DONE) return FASTOCR_ERR_STATE;
+
+  int rc = FASTOCR_OK;
+  const size_t BH = (size_t)c.batch * c.num_q_heads;
+  switch (h->phase) {
+    case PHASE_FULL:
+      rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr);
+      break;
+    case PHASE_WARMUP: {
+      float* tm = h->text_mass + ((size_t)layer * c.warmup_steps + h->step) * BH;
+      float* sc = (h->step == c.warmup_steps - 1)
+                      ? h->warm_scores + (size_t)layer * c.batch * h->n_stride
+                      : nullptr;
+      rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc);
+      if (!rc && sc && layer == 0) {
+        hipError_t e = hipMemcpyAsync(h->lens_shadow, lens, (size_t)c.batch * 2 * sizeof(int32_t),
+                                      hipMemcpyDeviceToDevice, h->stream);
+        if (e != hipSuccess) rc = fail_hip(h, e);
+      }
+      break;
+    }
+    case PHASE_PRUNED:
+      if (h->is_focal[layer]) {
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores);
+        if (!rc) rc = run_topk(h, h->scores, lens);
+      } else {
+        rc = run_sparse(h, q, k_cache, v_cache, lens, out);
+      }
+      break;
+    default:
+      return FASTOCR_ERR_STATE;
+  }
+  if (rc) return rc;
+  if (++h->next_layer == c.num_layers) {
+    h->next_layer = 0;
+    ++h->step;
+    if (h->phase == PHASE_WARMUP && h->step == c.warmup_steps) h->phase = PHASE_WARMUP_DONE;
+  }
+  return FASTOCR_OK;
+}
+
+int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out) {
+  if (!h || !focal_layers_out) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned || h->phase != PHASE_WARMUP_DONE) return FASTOCR_ERR_STATE;
+  const fastocr_config& c = h->cfg;
+  const size_t BH = (size_t)c.batch * c.num_q_heads;
+  const size_t per_layer = (size_t)c.warmup_steps * BH;
+  std::vector<float> tm((size_t)c.num_layers * per_layer);
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(tm.data(), h->text_mass, tm.size() * sizeof(float), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(h, e);
+  // Image-attention ratio of a layer: mean over warm-up steps, sequences and
+  // heads of the image probability mass, 1 - text mass (Focal Layer Selection).
+  h->ratios.assign(c.num_layers, 0.0);
+  for (int l = 0; l < c.num_layers; ++l) {
+    double s = 0.0;
+    for (size_t i = 0; i < per_layer; ++i) s += 1.0 - (double)tm[l * per_layer + i];
+    h->ratios[l] = s / (double)per_layer;
+  }
+  h->focal.assign(c.num_focal, 0);
+  select_focal(h->ratios.data(), c.num_layers, c.num_focal, h->focal.data());
+  h->is_focal.assign(c.num_layers, 0);
+  for (int32_t l : h->focal) h->is_focal[l] = 1;
+  // The first pruned step inherits the set picked from the last warm-up
+  // step's scores at the deepest focal layer (Cross-Step Fixation Reuse /
+  // Implementation).  The image-token counts come from the lens of the last
+  // warm-up step, copied aside when that step ran.
+  const int deepest = h->focal.back();
+  int rc = run_topk(h, h->warm_scores + (size_t)deepest * c.batch * h->n_stride, h->lens_shadow);
+  if (rc) return rc;
+  e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return fail_hip(h, e);
+  h->phase = PHASE_PRUNED;
+  std::memcpy(focal_layers_out, h->focal.data(), sizeof(int32_t) * c.num_focal);
+  return FASTOCR_OK;
+}
+
+int fastocr_destroy(fastocr_handle* h) {
+  if (!h) return FASTOCR_OK;
+  int rc = FASTOCR_OK;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) rc = FASTOCR_ERR_HIP;
+  for (auto& ep : h->events) {
+    (void)hipEventDestroy(ep.a);
+    (void)hipEventDestroy(ep.b);
+  }
+  if (h->arena && hipFree(h->arena) != hipSuccess) rc = FASTOCR_ERR_HIP;
+  delete h;
+  return rc;
+}
+
+int fastocr_get_status(fastocr_handle* h, int32_t* flags) {
+  if (!h || !flags) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned) return FASTOCR_ERR_STATE;
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess) e = hipMemcpy(flags, h->status, sizeof(int32_t), hipMemcpyDeviceToHost);
+  return fail_hip(h, e);
+}
+
+int fastocr_get_selection(fastocr_handle* h, int32_t* idx_dev, int32_t* cnt_dev) {
+  if (!h || !idx_dev || !cnt_dev) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned) return FASTOCR_ERR_STATE;
+  const size_t B = h->cfg.batch;
+  hipError_t e = hipMemcpyAsync(idx_dev, h->sel, B * h->k_max * sizeof(int32_t),
+                                hipMemcpyDeviceToDevice, h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(cnt_dev, h->sel_cnt, B * sizeof(int32_t), hipMemcpyDeviceToDevice, h->stream);
+  return fail_hip(h, e);
+}
+
+int fastocr_set_selection(fastocr_handle* h, const int32_t* idx_dev, const int32_t* cnt_dev) {
+  if (!h || !idx_dev || !cnt_dev) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned) return FASTOCR_ERR_STATE;
+  const size_t B = h->cfg.batch;
+  hipError_t e = hipMemcpyAsync(h->sel, idx_dev, B * h->k_max * sizeof(int32_t),
+                                hipMemcpyDeviceToDevice, h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->sel_cnt, cnt_dev, B * sizeof(int32_t), hipMemcpyDeviceToDevice, h->stream);
+  return fail_hip(h, e);
+}
+
+int fastocr_get_scores(fastocr_handle* h, float* scores_dev) {
+  if (!h || !scores_dev) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned || !h->scores) return FASTOCR_ERR_STATE;
+  if (h->n_cap == 0) return FASTOCR_OK;
+  hipError_t e = hipMemcpy2DAsync(scores_dev, (size_t)h->n_cap * sizeof(float), h->scores,
+                                  (size_t)h->n_stride * sizeof(float), (size_t)h->n_cap * sizeof(float),
+                                  h->cfg.batch, hipMemcpyDeviceToDevice, h->stream);
+  return fail_hip(h, e);
+}
+
+int fastocr_get_layer_ratios(fastocr_handle* h, double* ratios_host) {
+  if (!h || !ratios_host) return FASTOCR_ERR_INVALID_ARG;
+  if ((int)h->ratios.size() != h->cfg.num_layers) return FASTOCR_ERR_STATE;
+  std::memcpy(ratios_host, h->ratios.data(), sizeof(double) * h->ratios.size());
+  return FASTOCR_OK;
+}
+
+int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int32_t count) {
+  if (!h || !layers_host) return FASTOCR_ERR_INVALID_ARG;
+  const int L = h->cfg.num_layers;
+  if (count < 1 || count > L) return FASTOCR_ERR_INVALID_ARG;
+  std::vector<char> seen(L, 0);
+  for (int i = 0; i < count; ++i) {
+    const int l = layers_host[i];
+    if (l < 0 || l >= L || seen[l]) return FASTOCR_ERR_INVALID_ARG;
+    seen[l] = 1;
+  }
+  if (h->poisoned || (h->phase != PHASE_WARMUP_DONE && h->phase != PHASE_PRUNED)) return FASTOCR_ERR_STATE;
+  if (h->next_layer != 0) return FASTOCR_ERR_STATE;
+  h->focal.clear();
+  for (int l = 0; l < L; ++l)
+    if (seen[l]) h->focal.push_back(l);
+  h->is_focal = seen;
+  h->phase = PHASE_PRUNED;
+  return FASTOCR_OK;
+}
+
+int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
+  if (!h || !info) return FASTOCR_ERR_INVALID_ARG;
+  info->step = h->step;
+  info->next_layer = h->next_layer;
+  info->phase = h->phase;
+  info->k_max = h->k_max;
+  info->full_rows_per_split = h->full_R;
+  info->full_max_splits = h->full_splits;
+  info->sparse_rows_per_split = h->sparse_R;
+  info->sparse_max_splits = h->sparse_splits;
+  info->scratch_bytes = (int64_t)h->arena_bytes;
+  return FASTOCR_OK;
+}
+
+int fastocr_set_timing(fastocr_handle* h, int32_t enable) {
+  if (!h) return FASTOCR_ERR_INVALID_ARG;
+  h->timing = enable != 0;
+  return FASTOCR_OK;
+}
+
+int fastocr_get_timing(fastocr_handle* h, fastocr_timing* out) {
+  if (!h || !out) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned) return FASTOCR_ERR_STATE;
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return fail_hip(h, e);
+  for (size_t i = 0; i < h->ev_used; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->events[i].a, h->events[i].b);
+    if (e != hipSuccess) return fail_hip(h, e);
+    h->timing_acc.total_ms[h->events[i].cls] += ms;
+    h->timing_acc.launches[h->events[i].cls] += 1;
+  }
+  h->ev_used = 0;
+  *out = h->timing_acc;
+  return FASTOCR_OK;
+}
+
+int fastocr_reset_timing(fastocr_handle* h) {
+  if (!h) return FASTOCR_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) return fail_hip(h, hipErrorUnknown);
+  h->ev_used = 0;
+  h->timing_acc = fastocr_timing{};
+  return FASTOCR_OK;
+}
+
+int fastocr_select_topk(const float* scores, int32_t score_stride, const int32_t* lens,
+                        int32_t batch, double tau, int32_t* idx_out, int32_t idx_stride,
+                        int32_t* cnt_out, void* hip_stream) {
+  if (!scores || !lens || !idx_out || !cnt_out) return FASTOCR_ERR_INVALID_ARG;
+  if (score_stride < 1 || batch < 1 || idx_stride < 1) return FASTOCR_ERR_INVALID_ARG;
+  if (!(tau > 0.0 && tau <= 1.0)) return FASTOCR_ERR_INVALID_ARG;
+  TopkParams t{};
+  t.scores = scores;
+  t.score_stride = score_stride;
+  t.n_cap = score_stride;
+  t.lens = lens;
+  t.B = batch;
+  t.tau = tau;
+  t.idx = idx_out;
+  t.idx_stride = idx_stride;
+  t.cnt = cnt_out;
+  t.status = nullptr;
+  hipError_t e = launch_topk(t, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FASTOCR_OK : FASTOCR_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+/*
+ * fastocr.h -- C ABI of the MI355X (gfx950) decode-step attention library for
+ * FastOCR's Dynamic Visual Fixation.
+ *
+ * Source of the method: "FastOCR: Dynamic Visual Fixation via KV Cache Pruning
+ * for Efficient Document Parsing" -- the technical summary (sections "Method",
+ * "1. Focal-Guided Pruning" with "Focal Layer Selection" and "Cross-Layer
+ * Propagation", "2. Cross-Step Fixation Reuse" with "Mechanism" and
+ * "Implementation") and the paper's abstract.
+ *
+ * The library replaces the per-layer decode-attention call of a decoder.  The
+ * caller keeps the full KV cache; the library never writes it (nothing is
+ * evicted: Method).  Per decode step and layer it runs one of:
+ *   - full attention (warm-up steps, focal layers, and the FULL baseline mode),
+ *   - full attention + head-summed image-token scores + top-k(tau) on focal
+ *     layers (Cross-Layer Propagation),
+ *   - attention over the kept image tokens plus every text row on non-focal
+ *     layers (Cross-Layer Propagation),
+ * and carries the deepest focal layer's set into the next step on the device
+ * (Cross-Step Fixation Reuse / Implementation).  A w-step warm-up picks the
+ * focal layers from per-layer image-attention ratio (Focal Layer Selection).
+ *
+ * Conventions for every entry point:
+ *   - Return value: FASTOCR_OK (0) or a negative FASTOCR_ERR_* code.  Nothing
+ *     throws across the ABI and nothing aborts.
+ *   - "device" pointers are HIP device memory on the handle's device; "host"
+ *     pointers are ordinary host memory.  The caller owns every pointer it
+ *     passes; the library keeps none of them past the call (kernels read them
+ *     asynchronously on the handle's stream, so they must stay valid until
+ *     that stream has passed the work).
+ *   - Tensors are dense, row-major (last index fastest), 16-byte aligned.
+ *   - The handle owns its scratch memory (allocated in fastocr_create; no
+ *     allocation happens in fastocr_attend).  One handle = one stream; a
+ *     handle is not thread-safe.
+ *   - After FASTOCR_ERR_HIP the handle is poisoned: every later call except
+ *     fastocr_destroy returns FASTOCR_ERR_STATE.
+ */
+#ifndef FASTOCR_H
+#define FASTOCR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define FASTOCR_OK 0
+#define FASTOCR_ERR_INVALID_ARG (-1) /* null pointer, bad shape, tau out of range, layer out of [0,L) */
+#define FASTOCR_ERR_STATE (-2)       /* call out of order for the handle's state machine */
+#define FASTOCR_ERR_HIP (-3)         /* HIP runtime failure (no device, launch error, ...) */
+#define FASTOCR_ERR_OOM (-4)         /* scratch allocation failed */
+
+/* ---- element types of q, k_cache, v_cache and out ------------------------ */
+#define FASTOCR_DTYPE_F32 0
+#define FASTOCR_DTYPE_BF16 1
+
+/* ---- modes --------------------------------------------------------------- */
+#define FASTOCR_MODE_PRUNED 0 /* warm-up, then focal/non-focal pruning (the method) */
+#define FASTOCR_MODE_FULL 1   /* full attention on every layer (unpruned baseline) */
+
+/* ---- device status flags (fastocr_get_status) ---------------------------- */
+#define FASTOCR_FLAG_LENS_CLAMPED 1 /* a lens entry was out of range and was clamped */
+#define FASTOCR_FLAG_INDEX_CLAMPED 2 /* a selected index was out of range and was clamped */
+#define FASTOCR_FLAG_ROWS_TRUNCATED 4 /* a sequence had fewer image tokens than min_img_tokens;
+                                        its sparse rows beyond the launch were not attended */
+
+/* ---- kernel classes timed by fastocr_get_timing -------------------------- */
+#define FASTOCR_KC_FULL_SPLIT 0   /* split-K full attention (warm-up, FULL mode) */
+#define FASTOCR_KC_FOCAL_SPLIT 1  /* split-K full attention with image-logit export */
+#define FASTOCR_KC_SPARSE_SPLIT 2 /* split-K attention over gathered kept rows */
+#define FASTOCR_KC_COMBINE 3      /* split combine (+ image mass during warm-up) */
+#define FASTOCR_KC_SCORE 4        /* head-summed image-token scores */
+#define FASTOCR_KC_TOPK 5         /* radix top-k selection */
+#define FASTOCR_KC_COUNT 6
+
+typedef struct fastocr_config {
+  double tau;             /* kept ratio of image tokens, 0 < tau <= 1 */
+  float sm_scale;         /* logit scale; 0 selects 1/sqrt(head_dim) */
+  int32_t num_layers;     /* L >= 1 */
+  int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads, Hq/Hkv <= 16, Hq <= 128 */
+  int32_t num_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t batch;          /* B >= 1 sequences */
+  int32_t max_seq_len;    /* S: row stride of the KV cache (capacity per sequence) */
+  int32_t max_img_tokens; /* upper bound on image tokens per sequence (<= S) */
+  int32_t min_img_tokens; /* lower bound on image tokens per sequence, 0 if unknown;
+                             only used to size the sparse launch */
+  int32_t dtype;          /* FASTOCR_DTYPE_* */
+  int32_t num_focal;      /* |C|, 1 <= |C| <= L */
+  int32_t warmup_steps;   /* w >= 1 */
+  int32_t mode;           /* FASTOCR_MODE_* */
+} fastocr_config;
+
+typedef struct fastocr_info {
+  int32_t step;           /* decode steps completed */
+  int32_t next_layer;     /* layer the next fastocr_attend must name */
+  int32_t phase;          /* 0 warm-up, 1 warm-up done (profile next), 2 pruned, 3 full */
+  int32_t k_max;          /* capacity of the kept-set buffer per sequence */
+  int32_t full_rows_per_split;
+  int32_t full_max_splits;
+  int32_t sparse_rows_per_split;
+  int32_t sparse_max_splits;
+  int64_t scratch_bytes;  /* device bytes owned by the handle */
+} fastocr_info;
+
+typedef struct fastocr_timing {
+  double total_ms[FASTOCR_KC_COUNT]; /* summed kernel time per class (HIP events) */
+  int64_t launches[FASTOCR_KC_COUNT];
+} fastocr_timing;
+
+typedef struct fastocr_handle fastocr_handle;
+
+/* fastocr_create: validate cfg, allocate the handle's scratch on the current
+ * HIP device and bind the handle to hip_stream (a hipStream_t; NULL = the
+ * null stream).  On success *out receives the handle.  Errors:
+ * INVALID_ARG (cfg or out null, a field out of range), HIP (no device or
+ * runtime failure), OOM (scratch allocation failed). */
+int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out);
+
+/* fastocr_attend: decode attention of one layer at the current step
+ * (Method / Focal-Guided Pruning / Cross-Layer Propagation; Cross-Step
+ * Fixation Reuse / Implementation).
+ *   layer    0..L-1; each step calls every layer once, in order; the step
+ *            advances after layer L-1.
+ *   q        device [B, Hq, d] of dtype; query of the current token.
+ *   k_cache  device [B, Hkv, S, d] of dtype; keys of this layer (read only).
+ *   v_cache  device [B, Hkv, S, d] of dtype; values of this layer (read only).
+ *   lens     device int32 [B, 2]: (n_img_b, len_b).  Image tokens occupy rows
+ *            [0, n_img_b), prompt and generated tokens [n_img_b, len_b); the
+ *            current token's key/value is already at row len_b - 1.  n_img_b
+ *            must not change over the handle's life.  Out-of-range entries
+ *            are clamped on the device and latch FASTOCR_FLAG_LENS_CLAMPED.
+ *   out      device [B, Hq, d] of dtype; attention output.
+ * Query head h reads KV head h / (Hq / Hkv).  Which computation runs:
+ *   FULL mode: full attention.
+ *   PRUNED mode, step < w: full attention; records each head's image mass
+ *            and, at step w-1, every layer's image-token scores.
+ *   PRUNED mode, step >= w, layer in C: full attention, then per sequence the
+ *            head-summed attention probability of every image token, then the
+ *            k_b = clamp(ceil(tau*n_img_b - 1e-9), 1, n_img_b) highest
+ *            (ties to the lower index) replace the kept set.
+ *   PRUNED mode, step >= w, layer not in C: attention over the kept set plus
+ *            rows [n_img_b, len_b).
+ * Asynchronous: enqueues on the handle's stream and returns.  Errors:
+ * INVALID_ARG (null pointer, layer out of range), STATE (layer out of order,
+ * step >= w before fastocr_profile_warmup, poisoned handle), HIP. */
+int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* lens, void* out);
+
+/* fastocr_profile_warmup: after exactly w completed warm-up steps, pick the
+ * focal layers (Focal Layer Selection): the |C| layers with the largest mean
+ * image-attention mass over heads, sequences and warm-up steps (ties to the
+ * lower layer), written ascending to focal_layers_out (host, |C| entries).
+ * Initialises the kept set from step w-1's scores at the deepest focal layer
+ * and switches the handle to pruned steps.  Synchronises the stream.
+ * Errors: INVALID_ARG (null), STATE (not exactly after the warm-up), HIP. */
+int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out);
+
+/* fastocr_destroy: synchronise the stream and free the handle's scratch.
+ * NULL is accepted.  Returns HIP if the final synchronisation failed (the
+ * memory is released regardless). */
+int fastocr_destroy(fastocr_handle* h);
+
+/* ---- inspection and conditioning (test and measurement harness) ---------- */
+
+/* Synchronises; copies the device status flags (FASTOCR_FLAG_*) to *flags. */
+int fastocr_get_status(fastocr_handle* h, int32_t* flags);
+
+/* Enqueues device-to-device copies of the current kept set: idx_dev int32
+ * [B, k_max] (ascending, first cnt entries valid) and cnt_dev int32 [B]. */
+int fastocr_get_selection(fastocr_handle* h, int32_t* idx_dev, int32_t* cnt_dev);
+
+/* Enqueues a device-to-device copy of the last focal layer's image-token
+ * scores, float [B, max_img_tokens] (entries >= n_img_b are unspecified). */
+int fastocr_get_scores(fastocr_handle* h, float* scores_dev);
+
+/* After fastocr_profile_warmup: the L per-layer mean image-attention ratios
+ * (host double [L]). */
+int fastocr_get_layer_ratios(fastocr_handle* h, double* ratios_host);
+
+/* Replace the focal set C (host int32 [count], distinct, in [0, L)); switches
+ * a handle whose warm-up is complete to pruned steps without profiling. */
+int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int32_t count);
+
+/* Enqueues device-to-device copies into the kept set (same layout as
+ * fastocr_get_selection).  Indices >= n_img_b are clamped by the kernels and
+ * latch FASTOCR_FLAG_INDEX_CLAMPED. */
+int fastocr_set_selection(fastocr_handle* h, const int32_t* idx_dev, const int32_t* cnt_dev);
+
+int fastocr_get_info(fastocr_handle* h, fastocr_info* info);
+
+/* Kernel timing with HIP events on the handle's stream: enable != 0 records an
+ * event pair around every launch; fastocr_get_timing synchronises and returns
+ * the per-class totals since the last reset; fastocr_reset_timing clears them. */
+int fastocr_set_timing(fastocr_handle* h, int32_t enable);
+int fastocr_get_timing(fastocr_handle* h, fastocr_timing* out);
+int fastocr_reset_timing(fastocr_handle* h);
+
+/* ---- standalone operations ------------------------------------------------ */
+
+/* Top-k selection (Cross-Layer Propagation: top-attended image tokens at kept
+ * ratio tau) on caller buffers.  scores: device float [B, score_stride],
+ * non-negative; lens: device int32 [B, 2] (n_img_b read, clamped to
+ * score_stride); idx_out: device int32 [B, idx_stride] receives the k_b
+ * indices ascending (k_b as in fastocr_attend, and at most idx_stride);
+ * cnt_out: device int32 [B] receives k_b.  Ties go to the lower index.
+ * hip_stream: hipStream_t.  Asynchronous.  Errors: INVALID_ARG, HIP. */
+int fastocr_select_topk(const float* scores, int32_t score_stride, const int32_t* lens,
+                        int32_t batch, double tau, int32_t* idx_out, int32_t idx_stride,
+                        int32_t* cnt_out, void* hip_stream);
+
+/* Host helpers (no device use). */
+/* k = clamp(ceil(tau*n - 1e-9), 1, n) for n > 0; 0 for n <= 0; negative
+ * FASTOCR_ERR_INVALID_ARG if tau is outside (0, 1]. */
+int32_t fastocr_kept_count(double tau, int32_t n_img);
+
+/* Focal layers from per-layer ratios (host double [num_layers]): the
+ * num_focal largest, ties to the lower layer, ascending into out (host int32
+ * [num_focal]). */
+int fastocr_choose_focal_layers(const double* ratios, int32_t num_layers, int32_t num_focal,
+                                int32_t* out);
+
+/* Static text for a status code. */
+const char* fastocr_error_string(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASTOCR_H */

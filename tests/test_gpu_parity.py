@@ -1,0 +1,243 @@
+"""GPU parity of the HIP library against the CPU oracle (through the C ABI)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_kv_cache_amd as fo
+from oracle import full_attention, kept_count, select_top, sparse_attention
+from workload import get_workload
+
+from gpu_harness import Checker, check_out, check_set, log, make_config, run, upload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---------------------------------------------------------------------------
+# single-kernel checks
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name,steps", [("tiny-fp32", 6), ("7b-b1", 3)])
+def test_full_mode_matches_oracle(name, steps):
+    up = upload(get_workload(name), steps=steps)
+    h = fo.fastocr_create(make_config(up, mode="full"))
+    rec = run(up, h, steps)
+    assert rec.status == 0
+    scale = 1 / math.sqrt(up.wl.head_dim)
+    worst = 0.0
+    for t in range(steps):
+        lens = up.st.lens(t)
+        for l in range(up.wl.num_layers):
+            K, V = up.kv64(l)
+            for b in range(up.wl.batch):
+                out, _ = full_attention(up.q[l][t][b].astype(np.float64), K[b], V[b],
+                                        int(lens[b, 1]), scale)
+                worst = max(worst, check_out(rec.outs[t, l, b], out, up.wl.dtype, f"t={t} l={l}"))
+    log(f"[full] {name}: worst max-abs {worst:.3e}")
+
+
+def _topk_case(rng, B, n_cap, tau):
+    scores = np.zeros((B, n_cap), dtype=np.float32)
+    ns = []
+    for b in range(B):
+        n = [0, 1, 7, n_cap, n_cap // 3, 1000, 64, 65][b % 8]
+        n = min(n, n_cap)
+        ns.append(n)
+        kind = b % 3
+        if kind == 0:  # continuous
+            scores[b, :n] = rng.random(n).astype(np.float32) * 3
+        elif kind == 1:  # heavy ties
+            scores[b, :n] = (rng.integers(0, 5, n) / 4).astype(np.float32)
+        else:  # all equal, zeros mixed in
+            scores[b, :n] = np.float32(0.25)
+            scores[b, : n // 2] = 0.0
+    lens = np.stack([np.array(ns), np.array(ns) + 3], axis=1).astype(np.int32)
+    return scores, lens
+
+
+@pytest.mark.parametrize("tau", [0.02, 0.05, 0.1, 0.5, 1.0])
+@pytest.mark.parametrize("n_cap", [64, 6400, 16384])
+def test_topk_bit_exact(tau, n_cap):
+    rng = np.random.default_rng(int(tau * 1000) + n_cap)
+    B = 8
+    scores, lens = _topk_case(rng, B, n_cap, tau)
+    k_stride = max(kept_count(tau, n_cap), 1)
+    s_d = torch.from_numpy(scores).to(DEV)
+    l_d = torch.from_numpy(lens).to(DEV)
+    idx = torch.full((B, k_stride), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    fo.fastocr_select_topk(s_d, l_d, tau, idx, cnt)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        n = int(lens[b, 0])
+        k = kept_count(tau, n)
+        assert cnt[b] == k
+        want = select_top(scores[b, :n].astype(np.float64), k)
+        np.testing.assert_array_equal(idx[b, :k], want, err_msg=f"b={b} n={n} k={k}")
+
+
+def test_sparse_conditioned_on_injected_sets():
+    up = upload(get_workload("7b-b1").with_overrides(num_layers=3, warmup_steps=1, num_focal=1),
+                steps=3)
+    h = fo.fastocr_create(make_config(up))
+    wl = up.wl
+    for l in range(wl.num_layers):  # one warm-up step
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
+        fo.fastocr_attend(h, l, up.Qd[l][0], up.Kd[l], up.Vd[l], up.lens[0], out)
+    fo.fastocr_set_focal_layers(h, [2])
+    k_max = fo.fastocr_get_info(h)["k_max"]
+    rng = np.random.default_rng(5)
+    n = int(up.st.n_img[0])
+    scale = 1 / math.sqrt(wl.head_dim)
+    for t, k in [(1, k_max), (2, 17)]:
+        sel = np.zeros((1, k_max), dtype=np.int32)
+        chosen = np.sort(rng.choice(n, size=k, replace=False)).astype(np.int32)
+        sel[0, :k] = chosen
+        fo.fastocr_set_selection(h, torch.from_numpy(sel).to(DEV),
+                                 torch.tensor([k], dtype=torch.int32, device=DEV))
+        outs = []
+        for l in range(wl.num_layers):
+            out = torch.empty((1, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out)
+            outs.append(out)
+        torch.cuda.synchronize()
+        length = int(up.st.lens(t)[0, 1])
+        for l in range(2):  # layers before the focal layer use the injected set
+            K, V = up.kv64(l)
+            want = sparse_attention(up.q[l][t][0].astype(np.float64), K[0], V[0], chosen, n, length,
+                                    scale)
+            check_out(outs[l].float().cpu().numpy()[0], want, "bf16", f"sparse t={t} l={l}")
+    assert fo.fastocr_get_status(h) == 0
+
+
+def test_tau_one_sparse_equals_full():
+    wl = get_workload("tiny-fp32").with_overrides(tau=1.0)
+    up = upload(wl, steps=7)
+    rec = run(up, fo.fastocr_create(make_config(up)), 7)
+    full = run(up, fo.fastocr_create(make_config(up, mode="full")), 7)
+    np.testing.assert_allclose(rec.outs, full.outs, rtol=0, atol=1e-5)
+
+
+def test_lens_out_of_range_sets_flag():
+    up = upload(get_workload("tiny-fp32"), steps=1)
+    h = fo.fastocr_create(make_config(up, mode="full"))
+    bad = up.lens[0].clone()
+    bad[0, 1] = up.st.max_seq_len + 5
+    out = torch.empty((1, up.wl.num_q_heads, up.wl.head_dim), dtype=up.io_dtype, device=DEV)
+    fo.fastocr_attend(h, 0, up.Qd[0][0], up.Kd[0], up.Vd[0], bad, out)
+    assert fo.fastocr_get_status(h) & fo.FLAG_LENS_CLAMPED
+
+
+def test_state_machine_errors():
+    up = upload(get_workload("tiny-fp32"), steps=5)
+    wl = up.wl
+    h = fo.fastocr_create(make_config(up))
+    out = torch.empty((1, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_attend(h, 1, up.Qd[1][0], up.Kd[1], up.Vd[1], up.lens[0], out)
+    assert e.value.code == fo.ERR_STATE
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_profile_warmup(h)
+    assert e.value.code == fo.ERR_STATE
+    for t in range(wl.warmup_steps):
+        for l in range(wl.num_layers):
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out)
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_attend(h, 0, up.Qd[0][4], up.Kd[0], up.Vd[0], up.lens[4], out)
+    assert e.value.code == fo.ERR_STATE
+    assert len(fo.fastocr_profile_warmup(h)) == wl.num_focal
+    fo.fastocr_attend(h, 0, up.Qd[0][4], up.Kd[0], up.Vd[0], up.lens[4], out)
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_attend(h, 0, up.Qd[0][4], up.Kd[0], up.Vd[0], up.lens[4], out)
+    assert e.value.code == fo.ERR_STATE
+
+
+# ---------------------------------------------------------------------------
+# whole decode trajectories
+# ---------------------------------------------------------------------------
+
+
+def test_trajectory_tiny_all_steps():
+    wl = get_workload("tiny-fp32")
+    up = upload(wl)
+    rec = run(up, fo.fastocr_create(make_config(up)), wl.steps)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, wl.steps):
+        chk.pruned_step(t)
+    log(f"[tiny] focal {rec.focal}, worst out {chk.worst_out:.2e}, "
+        f"mean Jaccard {np.mean(chk.jaccard):.3f}")
+
+
+def test_trajectory_ragged_small():
+    wl = get_workload("7b-b16-ragged").with_overrides(
+        batch=4, num_layers=6, focal_band=(2, 3), num_focal=2, warmup_steps=3,
+        n_img_range=(100, 700), n_prompt=(5, 40))
+    up = upload(wl, steps=12)
+    rec = run(up, fo.fastocr_create(make_config(up)), 12)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 12):
+        chk.pruned_step(t)
+    log(f"[ragged] n={up.st.n_img.tolist()} focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
+def test_trajectory_layer0_focal():
+    # Layer 0 is forced focal: the warm start is never used for attention.
+    wl = get_workload("tiny-fp32").with_overrides(planted_layers=(0, 2))
+    up = upload(wl)
+    rec = run(up, fo.fastocr_create(make_config(up)), wl.steps)
+    chk = Checker(up, rec)
+    chk.warmup()
+    assert rec.focal[0] == 0
+    for t in range(wl.warmup_steps, wl.steps):
+        chk.pruned_step(t)
+
+
+def test_deterministic_replay():
+    wl = get_workload("7b-b1").with_overrides(num_layers=6, focal_band=(2, 3), num_focal=2,
+                                             warmup_steps=2)
+    up = upload(wl, steps=10)
+    a = run(up, fo.fastocr_create(make_config(up)), 10)
+    b = run(up, fo.fastocr_create(make_config(up)), 10)
+    np.testing.assert_array_equal(a.outs, b.outs)
+    np.testing.assert_array_equal(a.sets, b.sets)
+    np.testing.assert_array_equal(a.scores, b.scores)
+    assert a.focal == b.focal and a.ratios == b.ratios
+
+
+@pytest.fixture(scope="module")
+def traj_7b():
+    wl = get_workload("7b-b1")
+    up = upload(wl)
+    rec = run(up, fo.fastocr_create(make_config(up)), wl.steps)
+    chk = Checker(up, rec)
+    chk.warmup()
+    log(f"[7b] focal {rec.focal} ratios {np.round(rec.ratios, 6).tolist()}")
+    return up, rec, chk
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_trajectory_7b_all_steps(traj_7b, chunk):
+    up, rec, chk = traj_7b
+    assert rec.status == 0
+    w, T = up.wl.warmup_steps, up.wl.steps
+    edges = np.linspace(w, T, 5).astype(int)
+    for t in range(edges[chunk], edges[chunk + 1]):
+        chk.pruned_step(t)
+    log(f"[7b] steps {edges[chunk]}..{edges[chunk + 1] - 1} ok; worst out {chk.worst_out:.3e}, "
+        f"mean Jaccard {np.mean(chk.jaccard):.3f}")
