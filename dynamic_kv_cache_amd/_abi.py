@@ -26,11 +26,10 @@ FLAG_ROWS_TRUNCATED = 4
 KC_FULL_SPLIT = 0
 KC_FOCAL_SPLIT = 1
 KC_SPARSE_SPLIT = 2
-KC_COMBINE = 3
-KC_SCORE = 4
-KC_TOPK = 5
-KC_COUNT = 6
-KC_NAMES = ("full_split", "focal_split", "sparse_split", "combine", "score", "topk")
+KC_MERGE = 3
+KC_TOPK = 4
+KC_COUNT = 5
+KC_NAMES = ("full_split", "focal_split", "sparse_split", "merge", "topk")
 
 
 class Config(ctypes.Structure):
@@ -62,6 +61,8 @@ class Info(ctypes.Structure):
         ("full_max_splits", c_int32),
         ("sparse_rows_per_split", c_int32),
         ("sparse_max_splits", c_int32),
+        ("sparse_direct", c_int32),
+        ("reserved", c_int32),
         ("scratch_bytes", c_int64),
     ]
 

@@ -40,17 +40,22 @@ int env_int(const char* name, int dflt) {
 }
 
 // Rows per split for a pass that visits at most `rows` rows per (sequence,
-// KV head): aim for about `target` workgroups in total, with at least one
-// 64-row pass per workgroup, and at most kMaxSplits splits.
+// KV head).  A split is 128, 256 or 512 rows (1, 2 or 4 tiles per wave in
+// one round), or whole rounds beyond that: the smallest size that still
+// gives about `target` workgroups, so small batches spread over many CUs
+// (one CU streams only ~60 GB/s) and large ones read long runs per
+// workgroup.  At most kMaxMergeSplits splits.
 int plan_rows_per_split(int64_t pairs, int rows, int target, const char* env) {
   int R = env_int(env, 0);
   if (R <= 0) {
-    int64_t want = (pairs * (int64_t)std::max(rows, 1) + target - 1) / target;
-    R = (int)align_up((size_t)std::max<int64_t>(want, 1), kRowsPerPass);
+    const int64_t want = (pairs * (int64_t)std::max(rows, 1) + target - 1) / target;
+    R = 128;
+    while (R < want && R < kRowsPerRound) R *= 2;
+    if (want > kRowsPerRound) R = (int)align_up((size_t)want, kRowsPerRound);
   } else {
     R = (int)align_up((size_t)R, kTileRows);
   }
-  while ((rows + R - 1) / R > kMaxSplits) R += kRowsPerPass;
+  while ((rows + R - 1) / R > kMaxMergeSplits) R += kRowsPerRound;
   return R;
 }
 
@@ -124,8 +129,9 @@ int timed(fastocr_handle* h, int cls, F&& launch) {
 }
 
 SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const void* v,
-                         const int32_t* lens, bool sparse) {
+                         const int32_t* lens, void* out, bool sparse) {
   SplitParams p{};
+  p.out = out;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -150,25 +156,6 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   return p;
 }
 
-CombineParams combine_params(fastocr_handle* h, const int32_t* lens, void* out, bool sparse) {
-  CombineParams c{};
-  c.pstat = h->pstat;
-  c.po = h->po;
-  c.lens = lens;
-  c.sel_cnt = sparse ? h->sel_cnt : nullptr;
-  c.out = out;
-  c.B = h->cfg.batch;
-  c.Hq = h->cfg.num_q_heads;
-  c.S = h->cfg.max_seq_len;
-  c.n_cap = h->n_cap;
-  c.k_stride = h->k_max;
-  c.max_splits = h->max_splits;
-  c.rows_per_split = sparse ? h->sparse_R : h->full_R;
-  c.grid_splits = sparse ? h->sparse_splits : h->full_splits;
-  c.status = h->status;
-  return c;
-}
-
 int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens) {
   TopkParams t{};
   t.scores = scores;
@@ -184,45 +171,67 @@ int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens) {
   return timed(h, FASTOCR_KC_TOPK, [&] { return launch_topk(t, h->stream); });
 }
 
-// Full attention of one layer; optionally records per-head text mass and
-// per-image-token scores (into `scores_dst`).
+MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool sparse) {
+  const fastocr_config& c = h->cfg;
+  MergeParams m{};
+  m.pstat = h->pstat;
+  m.po = h->po;
+  m.lens = lens;
+  m.sel_cnt = sparse ? h->sel_cnt : nullptr;
+  m.out = out;
+  m.status = h->status;
+  m.B = c.batch;
+  m.Hq = c.num_q_heads;
+  m.S = c.max_seq_len;
+  m.n_cap = h->n_cap;
+  m.k_stride = h->k_max;
+  m.max_splits = h->max_splits;
+  m.rows_per_split = sparse ? h->sparse_R : h->full_R;
+  m.grid_splits = sparse ? h->sparse_splits : h->full_splits;
+  m.direct = sparse ? 1 : 0;
+  m.n_stride = h->n_stride;
+  return m;
+}
+
+// Full attention of one layer: split pass, then the merge (and optionally
+// each head's text mass and, with `scores_dst`, the image-token scores),
+// then with `topk` the selection of the kept set from those scores.
 int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
-             void* out, float* text_mass_dst, float* scores_dst) {
+             void* out, float* text_mass_dst, float* scores_dst, bool topk) {
   const fastocr_config& c = h->cfg;
   const bool focal = scores_dst != nullptr;
-  SplitParams sp = split_params(h, q, k, v, lens, false);
+  SplitParams sp = split_params(h, q, k, v, lens, out, false);
+  sp.direct = 0;
   int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&] {
     return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream);
   });
   if (rc) return rc;
-  CombineParams cp = combine_params(h, lens, out, false);
-  cp.mz = focal ? h->mz : nullptr;
-  cp.text_mass = text_mass_dst;
-  rc = timed(h, FASTOCR_KC_COMBINE, [&] { return launch_combine(c.dtype, c.head_dim, cp, h->stream); });
-  if (rc || !focal) return rc;
-  ScoreParams sc{};
-  sc.logits = h->logits;
-  sc.mz = h->mz;
-  sc.lens = lens;
-  sc.scores = scores_dst;
-  sc.B = c.batch;
-  sc.Hq = c.num_q_heads;
-  sc.S = c.max_seq_len;
-  sc.n_cap = h->n_cap;
-  sc.n_stride = h->n_stride;
-  return timed(h, FASTOCR_KC_SCORE, [&] { return launch_score(sc, h->stream); });
+  MergeParams mp = merge_params(h, lens, out, false);
+  mp.text_mass = text_mass_dst;
+  if (focal) {
+    mp.logits = h->logits;
+    mp.scores = scores_dst;
+    mp.score_blocks = (h->n_stride + kMergeThreads - 1) / kMergeThreads;
+  }
+  rc = timed(h, FASTOCR_KC_MERGE, [&] { return launch_merge(c.dtype, c.head_dim, mp, h->stream); });
+  if (rc || !topk) return rc;
+  return run_topk(h, scores_dst, lens);
 }
 
+// Non-focal layer: attention over the kept image rows and every text row.
+// Sequences whose rows fit one split are finished by the split kernel; the
+// merge runs only when some sequence can span several splits.
 int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
                void* out) {
   const fastocr_config& c = h->cfg;
-  SplitParams sp = split_params(h, q, k, v, lens, true);
+  SplitParams sp = split_params(h, q, k, v, lens, out, true);
+  sp.direct = 1;
   int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&] {
     return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream);
   });
-  if (rc) return rc;
-  CombineParams cp = combine_params(h, lens, out, true);
-  return timed(h, FASTOCR_KC_COMBINE, [&] { return launch_combine(c.dtype, c.head_dim, cp, h->stream); });
+  if (rc || h->sparse_splits <= 1) return rc;
+  MergeParams mp = merge_params(h, lens, out, true);
+  return timed(h, FASTOCR_KC_MERGE, [&] { return launch_merge(c.dtype, c.head_dim, mp, h->stream); });
 }
 
 void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {
@@ -321,7 +330,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->phase = c.mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
 
   const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
-  const int target = 4 * num_cu;
+  const int target = 2 * num_cu;
   h->full_R = plan_rows_per_split(pairs, c.max_seq_len, target, "FASTOCR_FULL_ROWS");
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
   int sparse_rows = c.max_seq_len;
@@ -395,14 +404,14 @@ int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* 
   const size_t BH = (size_t)c.batch * c.num_q_heads;
   switch (h->phase) {
     case PHASE_FULL:
-      rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr);
+      rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
       break;
     case PHASE_WARMUP: {
       float* tm = h->text_mass + ((size_t)layer * c.warmup_steps + h->step) * BH;
       float* sc = (h->step == c.warmup_steps - 1)
                       ? h->warm_scores + (size_t)layer * c.batch * h->n_stride
                       : nullptr;
-      rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc);
+      rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc, false);
       if (!rc && sc && layer == 0) {
         hipError_t e = hipMemcpyAsync(h->lens_shadow, lens, (size_t)c.batch * 2 * sizeof(int32_t),
                                       hipMemcpyDeviceToDevice, h->stream);
@@ -412,8 +421,7 @@ int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* 
     }
     case PHASE_PRUNED:
       if (h->is_focal[layer]) {
-        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores);
-        if (!rc) rc = run_topk(h, h->scores, lens);
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores, true);
       } else {
         rc = run_sparse(h, q, k_cache, v_cache, lens, out);
       }
@@ -557,6 +565,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->full_max_splits = h->full_splits;
   info->sparse_rows_per_split = h->sparse_R;
   info->sparse_max_splits = h->sparse_splits;
+  info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;
 }

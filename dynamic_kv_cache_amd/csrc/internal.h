@@ -14,13 +14,19 @@ enum SplitKind : int {
   KIND_SPARSE = 2,  // kept image rows (gathered by index) + rows [n_img_b, len_b)
 };
 
-// Rows a wave consumes per tile and waves per workgroup of the split kernel.
+// Split kernel geometry: a wave consumes 16-row MFMA tiles and loads
+// kTilesPerWave of them before computing any; a workgroup is kSplitWaves
+// waves, so one round of a workgroup covers kRowsPerRound cache rows.
 constexpr int kTileRows = 16;
-constexpr int kSplitWaves = 4;
-constexpr int kRowsPerPass = kTileRows * kSplitWaves;
-// Upper bound on splits per (sequence, KV head); the combine kernel keeps one
-// weight per split in LDS.
-constexpr int kMaxSplits = 2048;
+constexpr int kSplitWaves = 8;
+constexpr int kTilesPerWave = 4;
+constexpr int kRowsPerRound = kTileRows * kSplitWaves * kTilesPerWave;
+constexpr int kSplitThreads = kSplitWaves * 64;
+constexpr int kMergeThreads = 256;
+constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
+constexpr int kMaxHeads = 128;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkRegKeys = 8;  // keys per thread the top-k holds in registers
 
 struct SplitParams {
   const void* q;          // [B, Hq, D]
@@ -32,31 +38,30 @@ struct SplitParams {
   float* logits;          // [B, Hq, n_stride] log2-domain scaled logits (focal)
   float4* pstat;          // [B, Hq, max_splits] (max, sum p, sum rounded p, text sum p)
   float* po;              // [B, Hq, max_splits, D] unnormalised partial outputs
+  void* out;              // [B, Hq, D] in the io dtype (direct outputs)
   int32_t* status;
   int32_t B, Hq, Hkv, S, n_cap, n_stride, k_stride, max_splits, rows_per_split;
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
+  int32_t direct;         // a sequence whose rows fit one split writes its output
   float scale_log2;       // logit scale * log2(e)
 };
 
-struct CombineParams {
+// Merge of a split pass (one workgroup per head) and, for focal layers, the
+// head-summed image-token scores (score_blocks workgroups per sequence).
+struct MergeParams {
   const float4* pstat;
   const float* po;
   const int32_t* lens;
-  const int32_t* sel_cnt; // non-null: sparse row count
+  const int32_t* sel_cnt; // non-null: the split pass was sparse
   void* out;              // [B, Hq, D] in the io dtype
-  float2* mz;             // [B, Hq] (max, 1 / sum p) or null
-  float* text_mass;       // [B, Hq] text probability mass or null
-  int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split;
-  int32_t grid_splits;    // splits the matching split pass launched
+  float* text_mass;       // [B, Hq] or null
   int32_t* status;
-};
-
-struct ScoreParams {
+  int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split, grid_splits;
+  int32_t direct;         // sequences with one split were finished by the split kernel
   const float* logits;    // [B, Hq, n_stride]
-  const float2* mz;       // [B, Hq]
-  const int32_t* lens;
   float* scores;          // [B, n_stride]
-  int32_t B, Hq, S, n_cap, n_stride;
+  int32_t n_stride;
+  int32_t score_blocks;   // workgroups per sequence for scores (0: none)
 };
 
 struct TopkParams {
@@ -74,8 +79,7 @@ struct TopkParams {
 
 hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p,
                         hipStream_t stream);
-hipError_t launch_combine(int dtype, int head_dim, const CombineParams& p, hipStream_t stream);
-hipError_t launch_score(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 
 }  // namespace fastocr

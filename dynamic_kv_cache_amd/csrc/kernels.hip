@@ -6,21 +6,25 @@
 // Fixation Reuse; the paper's abstract.
 //
 // Kernels
-//   split_attn_kernel  split-K decode attention over one chunk of rows per
-//                      workgroup, for one (sequence, KV head).  Three kinds:
+//   split_attn_kernel  split-K decode attention of one (sequence, KV head)
+//                      over one chunk of rows per workgroup.  Three kinds:
 //                      full rows, full rows + image-logit export (focal
 //                      layers), and kept image rows gathered by index + every
-//                      text row (non-focal layers).
-//   combine_kernel     merges the per-split partial softmax states into the
-//                      output; optionally exports each head's (max, 1/sum) and
-//                      its text-probability mass.
-//   score_kernel       head-summed probability of every image token.
-//   topk_kernel        radix select of the k_b highest scores per sequence,
-//                      ties to the lower index, ascending output.
+//                      text row (non-focal layers).  Writes one partial
+//                      softmax state per split, or the output itself when a
+//                      sequence's rows fit one split.
+//   merge_kernel       one workgroup per head merges the split states into
+//                      the output (and the head's text-probability mass);
+//                      for focal layers, score workgroups compute the
+//                      head-summed probability of every image token.
+//   topk_kernel        the k_b highest scores per sequence, ties to the lower
+//                      index, ascending output.
+// Workgroups never wait on each other inside a kernel: on this GPU a device
+// fence plus an arrival atomic costs more than the next kernel launch.
 //
-// Matrix layout on the MFMA units.  A workgroup is 4 waves; a wave consumes
-// 16 cache rows per tile.  The GQA query group of one KV head (up to 16
-// heads, zero padded) is the N side of a 16x16 MFMA tile:
+// Matrix layout on the MFMA units.  A wave consumes 16 cache rows per tile.
+// The GQA query group of one KV head (up to 16 heads, zero padded) is the N
+// side of a 16x16 MFMA tile:
 //   logits^T[16 rows x 16 heads]  = K_tile[16 x d] * Q^T[d x 16]
 //   out^T   [16 d     x 16 heads] += V_tile^T[16 d x 16 rows] * P^T[16 rows x 16 heads]
 // Because a contraction may visit its index in any order, the d index is
@@ -36,7 +40,9 @@
 //       d = (4g+i)*(d/16) + db, i.e. the contiguous range [g*d/4, (g+1)*d/4).
 // The logits come out as lane (c, g) = head c, rows 4g..4g+3, which is
 // exactly the P^T operand the PV product needs, so softmax stays in
-// registers.
+// registers.  A wave issues the loads of all its tiles of a round (up to 4)
+// before computing any, and rescales its running softmax state once per
+// round.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -109,50 +115,257 @@ __device__ __forceinline__ void load_words(uint32_t* dst, const T* src, int nwor
   }
 }
 
-__device__ __forceinline__ float wave_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// ---------------------------------------------------------------------------
+// wave and workgroup primitives (DPP row shifts and row broadcasts)
+// ---------------------------------------------------------------------------
+// These kernels run once per launch on CUs whose instruction cache is cold,
+// so they are written as short loops rather than long unrolled sequences.
+
+#define FASTOCR_DPP(old, x, ctrl, rmask) __builtin_amdgcn_update_dpp((old), (x), (ctrl), (rmask), 0xf, false)
+
+// Inclusive prefix sum over the 64 lanes of a wave: scans within each
+// 16-lane row (row_shr 1, 2, 4, 8), then carries row totals with
+// row_bcast:15 (into rows 1 and 3) and row_bcast:31 (into rows 2 and 3).
+__device__ __forceinline__ unsigned int wave_incl_scan(unsigned int x) {
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x111, 0xf);
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x112, 0xf);
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x114, 0xf);
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x118, 0xf);
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x142, 0xa);
+  x += (unsigned int)FASTOCR_DPP(0, (int)x, 0x143, 0xc);
+  return x;
 }
-__device__ __forceinline__ float wave_sum16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x111, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x112, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x114, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x118, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x142, 0xa));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x143, 0xc));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  int v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x111, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x112, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x114, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x118, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x142, 0xa))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x143, 0xc))); v = __float_as_int(x);
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
+// ---------------------------------------------------------------------------
+// top-k selection
+// ---------------------------------------------------------------------------
+
+// k = clamp(ceil(tau*n - 1e-9), 1, n); the products and differences are
+// rounded one operation at a time so host and device agree bit for bit.
+__device__ __forceinline__ int device_kept_count(double tau, int n) {
+  if (n <= 0) return 0;
+  const double prod = __dmul_rn(tau, (double)n);
+  const double k = ceil(__dadd_rn(prod, -1e-9));
+  int ki = (int)k;
+  return min(max(ki, 1), n);
+}
+
+struct TopkShared {
+  unsigned int hist[kTopkThreads / 64][256];  // one histogram per wave
+  unsigned int wave_sum[kTopkThreads / 64];
+  unsigned int prefix;
+  int remaining;
+};
+
+// Count one key into this wave's histogram of digit (key >> shift) & 255,
+// if its higher digits match `prefix` under `mask`.  Keys of one wave mostly
+// share their leading digits, so lanes with the first pending lane's digit
+// are counted by one atomic; the remaining lanes add one each.
+__device__ __forceinline__ void hist_key(unsigned int key, bool valid, int shift, unsigned int mask,
+                                         unsigned int prefix, unsigned int* hist, int lane) {
+  const unsigned int dig = (key >> shift) & 255u;
+  const bool pending = valid && (key & mask) == prefix;
+  const unsigned long long pm = __ballot(pending);
+  if (pm != 0ull) {
+    const int leader = __ffsll((unsigned long long)pm) - 1;
+    const unsigned int ld = (unsigned int)__builtin_amdgcn_readlane((int)dig, leader);
+    const bool same = pending && dig == ld;
+    const unsigned long long sm = __ballot(same);
+    if (lane == leader) atomicAdd(&hist[ld], (unsigned int)__popcll(sm));
+    if (pending && !same) atomicAdd(&hist[dig], 1u);
+  }
+}
+
+// Top-k of the non-negative float keys[0, n) by one kTopkThreads workgroup.
+// Thread t owns keys [t*per, t*per + per), in registers when per is small,
+// re-read from memory otherwise.  A 4-pass radix select (8 bits per pass,
+// most significant first; the IEEE bits of a non-negative float order like
+// its value) finds the k-th largest key theta and how many keys equal to
+// theta are kept; one workgroup prefix sum then places every kept index, so
+// the output is in ascending index order and ties at theta go to the lowest
+// indices.
+__device__ void block_topk(const unsigned int* __restrict__ keys, int n, int k,
+                           int32_t* __restrict__ out, TopkShared& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int base = tid * per;
+  const int mine = max(0, min(per, n - base));
+  const bool in_regs = per <= kTopkRegKeys;
+  unsigned int reg[kTopkRegKeys];
+#pragma unroll
+  for (int i = 0; i < kTopkRegKeys; ++i) reg[i] = in_regs ? keys[min(base + i, n - 1)] : 0u;
+
+  unsigned int prefix = 0u, mask = 0u;
+  int remaining = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0u;
+    __syncthreads();
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kTopkRegKeys; ++i)
+        if (i < per) hist_key(reg[i], i < mine, shift, mask, prefix, sh.hist[wave], lane);
+    } else {
+#pragma unroll 1
+      for (int i = 0; i < per; ++i)
+        hist_key(keys[min(base + i, n - 1)], i < mine, shift, mask, prefix, sh.hist[wave], lane);
+    }
+    __syncthreads();
+    // thread t < 256 owns digit 255 - t: inclusive count in descending digit order
+    unsigned int c = 0, incl = 0;
+    if (tid < 256) {
+      for (int w = 0; w < kTopkThreads / 64; ++w) c += sh.hist[w][255 - tid];
+      incl = wave_incl_scan(c);
+      if (lane == 63) sh.wave_sum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) incl += sh.wave_sum[w];
+      const unsigned int above = incl - c;  // keys with a larger digit
+      if (above < (unsigned int)remaining && (unsigned int)remaining <= incl) {
+        sh.prefix = prefix | ((unsigned int)(255 - tid) << shift);
+        sh.remaining = remaining - (int)above;
+      }
+    }
+    __syncthreads();
+    prefix = sh.prefix;
+    remaining = sh.remaining;
+    mask |= 255u << shift;
+  }
+  const unsigned int theta = prefix;  // k-th largest key
+  const int need_eq = remaining;      // keys equal to theta to keep, lowest index first
+
+  unsigned int gt = 0, eq = 0;
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; ++i) {
+      gt += (i < mine && reg[i] > theta) ? 1u : 0u;
+      eq += (i < mine && reg[i] == theta) ? 1u : 0u;
+    }
+  } else {
+#pragma unroll 1
+    for (int i = 0; i < mine; ++i) {
+      const unsigned int key = keys[base + i];
+      gt += key > theta ? 1u : 0u;
+      eq += key == theta ? 1u : 0u;
+    }
+  }
+  // both counts stay below 2^16 for n < 65536, so one packed scan serves both
+  const unsigned int v = (gt << 16) | eq;
+  unsigned int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) sh.wave_sum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += sh.wave_sum[w];
+  const unsigned int excl = incl - v;
+  int eq_seen = (int)(excl & 0xffffu);
+  int pos = (int)(excl >> 16) + min(eq_seen, need_eq);
+#pragma unroll 1
+  for (int i = 0; i < mine; ++i) {
+    unsigned int key = 0u;
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < kTopkRegKeys; ++r) key = (r == i) ? reg[r] : key;
+    } else {
+      key = keys[base + i];
+    }
+    if (key > theta) {
+      out[pos++] = base + i;
+    } else if (key == theta) {
+      if (eq_seen < need_eq) out[pos++] = base + i;
+      ++eq_seen;
+    }
+  }
+}
+
+__device__ __forceinline__ void topk_sequence(const float* keys, int n, double tau, int idx_stride,
+                                              int32_t* out, int32_t* cnt, TopkShared& sh) {
+  const int k = min(device_kept_count(tau, n), idx_stride);
+  if (threadIdx.x == 0) *cnt = k;
+  if (k == 0) return;
+  block_topk(reinterpret_cast<const unsigned int*>(keys), n, k, out, sh);
 }
 
 // ---------------------------------------------------------------------------
 // split-K decode attention
 // ---------------------------------------------------------------------------
 
+// Splits holding rows of a sequence with `rows` attended rows.
+__device__ __forceinline__ int split_count(int rows, int rows_per_split, int grid_splits,
+                                           int32_t* status, bool report) {
+  int nsplit = (rows + rows_per_split - 1) / rows_per_split;
+  if (nsplit > grid_splits) {
+    // more rows than the launch was sized for (a sequence below the declared
+    // minimum image-token count): only the launched splits exist
+    if (report) atomicOr(status, FASTOCR_FLAG_ROWS_TRUNCATED);
+    nsplit = grid_splits;
+  }
+  return nsplit;
+}
+
 template <typename T, int D, int KIND>
-__global__ __launch_bounds__(256) void split_attn_kernel(SplitParams p) {
+__global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
-  constexpr int E = D / 4;                           // K/q elements per lane
-  constexpr int KW = E * (int)sizeof(T) / 4;         // ... as 32-bit words
-  constexpr int NDB = D / 16;                        // PV d-blocks = V elements per row per lane
-  constexpr int VW = NDB * (int)sizeof(T) / 4;       // V words per row per lane
-  constexpr int OST = D + 1;                         // padded LDS row of partial outputs
+  constexpr int E = D / 4;                      // K/q elements per lane
+  constexpr int KW = E * (int)sizeof(T) / 4;    // ... as 32-bit words
+  constexpr int NDB = D / 16;                   // PV d-blocks = V elements per row per lane
+  constexpr int VW = NDB * (int)sizeof(T) / 4;  // V words per row per lane
+  constexpr int TPW = kTilesPerWave;
+  constexpr int HH = 8;                         // heads per LDS merge round
+  constexpr int OST = D + 1;                    // padded LDS row of partial outputs
 
   __shared__ float s_stat[kSplitWaves][16][4];
-  __shared__ float s_o[kSplitWaves][16][OST];
+  __shared__ float4 s_head[16];
+  __shared__ float s_o[kSplitWaves][HH][OST];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
 
   int n, len;
   const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
-  if (clamped && split == 0 && kvh == 0 && threadIdx.x == 0)
-    atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
+  const bool reporter = split == 0 && kvh == 0 && tid == 0;
+  if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
   const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
   const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
+  const int nsplit = split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
+  const bool direct = p.direct && nsplit <= 1;
   const int begin = split * p.rows_per_split;
-  if (begin >= rows) return;
+  if (begin >= rows) {
+    if (direct && split == 0) {  // no rows at all: zero output
+      T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
+      for (int i = tid; i < G * D; i += kSplitThreads) store_out<T>(out + i, 0.f);
+    }
+    return;
+  }
   const int end = min(begin + p.rows_per_split, rows);
 
   const size_t row_base = ((size_t)b * p.Hkv + kvh) * (size_t)p.S;
@@ -160,18 +373,17 @@ __global__ __launch_bounds__(256) void split_attn_kernel(SplitParams p) {
   const T* __restrict__ Vb = reinterpret_cast<const T*>(p.v) + row_base * D;
   const int32_t* __restrict__ selb = (KIND == KIND_SPARSE) ? p.sel + (size_t)b * p.k_stride : nullptr;
 
-  // virtual row -> cache row
+  // Virtual row -> cache row.  Branch-free, so the index loads of a round
+  // are all in flight together; a kept index outside [0, n) is clamped and
+  // reported once at the end.
+  bool bad_index = false;
   auto phys = [&](int r) -> int {
     if (KIND == KIND_SPARSE) {
-      if (r < kept) {
-        int j = selb[r];
-        if (j < 0 || j >= n) {
-          atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
-          j = min(max(j, 0), max(n - 1, 0));
-        }
-        return j;
-      }
-      return n + (r - kept);
+      const int j = selb[min(r, p.k_stride - 1)];
+      const bool img = r < kept;
+      bad_index |= img && (j < 0 || j >= n);
+      const int jc = min(max(j, 0), max(n - 1, 0));
+      return img ? jc : n + (r - kept);
     }
     return r;
   };
@@ -191,369 +403,358 @@ __global__ __launch_bounds__(256) void split_attn_kernel(SplitParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int tile = begin + wave * kTileRows; tile < end; tile += kRowsPerPass) {
-    // ---- loads: K row (tile+col), slice grp; V rows tile+4grp+j, slice col
-    uint32_t kw[KW];
-    {
-      const int pk = phys(min(tile + col, end - 1));
-      load_words(kw, Kb + (size_t)pk * D + grp * E, KW);
-    }
-    uint32_t vw[4][VW];
+  // Round r covers rows [begin + r*kRowsPerRound, +kRowsPerRound); tile u of
+  // wave w in a round starts at row (u*kSplitWaves + w)*16, so a split of
+  // 128 / 256 / 512 rows gives every wave 1 / 2 / 4 tiles.
+  for (int r0 = begin + wave * kTileRows; r0 < end; r0 += kRowsPerRound) {
+    // ---- cache rows of this round's tiles, then all their loads
+    int pk[TPW], pvr[TPW][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pv = phys(min(tile + 4 * grp + j, end - 1));
-      load_words(vw[j], Vb + (size_t)pv * D + col * NDB, VW);
-    }
-
-    // ---- logits^T = K_tile * Q^T
-    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF) {
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r0 + u * kSplitWaves * kTileRows;
+      pk[u] = phys(min(tile + col, end - 1));
 #pragma unroll
-      for (int kk = 0; kk < E / 4; ++kk) {
-        bf16x4_t a, bq;
-        uint32_t a0 = kw[2 * kk], a1 = kw[2 * kk + 1];
-        uint32_t b0 = qw[2 * kk], b1 = qw[2 * kk + 1];
-        a = bf16x4_t{(short)(a0 & 0xffff), (short)(a0 >> 16), (short)(a1 & 0xffff), (short)(a1 >> 16)};
-        bq = bf16x4_t{(short)(b0 & 0xffff), (short)(b0 >> 16), (short)(b1 & 0xffff), (short)(b1 >> 16)};
-        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bq, s, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) pvr[u][j] = phys(min(tile + 4 * grp + j, end - 1));
+    }
+    uint32_t kw[TPW][KW];
+    uint32_t vw[TPW][4][VW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (r0 + u * kSplitWaves * kTileRows < end) {  // uniform over the wave
+        load_words(kw[u], Kb + (size_t)pk[u] * D + grp * E, KW);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load_words(vw[u][j], Vb + (size_t)pvr[u][j] * D + col * NDB, VW);
       }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < E; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[kk]), __uint_as_float(qw[kk]), s,
-                                                 0, 0, 0);
     }
 
-    // ---- masked, scaled logits of rows tile+4grp+i for head col
-    float x[4];
+    // ---- logits^T = K_tile * Q^T for every tile of the round
+    float x[TPW][4];
+    float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = tile + 4 * grp + i;
-      x[i] = (r < end) ? s[i] * p.scale_log2 : -INFINITY;
-    }
-    if constexpr (KIND == KIND_FOCAL) {
-      if (col < G) {
-        float* lg = p.logits + ((size_t)b * p.Hq + kvh * G + col) * p.n_stride;
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r0 + u * kSplitWaves * kTileRows;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = tile + 4 * grp + i;
-          if (r < end && r < n) lg[r] = x[i];
+      for (int i = 0; i < 4; ++i) x[u][i] = -INFINITY;
+      if (tile >= end) continue;
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF) {
+#pragma unroll
+        for (int kk = 0; kk < E / 4; ++kk) {
+          const uint32_t a0 = kw[u][2 * kk], a1 = kw[u][2 * kk + 1];
+          const uint32_t b0 = qw[2 * kk], b1 = qw[2 * kk + 1];
+          const bf16x4_t a = bf16x4_t{(short)(a0 & 0xffff), (short)(a0 >> 16), (short)(a1 & 0xffff), (short)(a1 >> 16)};
+          const bf16x4_t bq = bf16x4_t{(short)(b0 & 0xffff), (short)(b0 >> 16), (short)(b1 & 0xffff), (short)(b1 >> 16)};
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bq, s, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < E; ++kk)
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[u][kk]), __uint_as_float(qw[kk]), s,
+                                                   0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tile + 4 * grp + i;
+        x[u][i] = (r < end) ? s[i] * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[u][i]);
+      }
+      if constexpr (KIND == KIND_FOCAL) {
+        if (col < G) {
+          float* lg = p.logits + ((size_t)b * p.Hq + kvh * G + col) * p.n_stride;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = tile + 4 * grp + i;
+            if (r < end && r < n) lg[r] = x[u][i];
+          }
         }
       }
     }
 
-    // ---- online softmax (per head; the 4 lane groups share a head)
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = wave_max16_32(mt);
+    // ---- online softmax: one rescale per round (per head; the 4 lane
+    // groups of a column share the head)
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    float pr[4], pu[4];
-    uint32_t pb[4];
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    z *= alpha;
+    lsum *= alpha;
+    zt *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = exp2f(x[i] - m_new);
-      if constexpr (BF) {
-        pb[i] = f32_to_bf16(pr[i]);
-        pu[i] = bf16_to_f32(pb[i]);
-      } else {
-        pu[i] = pr[i];
-      }
-    }
-    float ztile = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = tile + 4 * grp + i;
-      const bool text = (KIND == KIND_SPARSE) ? (r >= kept) : (r >= n);
-      ztile += text ? pr[i] : 0.f;
-    }
-    z = z * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    lsum = lsum * alpha + ((pu[0] + pu[1]) + (pu[2] + pu[3]));
-    zt = zt * alpha + ztile;
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
     m_run = m_new;
 
-    // ---- out^T += V_tile^T * P^T
-    if constexpr (BF) {
-      const bf16x4_t pv = bf16x4_t{(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+    // ---- out^T += V_tile^T * P^T (rows past `end` have p = 0)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int w = db >> 1;
-        uint32_t e[4];
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r0 + u * kSplitWaves * kTileRows;
+      if (tile >= end) continue;
+      float pr[4], pu[4];
+      uint32_t pb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = (db & 1) ? (vw[j][w] >> 16) : (vw[j][w] & 0xffffu);
-        const bf16x4_t a = bf16x4_t{(short)e[0], (short)e[1], (short)e[2], (short)e[3]};
-        f32x4_t c = acc[db] * alpha;
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pv, c, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[u][i] - m_new);
+        if constexpr (BF) {
+          pb[i] = f32_to_bf16(pr[i]);
+          pu[i] = bf16_to_f32(pb[i]);
+        } else {
+          pu[i] = pr[i];
+        }
+        const int r = tile + 4 * grp + i;
+        const bool text = (KIND == KIND_SPARSE) ? (r >= kept) : (r >= n);
+        zt += text ? pr[i] : 0.f;
       }
-    } else {
+      z += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      lsum += (pu[0] + pu[1]) + (pu[2] + pu[3]);
+      if constexpr (BF) {
+        const bf16x4_t pv = bf16x4_t{(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        f32x4_t c = acc[db] * alpha;
+        for (int db = 0; db < NDB; ++db) {
+          const int w = db >> 1;
+          uint32_t e[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vw[i][db]), pr[i], c, 0, 0, 0);
-        acc[db] = c;
+          for (int j = 0; j < 4; ++j) e[j] = (db & 1) ? (vw[u][j][w] >> 16) : (vw[u][j][w] & 0xffffu);
+          const bf16x4_t a = bf16x4_t{(short)e[0], (short)e[1], (short)e[2], (short)e[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pv, acc[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vw[u][i][db]), pr[i], acc[db],
+                                                           0, 0, 0);
       }
     }
   }
 
-  // ---- per-wave totals (lane groups of one head hold partial sums)
-  z = wave_sum16_32(z);
-  lsum = wave_sum16_32(lsum);
-  zt = wave_sum16_32(zt);
+  if (KIND == KIND_SPARSE && bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
+
+  // ---- per-wave totals (the 4 lane groups of a head hold partial sums)
+  z += __shfl_xor(z, 16);
+  z += __shfl_xor(z, 32);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  zt += __shfl_xor(zt, 16);
+  zt += __shfl_xor(zt, 32);
   if (grp == 0) {
     s_stat[wave][col][0] = m_run;
     s_stat[wave][col][1] = z;
     s_stat[wave][col][2] = lsum;
     s_stat[wave][col][3] = zt;
   }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][col][(4 * grp + i) * NDB + db] = acc[db][i];
   __syncthreads();
 
-  // ---- merge the 4 waves into this split's partial state
-  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = s_stat[0][h][0];
+  // ---- merge the waves: head totals, then outputs in rounds of HH heads
+  float M = -INFINITY;
 #pragma unroll
-    for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, s_stat[w][h][0]);
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) o += s_o[w][h][d] * exp2f(s_stat[w][h][0] - M);
-    p.po[(slot0 + (size_t)h * p.max_splits) * D + d] = o;
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float M = s_stat[0][h][0];
-#pragma unroll
-    for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, s_stat[w][h][0]);
+  for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, s_stat[w][col][0]);
+  const float e_self = __builtin_amdgcn_exp2f(m_run - M);  // this wave's weight for head col
+  if (tid < G) {
     float zz = 0.f, ll = 0.f, tt = 0.f;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
-      const float e = exp2f(s_stat[w][h][0] - M);
-      zz += s_stat[w][h][1] * e;
-      ll += s_stat[w][h][2] * e;
-      tt += s_stat[w][h][3] * e;
+      const float e = __builtin_amdgcn_exp2f(s_stat[w][tid][0] - M);
+      zz += s_stat[w][tid][1] * e;
+      ll += s_stat[w][tid][2] * e;
+      tt += s_stat[w][tid][3] * e;
     }
-    p.pstat[slot0 + (size_t)h * p.max_splits] = make_float4(M, zz, ll, tt);
+    s_head[tid] = make_float4(M, zz, ll, tt);
   }
+  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
+  for (int h0 = 0; h0 < G; h0 += HH) {
+    if (col >= h0 && col < h0 + HH) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i] * e_self;
+    }
+    __syncthreads();
+    const int hn = min(HH, G - h0);
+    for (int idx = tid; idx < hn * D; idx += kSplitThreads) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSplitWaves; ++w) o += s_o[w][h][d];
+      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, o / s_head[h0 + h].z);
+      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+    }
+    __syncthreads();
+  }
+  if (!direct && tid < G) p.pstat[slot0 + (size_t)tid * p.max_splits] = s_head[tid];
 }
 
 // ---------------------------------------------------------------------------
-// split combine
+// merge of split states, and image-token scores
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = fmaxf(r, red[w]);
-  return r;
+// Sum over groups of SL = 8 or 16 adjacent lanes; every lane of a group gets
+// the group total.  Pairs lanes i and 15-i (row_mirror, SL = 16) and i and
+// 7-i (row_half_mirror), then folds with the quad permutations 1,0,3,2 and
+// 2,3,0,1.
+template <int SL>
+__device__ __forceinline__ float group_sum(float x) {
+  if (SL == 16) x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x140, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x141, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0xb1, 0xf));
+  x += __int_as_float(FASTOCR_DPP(0, __float_as_int(x), 0x4e, 0xf));
+  return x;
 }
 
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r += red[w];
-  return r;
+// Max over each 16-lane row; every lane gets its row's result (the same
+// mirror/quad folds as group_sum<16>).
+__device__ __forceinline__ float row_max16(float x) {
+  int v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x140, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x141, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0xb1, 0xf))); v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(FASTOCR_DPP(v, v, 0x4e, 0xf)));
+  return x;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[4];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  int n, len;
+__device__ __forceinline__ int merge_splits(const MergeParams& p, int b, int& n, int& len) {
   seq_extent(p.lens, b, p.S, p.n_cap, n, len);
   const int rows = p.sel_cnt ? kept_rows(p.sel_cnt, b, n, p.k_stride) + (len - n) : len;
-  int nsplit = (rows + p.rows_per_split - 1) / p.rows_per_split;
-  if (nsplit > p.grid_splits) {
-    // more rows than the launch was sized for (a sequence below the declared
-    // minimum image-token count): only the launched splits exist
-    if (threadIdx.x == 0) atomicOr(p.status, FASTOCR_FLAG_ROWS_TRUNCATED);
-    nsplit = p.grid_splits;
-  }
-  const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
-  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
-
-  if (nsplit == 0) {
-    for (int d = threadIdx.x; d < D; d += blockDim.x) store_out<T>(out + d, 0.f);
-    if (threadIdx.x == 0) {
-      if (p.mz) p.mz[b * p.Hq + h] = make_float2(-INFINITY, 0.f);
-      if (p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
-    }
-    return;
-  }
-
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mloc = fmaxf(mloc, p.pstat[slot0 + s].x);
-  const float M = block_reduce_max(mloc, s_red);
-  float zl = 0.f, ll = 0.f, tl = 0.f;
-  for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
-    const float4 st = p.pstat[slot0 + s];
-    const float w = exp2f(st.x - M);
-    s_w[s] = w;
-    zl += st.y * w;
-    ll += st.z * w;
-    tl += st.w * w;
-  }
-  const float Z = block_reduce_sum(zl, s_red);
-  const float Lr = block_reduce_sum(ll, s_red);
-  const float Zt = block_reduce_sum(tl, s_red);  // ends with a barrier: s_w is visible
-  const float inv_l = 1.f / Lr;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float o = 0.f;
-    const float* po = p.po + slot0 * D + d;
-    for (int s = 0; s < nsplit; ++s) o += po[(size_t)s * D] * s_w[s];
-    store_out<T>(out + d, o * inv_l);
-  }
-  if (threadIdx.x == 0) {
-    if (p.mz) p.mz[b * p.Hq + h] = make_float2(M, 1.f / Z);
-    if (p.text_mass) p.text_mass[b * p.Hq + h] = Zt / Z;
-  }
+  return split_count(rows, p.rows_per_split, p.grid_splits, p.status, false);
 }
 
-// ---------------------------------------------------------------------------
-// head-summed image-token scores
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-  __shared__ float2 s_mz[128];
-  const int b = blockIdx.y;
-  for (int h = threadIdx.x; h < p.Hq; h += blockDim.x) s_mz[h] = p.mz[b * p.Hq + h];
-  __syncthreads();
+// Workgroups [0, Hq): merge head h's split states into its output.  Thread
+// t covers float4 column t / SL of the output and splits s = t % SL (mod SL).
+template <typename T, int D>
+__device__ void merge_head(const MergeParams& p, int b, int h) {
+  constexpr int D4 = D / 4;
+  constexpr int SL = kMergeThreads / D4;
+  __shared__ float s_w[kMaxMergeSplits];
+  __shared__ float s_red[kMergeThreads / 64][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n, len;
-  seq_extent(p.lens, b, p.S, p.n_cap, n, len);
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nsplit = merge_splits(p, b, n, len);
+  if (p.direct && nsplit <= 1) return;  // finished by the split kernel
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  if (nsplit == 0) {
+    for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
+    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
+    return;
+  }
+  const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
+  float m = -INFINITY;
+  for (int s = tid; s < nsplit; s += kMergeThreads) m = fmaxf(m, p.pstat[slot0 + s].x);
+  m = wave_max(m);
+  if (lane == 0) s_red[wave][0] = m;
+  __syncthreads();
+  float M = s_red[0][0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
+  float z = 0.f, l = 0.f, t = 0.f;
+  for (int s = tid; s < nsplit; s += kMergeThreads) {
+    const float4 st = p.pstat[slot0 + s];
+    const float w = __builtin_amdgcn_exp2f(st.x - M);
+    s_w[s] = w;
+    z += st.y * w;
+    l += st.z * w;
+    t += st.w * w;
+  }
+  z = wave_sum(z);
+  l = wave_sum(l);
+  t = wave_sum(t);
+  if (lane == 0) {
+    s_red[wave][1] = z;
+    s_red[wave][2] = l;
+    s_red[wave][3] = t;
+  }
+  __syncthreads();
+  float Z = 0.f, L = 0.f, Zt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) {
+    Z += s_red[w][1];
+    L += s_red[w][2];
+    Zt += s_red[w][3];
+  }
+  const int d4 = tid / SL, sl = tid % SL;
+  const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int s = sl; s < nsplit; s += SL) {
+    const float4 v = po[(size_t)s * D4];
+    const float w = s_w[s];
+    a0 += v.x * w;
+    a1 += v.y * w;
+    a2 += v.z * w;
+    a3 += v.w * w;
+  }
+  a0 = group_sum<SL>(a0);
+  a1 = group_sum<SL>(a1);
+  a2 = group_sum<SL>(a2);
+  a3 = group_sum<SL>(a3);
+  if (sl == 0) {
+    const float inv = 1.f / L;
+    store_out<T>(out + 4 * d4 + 0, a0 * inv);
+    store_out<T>(out + 4 * d4 + 1, a1 * inv);
+    store_out<T>(out + 4 * d4 + 2, a2 * inv);
+    store_out<T>(out + 4 * d4 + 3, a3 * inv);
+  }
+  if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = Zt / Z;
+}
+
+// Workgroups [Hq, Hq + score_blocks): head-summed probability of
+// kMergeThreads image tokens each.  Each score workgroup derives every
+// head's softmax max and sum from the split states itself (32 lanes per
+// head), so it does not depend on the merge workgroups.
+__device__ void score_block(const MergeParams& p, int b, int sb) {
+  __shared__ float2 s_mz[kMaxHeads];
+  const int tid = threadIdx.x;
+  int n, len;
+  const int nsplit = merge_splits(p, b, n, len);
+  const int hl = tid & 15;
+  for (int h0 = 0; h0 < p.Hq; h0 += kMergeThreads / 16) {
+    const int h = h0 + (tid >> 4);
+    const bool hv = h < p.Hq;
+    const float4* ps = p.pstat + ((size_t)b * p.Hq + (hv ? h : 0)) * p.max_splits;
+    float m = -INFINITY;
+    if (hv)
+      for (int s = hl; s < nsplit; s += 16) m = fmaxf(m, ps[s].x);
+    m = row_max16(m);
+    float z = 0.f;
+    if (hv)
+      for (int s = hl; s < nsplit; s += 16) {
+        const float4 st = ps[s];
+        z += st.y * __builtin_amdgcn_exp2f(st.x - m);
+      }
+    z = group_sum<16>(z);
+    if (hv && hl == 0) s_mz[h] = make_float2(m, 1.f / z);
+  }
+  __syncthreads();
+  const int j = sb * kMergeThreads + tid;
   if (j >= n) return;
   const float* lg = p.logits + (size_t)b * p.Hq * p.n_stride + j;
   float s = 0.f;
-  for (int h = 0; h < p.Hq; ++h) s += exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
+  int h = 0;
+  for (; h + 4 <= p.Hq; h += 4) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = lg[(size_t)(h + u) * p.n_stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += __builtin_amdgcn_exp2f(x[u] - s_mz[h + u].x) * s_mz[h + u].y;
+  }
+  for (; h < p.Hq; ++h) s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
   p.scores[(size_t)b * p.n_stride + j] = s;
 }
 
-// ---------------------------------------------------------------------------
-// top-k selection
-// ---------------------------------------------------------------------------
-
-// k = clamp(ceil(tau*n - 1e-9), 1, n); the products and differences are
-// rounded one operation at a time so host and device agree bit for bit.
-__device__ __forceinline__ int device_kept_count(double tau, int n) {
-  if (n <= 0) return 0;
-  const double prod = __dmul_rn(tau, (double)n);
-  const double k = ceil(__dadd_rn(prod, -1e-9));
-  int ki = (int)k;
-  return min(max(ki, 1), n);
-}
-
-constexpr int kTopkThreads = 1024;
-
-// Exclusive prefix count of `flag` over the workgroup in thread order, using
-// wave ballots; returns the prefix and stores the workgroup total in *total.
-__device__ __forceinline__ int block_exclusive_count(bool flag, int* s_wave, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  __syncthreads();
-  if (lane == 0) s_wave[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0, all = 0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) {
-    const int c = s_wave[w];
-    before += (w < wave) ? c : 0;
-    all += c;
-  }
-  *total = all;
-  return before + below;
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x < p.Hq) merge_head<T, D>(p, b, blockIdx.x);
+  else score_block(p, b, blockIdx.x - p.Hq);
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  __shared__ unsigned int s_hist[256];
-  __shared__ unsigned int s_prefix;
-  __shared__ int s_remaining;
-  __shared__ int s_wave[kTopkThreads / 64];
+  __shared__ TopkShared sh;
   const int b = blockIdx.x;
   const int n0 = p.lens[2 * b];
   const int n = min(max(n0, 0), min(max(p.lens[2 * b + 1], 0), p.n_cap));
   if (n0 != n && threadIdx.x == 0 && p.status) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
-  const int k = min(device_kept_count(p.tau, n), p.idx_stride);
-  if (threadIdx.x == 0) p.cnt[b] = k;
-  if (k == 0) return;
-  const unsigned int* keys = reinterpret_cast<const unsigned int*>(p.scores) + (size_t)b * p.score_stride;
-  int32_t* out = p.idx + (size_t)b * p.idx_stride;
-
-  // Radix select of the k-th largest key, 8 bits per pass from the top.  For
-  // non-negative floats the IEEE bit pattern orders like the value.
-  unsigned int prefix = 0u, mask = 0u;
-  int remaining = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0u;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n; j += blockDim.x) {
-      const unsigned int key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      const int lane = threadIdx.x;
-      unsigned int c[4], sum = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = s_hist[255 - 4 * lane - i];
-        sum += c[i];
-      }
-      unsigned int incl = sum;
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-      }
-      unsigned int above = incl - sum;  // keys with a larger digit
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (above < (unsigned int)remaining && (unsigned int)remaining <= above + c[i]) {
-          s_prefix = prefix | ((unsigned int)(255 - 4 * lane - i) << shift);
-          s_remaining = remaining - (int)above;
-        }
-        above += c[i];
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    remaining = s_remaining;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const unsigned int theta = prefix;  // k-th largest key
-  const int need_eq = remaining;      // keys equal to theta to take, lowest index first
-
-  int out_base = 0, eq_base = 0;
-  for (int base = 0; base < n; base += blockDim.x) {
-    const int j = base + threadIdx.x;
-    const unsigned int key = (j < n) ? keys[j] : 0u;
-    const bool gt = (j < n) && key > theta;
-    const bool eq = (j < n) && key == theta;
-    int eq_total, keep_total;
-    const int eq_rank = eq_base + block_exclusive_count(eq, s_wave, &eq_total);
-    const bool keep = gt || (eq && eq_rank < need_eq);
-    const int pos = out_base + block_exclusive_count(keep, s_wave, &keep_total);
-    if (keep) out[pos] = j;
-    eq_base += eq_total;
-    out_base += keep_total;
-  }
+  topk_sequence(p.scores + (size_t)b * p.score_stride, n, p.tau, p.idx_stride,
+                p.idx + (size_t)b * p.idx_stride, p.cnt + b, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,7 +763,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
 
 template <typename T, int D>
 static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream) {
-  dim3 grid(p.grid_splits, p.Hkv, p.B), block(kSplitWaves * 64);
+  dim3 grid(p.grid_splits, p.Hkv, p.B), block(kSplitThreads);
   switch (kind) {
     case KIND_FULL: split_attn_kernel<T, D, KIND_FULL><<<grid, block, 0, stream>>>(p); break;
     case KIND_FOCAL: split_attn_kernel<T, D, KIND_FOCAL><<<grid, block, 0, stream>>>(p); break;
@@ -580,21 +781,15 @@ hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitPara
                          : launch_split_t<float, 64>(kind, p, stream);
 }
 
-hipError_t launch_combine(int dtype, int head_dim, const CombineParams& p, hipStream_t stream) {
-  dim3 grid(p.Hq, p.B), block(128);
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream) {
+  dim3 grid(p.Hq + p.score_blocks, p.B), block(kMergeThreads);
   if (dtype == FASTOCR_DTYPE_BF16) {
-    if (head_dim == 128) combine_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(p);
-    else combine_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(p);
+    if (head_dim == 128) merge_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(p);
+    else merge_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(p);
   } else {
-    if (head_dim == 128) combine_kernel<float, 128><<<grid, block, 0, stream>>>(p);
-    else combine_kernel<float, 64><<<grid, block, 0, stream>>>(p);
+    if (head_dim == 128) merge_kernel<float, 128><<<grid, block, 0, stream>>>(p);
+    else merge_kernel<float, 64><<<grid, block, 0, stream>>>(p);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
-  dim3 grid((p.n_stride + 255) / 256, p.B), block(256);
-  score_kernel<<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -67,12 +67,12 @@ extern "C" {
 
 /* ---- kernel classes timed by fastocr_get_timing -------------------------- */
 #define FASTOCR_KC_FULL_SPLIT 0   /* split-K full attention (warm-up, FULL mode) */
-#define FASTOCR_KC_FOCAL_SPLIT 1  /* split-K full attention with image-logit export */
-#define FASTOCR_KC_SPARSE_SPLIT 2 /* split-K attention over gathered kept rows */
-#define FASTOCR_KC_COMBINE 3      /* split combine (+ image mass during warm-up) */
-#define FASTOCR_KC_SCORE 4        /* head-summed image-token scores */
-#define FASTOCR_KC_TOPK 5         /* radix top-k selection */
-#define FASTOCR_KC_COUNT 6
+#define FASTOCR_KC_FOCAL_SPLIT 1  /* the same with image-logit export (focal layers) */
+#define FASTOCR_KC_SPARSE_SPLIT 2 /* split-K attention over gathered kept rows; writes the
+                                     output itself when a sequence fits one split */
+#define FASTOCR_KC_MERGE 3        /* split merge (+ head-summed image-token scores) */
+#define FASTOCR_KC_TOPK 4         /* top-k selection of the kept set */
+#define FASTOCR_KC_COUNT 5
 
 typedef struct fastocr_config {
   double tau;             /* kept ratio of image tokens, 0 < tau <= 1 */
@@ -101,6 +101,8 @@ typedef struct fastocr_info {
   int32_t full_max_splits;
   int32_t sparse_rows_per_split;
   int32_t sparse_max_splits;
+  int32_t sparse_direct;  /* 1: non-focal layers finish in one split (no merge launch) */
+  int32_t reserved;
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     # double first, then a float and twelve int32 -> 60 bytes, padded to 64
     assert ctypes.sizeof(_abi.Config) == 64
-    assert ctypes.sizeof(_abi.Info) == 40
+    assert ctypes.sizeof(_abi.Info) == 48
     assert ctypes.sizeof(_abi.Timing) == 2 * 8 * _abi.KC_COUNT
 
 
