@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="7b-b1")
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline sample (0 disables it)")
@@ -62,15 +63,18 @@ def main():
     import torch
 
     import dynamic_kv_cache_amd as fo
-    from workload import Generator, get_workload, make_structure
+    from workload import DeviceGenerator, get_workload, make_structure
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    wl = get_workload(args.workload)
+    overrides = {}
     if args.tau is not None:
-        wl = wl.with_overrides(tau=args.tau)
+        overrides["tau"] = args.tau
+    if args.sigma is not None:
+        overrides["sigma"] = args.sigma
+    wl = get_workload(args.workload, **overrides)
     st = make_structure(wl)
-    gen = Generator(wl, st)
+    gen = DeviceGenerator(wl, st, device=dev)
     L, B, Hq, Hkv, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     w, W, K = wl.warmup_steps, args.warmup, args.steps
     # decode steps used: warm-up, untimed pruned, timed (graph), timed (per-kernel events)
@@ -82,15 +86,11 @@ def main():
 
     t0 = time.time()
     Kd, Vd, Qall = [], [], torch.empty((n_steps, L, B, Hq, d), dtype=io, device=dev)
-    host_kv = []
     for l in range(L):
         k, v = gen.layer_kv(l)
-        q = gen.layer_queries(l, steps=range(n_steps), K=k)
-        Kd.append(torch.from_numpy(k).to(dev).to(io))
-        Vd.append(torch.from_numpy(v).to(dev).to(io))
-        Qall[:, l] = torch.from_numpy(q).to(dev).to(io)
-        if args.cpu_seconds > 0 and not args.profile_only:
-            host_kv.append((k, v, q))
+        Kd.append(k)
+        Vd.append(v)
+        Qall[:, l] = gen.layer_queries(l, range(n_steps), k)
     lens_all = torch.from_numpy(np.stack([st.lens(t) for t in range(n_steps)])).to(dev)
     torch.cuda.synchronize()
     log(f"inputs for {wl.name} ready in {time.time() - t0:.1f}s "
@@ -264,7 +264,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0 and not args.profile_only:
-        cpu = cpu_baseline(wl, st, host_kv, focal, t_timed, args.cpu_seconds)
+        cpu = cpu_baseline(wl, st, Kd, Vd, Qall, focal, args.cpu_seconds)
 
     line = {
         "metric": "decode-step attention us (all layers) + HBM GB/s, tau=0.05 vs full attention",
@@ -290,40 +290,76 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, st, host_kv, focal_gpu, t_start, budget_s):
-    """The CPU oracle, as written, timed on a bounded sample of the same run."""
+def cpu_baseline(wl, st, Kd, Vd, Qall, focal_gpu, budget_s):
+    """The CPU oracle, as written, timed on a bounded sample of the same run.
+
+    Whole decode steps when every layer's cache fits comfortably in host
+    memory as float64 (the 7B-like workloads); otherwise one focal and one
+    non-focal layer of one pruned step are timed and the step time is
+    extrapolated to all layers.
+    """
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    from oracle import DecodeOracle
+    from oracle import DecodeOracle, full_attention, sparse_attention, image_scores, kept_count, select_top
 
-    orc = DecodeOracle(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads,
-                       num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, tau=wl.tau,
-                       num_focal=wl.num_focal, warmup_steps=wl.warmup_steps)
-    kv64 = [(k.astype(np.float64), v.astype(np.float64)) for k, v, _ in host_kv]
-    qs = [q for _, _, q in host_kv]
-    t0 = time.time()
-    for t in range(wl.warmup_steps):
-        orc.step(t, lambda l: qs[l][t].astype(np.float64), lambda l: kv64[l], st.lens(t))
-    warm_s = time.time() - t0
-    times = []
-    t = wl.warmup_steps
-    begin = time.time()
-    while time.time() - begin < budget_s and t < qs[0].shape[0]:
+    L = wl.num_layers
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    layer_bytes = Kd[0].numel() * 8 * 2
+    if L * layer_bytes < 4e9:
+        kv64 = [(host(k), host(v)) for k, v in zip(Kd, Vd)]
+        q_of = lambda t: (lambda l: host(Qall[t, l]))  # noqa: E731
+        orc = DecodeOracle(num_layers=L, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                           head_dim=wl.head_dim, tau=wl.tau, num_focal=wl.num_focal,
+                           warmup_steps=wl.warmup_steps)
+        t0 = time.time()
+        for t in range(wl.warmup_steps):
+            orc.step(t, q_of(t), lambda l: kv64[l], st.lens(t))
+        warm_s = time.time() - t0
+        times = []
+        t = wl.warmup_steps
+        begin = time.time()
+        while time.time() - begin < budget_s and t < Qall.shape[0]:
+            s0 = time.time()
+            orc.step(t, q_of(t), lambda l: kv64[l], st.lens(t))
+            times.append(time.time() - s0)
+            t += 1
+        us = float(np.median(times)) * 1e6 if times else None
+        log(f"cpu oracle: warm-up {warm_s:.1f}s, {len(times)} pruned steps, median {us:.0f} us/step, "
+            f"focal {[int(c) for c in orc.focal]} (gpu {focal_gpu})")
+        sample = (f"float64 numpy oracle: {wl.warmup_steps} warm-up steps then {len(times)} pruned "
+                  f"decode steps (all {L} layers) of the same workload; median per pruned step")
+    else:
+        t = wl.warmup_steps
+        lens = st.lens(t)
+        scale = 1.0 / math.sqrt(wl.head_dim)
+        lf = int(focal_gpu[0])
+        ln = next(l for l in range(L) if l not in focal_gpu)
+        Kf, Vf, qf = host(Kd[lf]), host(Vd[lf]), host(Qall[t, lf])
         s0 = time.time()
-        orc.step(t, lambda l: qs[l][t].astype(np.float64), lambda l: kv64[l], st.lens(t))
-        times.append(time.time() - s0)
-        t += 1
-    us = float(np.median(times)) * 1e6 if times else None
-    log(f"cpu oracle: warm-up {warm_s:.1f}s, {len(times)} pruned steps, median {us:.0f} us/step, "
-        f"focal {list(orc.focal)} (gpu {focal_gpu})")
+        sets = []
+        for b in range(wl.batch):
+            n, length = int(lens[b, 0]), int(lens[b, 1])
+            _, p = full_attention(qf[b], Kf[b], Vf[b], length, scale)
+            sets.append(select_top(image_scores(p, n), kept_count(wl.tau, n)))
+        t_focal = time.time() - s0
+        del Kf, Vf
+        Kn, Vn, qn = host(Kd[ln]), host(Vd[ln]), host(Qall[t, ln])
+        s0 = time.time()
+        for b in range(wl.batch):
+            n, length = int(lens[b, 0]), int(lens[b, 1])
+            sparse_attention(qn[b], Kn[b], Vn[b], sets[b], n, length, scale)
+        t_sparse = time.time() - s0
+        C = len(focal_gpu)
+        us = (C * t_focal + (L - C) * t_sparse) * 1e6
+        log(f"cpu oracle (sampled layers): focal layer {t_focal:.2f}s, non-focal layer {t_sparse:.2f}s, "
+            f"step estimate {us / 1e6:.1f}s")
+        sample = (f"float64 numpy oracle on one focal and one non-focal layer of pruned step "
+                  f"{t}, extrapolated to {C} focal + {L - C} non-focal layers")
     return {"value": round(us, 1) if us else None, "unit": "us/step", "cores": threads,
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle: {wl.warmup_steps} warm-up steps then {len(times)} "
-                      f"pruned decode steps (all {wl.num_layers} layers) of the same workload; "
-                      f"median per pruned step"}
+            "kind": "oracle", "sample": sample}
 
 
 if __name__ == "__main__":

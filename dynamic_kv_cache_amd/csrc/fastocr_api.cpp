@@ -40,18 +40,15 @@ int env_int(const char* name, int dflt) {
 }
 
 // Rows per split for a pass that visits at most `rows` rows per (sequence,
-// KV head).  A split is 128, 256 or 512 rows (1, 2 or 4 tiles per wave in
-// one round), or whole rounds beyond that: the smallest size that still
-// gives about `target` workgroups, so small batches spread over many CUs
-// (one CU streams only ~60 GB/s) and large ones read long runs per
-// workgroup.  At most kMaxMergeSplits splits.
+// KV head): whole rounds (kRowsPerRound rows, one tile group per wave),
+// the fewest that still give about `target` workgroups, so a small batch
+// spreads over many CUs (one CU streams only ~60 GB/s) and a large one
+// reads long runs per workgroup.  At most kMaxMergeSplits splits.
 int plan_rows_per_split(int64_t pairs, int rows, int target, const char* env) {
   int R = env_int(env, 0);
   if (R <= 0) {
     const int64_t want = (pairs * (int64_t)std::max(rows, 1) + target - 1) / target;
-    R = 128;
-    while (R < want && R < kRowsPerRound) R *= 2;
-    if (want > kRowsPerRound) R = (int)align_up((size_t)want, kRowsPerRound);
+    R = (int)align_up((size_t)std::max<int64_t>(want, 1), kRowsPerRound);
   } else {
     R = (int)align_up((size_t)R, kTileRows);
   }
@@ -330,7 +327,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->phase = c.mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
 
   const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
-  const int target = 2 * num_cu;
+  const int target = 3 * num_cu;  // three resident split workgroups per CU
   h->full_R = plan_rows_per_split(pairs, c.max_seq_len, target, "FASTOCR_FULL_ROWS");
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
   int sparse_rows = c.max_seq_len;

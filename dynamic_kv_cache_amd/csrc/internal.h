@@ -18,15 +18,15 @@ enum SplitKind : int {
 // kTilesPerWave of them before computing any; a workgroup is kSplitWaves
 // waves, so one round of a workgroup covers kRowsPerRound cache rows.
 constexpr int kTileRows = 16;
-constexpr int kSplitWaves = 8;
-constexpr int kTilesPerWave = 4;
+constexpr int kSplitWaves = 4;
+constexpr int kTilesPerWave = 2;
 constexpr int kRowsPerRound = kTileRows * kSplitWaves * kTilesPerWave;
 constexpr int kSplitThreads = kSplitWaves * 64;
 constexpr int kMergeThreads = 256;
 constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
 constexpr int kMaxHeads = 128;
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkRegKeys = 8;  // keys per thread the top-k holds in registers
+constexpr int kTopkRegKeys = 16;  // keys per thread the top-k holds in registers
 
 struct SplitParams {
   const void* q;          // [B, Hq, D]

@@ -30,10 +30,11 @@
 // Because a contraction may visit its index in any order, the d index is
 // permuted so every lane's operands come straight from global memory with
 // no LDS transpose:
-//   QK: lane (c = lane%16, g = lane/16) loads the contiguous slice
-//       K[row c][g*d/4, (g+1)*d/4) and the same slice of its query head c;
-//       MFMA number kk contracts elements kk*4..kk*4+3 of those slices (bf16
-//       16x16x16) or element kk (fp32 16x16x4).
+//   QK: lane (c = lane%16, g = lane/16) loads the 16-byte pieces i*4 + g of
+//       K[row c] (so the 4 lane groups read 64 contiguous bytes per load)
+//       and the same pieces of its query head c; MFMA number kk contracts
+//       elements kk*4..kk*4+3 of those slices (bf16 16x16x16) or element kk
+//       (fp32 16x16x4).
 //   PV: lane (c, g) loads rows 4g..4g+3 of the tile, each the contiguous
 //       slice [c*d/16, (c+1)*d/16); MFMA number db uses element db of each
 //       row, so output lane (c, g) ends up holding head c's outputs for
@@ -54,6 +55,13 @@
 namespace fastocr {
 
 typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Two 32-bit words holding bf16 pairs, as an MFMA bf16x4 operand (no data
+// movement).
+__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x4_t, u32x2_t{lo, hi});
+}
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -94,6 +102,22 @@ __device__ __forceinline__ bool seq_extent(const int32_t* lens, int b, int S, in
 // the text rows [n, len).
 __device__ __forceinline__ int kept_rows(const int32_t* sel_cnt, int b, int n, int k_stride) {
   return min(max(sel_cnt[b], 0), min(n, k_stride));
+}
+
+// This lane's slice of a K row (or of its query row): 16-byte pieces
+// i*4 + grp of the row, i = 0 .. KW/4 - 1.  The four lane groups of a column
+// therefore read 64 contiguous bytes per load instruction.
+template <typename T, int KW>
+__device__ __forceinline__ void load_slice(uint32_t* dst, const T* row, int grp) {
+  constexpr int PIECE = 16 / (int)sizeof(T);  // elements per 16-byte piece
+#pragma unroll
+  for (int i = 0; i < KW / 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + (i * 4 + grp) * PIECE);
+    dst[4 * i] = v.x;
+    dst[4 * i + 1] = v.y;
+    dst[4 * i + 2] = v.z;
+    dst[4 * i + 3] = v.w;
+  }
 }
 
 template <typename T>
@@ -326,7 +350,7 @@ __device__ __forceinline__ int split_count(int rows, int rows_per_split, int gri
 }
 
 template <typename T, int D, int KIND>
-__global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p) {
+__global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int E = D / 4;                      // K/q elements per lane
   constexpr int KW = E * (int)sizeof(T) / 4;    // ... as 32-bit words
@@ -391,8 +415,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p
   // Query operand of this lane: head (kvh*G + col), elements [grp*E, grp*E+E).
   uint32_t qw[KW];
   if (col < G) {
-    const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D + grp * E;
-    load_words(qw, qp, KW);
+    const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D;
+    load_slice<T, KW>(qw, qp, grp);
   } else {
 #pragma unroll
     for (int i = 0; i < KW; ++i) qw[i] = 0u;
@@ -421,7 +445,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (r0 + u * kSplitWaves * kTileRows < end) {  // uniform over the wave
-        load_words(kw[u], Kb + (size_t)pk[u] * D + grp * E, KW);
+        load_slice<T, KW>(kw[u], Kb + (size_t)pk[u] * D, grp);
 #pragma unroll
         for (int j = 0; j < 4; ++j) load_words(vw[u][j], Vb + (size_t)pvr[u][j] * D + col * NDB, VW);
       }
@@ -440,11 +464,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p
       if constexpr (BF) {
 #pragma unroll
         for (int kk = 0; kk < E / 4; ++kk) {
-          const uint32_t a0 = kw[u][2 * kk], a1 = kw[u][2 * kk + 1];
-          const uint32_t b0 = qw[2 * kk], b1 = qw[2 * kk + 1];
-          const bf16x4_t a = bf16x4_t{(short)(a0 & 0xffff), (short)(a0 >> 16), (short)(a1 & 0xffff), (short)(a1 >> 16)};
-          const bf16x4_t bq = bf16x4_t{(short)(b0 & 0xffff), (short)(b0 >> 16), (short)(b1 & 0xffff), (short)(b1 >> 16)};
-          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bq, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(kw[u][2 * kk], kw[u][2 * kk + 1]),
+                                                        as_bf16x4(qw[2 * kk], qw[2 * kk + 1]), s, 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -506,15 +527,16 @@ __global__ __launch_bounds__(kSplitThreads) void split_attn_kernel(SplitParams p
       z += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       lsum += (pu[0] + pu[1]) + (pu[2] + pu[3]);
       if constexpr (BF) {
-        const bf16x4_t pv = bf16x4_t{(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+        const bf16x4_t pv = as_bf16x4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
+          // element db of rows j = 0..3: the low (even db) or high (odd db)
+          // halves of word db/2, packed pairwise with v_perm
           const int w = db >> 1;
-          uint32_t e[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) e[j] = (db & 1) ? (vw[u][j][w] >> 16) : (vw[u][j][w] & 0xffffu);
-          const bf16x4_t a = bf16x4_t{(short)e[0], (short)e[1], (short)e[2], (short)e[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pv, acc[db], 0, 0, 0);
+          const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo = __builtin_amdgcn_perm(vw[u][1][w], vw[u][0][w], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vw[u][3][w], vw[u][2][w], sel);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(lo, hi), pv, acc[db], 0, 0, 0);
         }
       } else {
 #pragma unroll

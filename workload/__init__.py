@@ -11,6 +11,7 @@ from .synth import (  # noqa: F401
     Workload,
     Structure,
     Generator,
+    DeviceGenerator,
     make_structure,
     SIGMA_SWEEP,
     TAU_SWEEP,

@@ -344,3 +344,73 @@ class Generator:
             mean_q = np.repeat(mean, g, axis=1)  # [S, Hq, d], head h -> kv head h // g
             q[:, b] = st.alpha[l] * mean_q + np.float32(wl.sigma) * eps[:, b]
         return _to_dtype(q, wl.dtype)
+
+
+# --------------------------------------------------------------------------
+# Device-side generation for the large workloads
+# --------------------------------------------------------------------------
+
+
+class DeviceGenerator:
+    """The same workload drawn on the GPU with torch's seeded generator.
+
+    Host generation of the 32B/72B-like caches (tens of GB) would take
+    minutes, so these tensors are drawn on the device: keys and values
+    N(0, 1) per (layer, tensor) stream, queries alpha * window-mean key +
+    sigma * N(0, I).  Values are produced in float32 and rounded to the
+    workload dtype.  The structure (lengths, windows, alphas) is the same as
+    the host generator's; only the random numbers differ.  Anything checked
+    on the CPU is read back from these device tensors.
+    """
+
+    def __init__(self, wl: Workload, structure: Optional[Structure] = None, device="cuda:0"):
+        import torch
+
+        self.torch = torch
+        self.wl = wl
+        self.st = structure if structure is not None else make_structure(wl)
+        self.device = torch.device(device)
+        self.io_dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        _, _, self._layer_ss = _seeds(wl)
+
+    def _seed(self, l: int, which: int) -> int:
+        return int(self._layer_ss[l].spawn(3)[which].generate_state(1, dtype=np.uint64)[0] % (2**63))
+
+    def _normal(self, shape, seed: int):
+        g = self.torch.Generator(device=self.device)
+        g.manual_seed(seed)
+        return self.torch.randn(shape, generator=g, device=self.device, dtype=self.torch.float32)
+
+    def layer_kv(self, l: int):
+        wl = self.wl
+        shape = (wl.batch, wl.num_kv_heads, self.st.max_seq_len, wl.head_dim)
+        K = self._normal(shape, self._seed(l, 0)).to(self.io_dtype)
+        V = self._normal(shape, self._seed(l, 1)).to(self.io_dtype)
+        return K, V
+
+    def layer_queries(self, l: int, steps: Sequence[int], K):
+        """Queries of layer l at the given steps, [len(steps), B, Hq, d] on the device."""
+        torch = self.torch
+        wl, st = self.wl, self.st
+        steps = list(steps)
+        T, B, Hq, Hkv, d = wl.steps, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+        g_ = Hq // Hkv
+        # the noise of all T steps is one block, so any subset sees the same numbers
+        eps = self._normal((T, B, Hq, d), self._seed(l, 2))[steps]
+        q = torch.empty((len(steps), B, Hq, d), dtype=torch.float32, device=self.device)
+        for b in range(B):
+            wins = [st.windows[b][int(t)] for t in steps]
+            wmax = max(len(w) for w in wins)
+            idx = np.zeros((len(steps), wmax), dtype=np.int64)
+            wgt = np.zeros((len(steps), wmax), dtype=np.float32)
+            for i, w in enumerate(wins):
+                idx[i, :len(w)] = w
+                wgt[i, :len(w)] = 1.0 / len(w)
+            idx_t = torch.from_numpy(idx).to(self.device)
+            wgt_t = torch.from_numpy(wgt).to(self.device)
+            Kb = K[b].float()  # [Hkv, S, d]
+            gathered = Kb[:, idx_t.reshape(-1)].reshape(Hkv, len(steps), wmax, d)
+            mean = (gathered * wgt_t[None, :, :, None]).sum(dim=2)  # [Hkv, S, d]
+            mean_q = mean.permute(1, 0, 2).repeat_interleave(g_, dim=1)  # [S, Hq, d]
+            q[:, b] = float(st.alpha[l]) * mean_q + float(wl.sigma) * eps[:, b]
+        return q.to(self.io_dtype)
