@@ -31,6 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+SPIN_PROBE_CYCLES = 2_000_000  # spin-kernel length used to convert cycles to ms
+EVENT_LAUNCHES_PER_CHUNK = 192  # timed launches queued behind one spin kernel
 
 
 def log(msg):
@@ -50,11 +52,137 @@ def parse():
                     help="budget of the CPU oracle baseline sample (0 disables it)")
     ap.add_argument("--profile-only", action="store_true",
                     help="skip the CPU baseline and the FULL comparison (for profiler runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with a 256 MiB device-to-device copy, the reference kernel that "
+                         "scales hardware byte counters")
+    ap.add_argument("--pmc-summary", default=None, nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 counter CSVs under the DIRs and exit (no GPU use)")
+    ap.add_argument("--trace-summary", default=None, nargs=2, metavar=("DIR", "COMMAND"),
+                    help="summarise a rocprofv3 kernel trace under DIR made by COMMAND and exit")
     return ap.parse_args()
+
+
+CAL_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "dynamic_kv_cache_amd", "csrc", "kernels.hip")
+
+
+def kernel_source_digest():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+KERNEL_CLASSES = ["full_split", "focal_split", "sparse_split", "merge", "topk"]
+
+
+def kernel_class(name):
+    """Timing class of a library kernel from its demangled name."""
+    import re
+    head = name.split("(")[0]
+    m = re.search(r"split_attn_kernel<[^,]+, \d+, (\d)", head)
+    if m:
+        return KERNEL_CLASSES[int(m.group(1))]
+    if "fastocr::merge_kernel<" in head:
+        return "merge"
+    if "fastocr::topk_kernel" in head:
+        return "topk"
+    return None
+
+
+def pmc_summary(directories):
+    """HBM bytes per dispatch of each library kernel from rocprofv3 counter
+    CSVs (one directory per counter pass).  Each counter is scaled by what
+    it reads for the calibration kernel (an int64 add that reads and writes
+    CAL_BYTES once each)."""
+    import csv
+    import glob
+    acc = {}
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    scale = {}
+    for (name, ctr), vals in acc.items():
+        if "add<long>" in name and np.mean(vals) > 0.5 * CAL_BYTES / 1024:
+            scale[ctr] = CAL_BYTES / 1024 / np.mean(vals)
+    print(f"kernel_source_sha256_16: {kernel_source_digest()}")
+    for ctr, f in sorted(scale.items()):
+        print(f"calibration_{ctr}: {f:.4f}  # {CAL_BYTES >> 20} MiB int64 add counts "
+              f"{CAL_BYTES / 1024 / f:.0f} KiB")
+    per = {}
+    for (name, ctr), vals in acc.items():
+        cls = kernel_class(name)
+        if cls is not None:
+            per.setdefault(cls, {})[ctr] = (np.mean(vals), len(vals))
+    for cls in [c for c in KERNEL_CLASSES if c in per]:
+        ctrs = per[cls]
+        for ctr, (v, n) in sorted(ctrs.items()):
+            print(f"{cls}.{ctr}_KiB_per_dispatch: {v:.1f}  # {n} dispatches")
+        if all(c in ctrs and c in scale for c in ("FETCH_SIZE", "WRITE_SIZE")):
+            hbm = sum(ctrs[c][0] * scale[c] * 1024 for c in ("FETCH_SIZE", "WRITE_SIZE"))
+            print(f"{cls}.hbm_bytes_per_launch: {hbm:.0f}")
+
+
+def trace_summary(directory, command):
+    """Per-kernel durations from a rocprofv3 --kernel-trace --stats run of
+    this script, beside the averages the same run measured with its own
+    dispatch events (bench.json in the same directory)."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    print(f"# command: {command}")
+    print(f"kernel_source_sha256_16: {kernel_source_digest()}")
+    bench = {}
+    bj = os.path.join(directory, "bench.json")
+    if os.path.exists(bj):
+        with open(bj) as f:
+            bench = json.loads(f.read().strip().splitlines()[-1])
+        print(f"# bench: value {bench.get('value')} {bench.get('unit')}, workload {bench['config'].get('name')}")
+    ev = bench.get("per_kernel", {})
+    print(f"# {'kernel class':14s} {'calls':>7s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} "
+          f"{'bench_event_avg_us':>18s}  name")
+    for path in stats:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                cls = kernel_class(r["Name"])
+                if cls is None:
+                    continue
+                e = ev.get(cls, {}).get("avg_us")
+                print(f"{cls:16s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:8.3f} "
+                      f"{float(r['MinNs']) / 1e3:8.3f} {float(r['MaxNs']) / 1e3:8.3f} "
+                      f"{(f'{e:.3f}' if e is not None else '-'):>18s}  {r['Name'].split('(')[0]}")
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/pmc_<workload>.txt), or None when there is none or the kernels
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.split("#", 1)[0]
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(vals[f"{kernel}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1])
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -145,6 +273,58 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    def spin_ms(cycles):
+        with torch.cuda.stream(stream):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            torch.cuda._sleep(cycles)
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    spin_ms(SPIN_PROBE_CYCLES)  # first launch of the spin kernel
+    cycles_per_ms = SPIN_PROBE_CYCLES / max(spin_ms(2 * SPIN_PROBE_CYCLES) - spin_ms(SPIN_PROBE_CYCLES), 1e-3)
+
+    def kernel_times(h, steps, out_hist):
+        """Per-kernel-class launch durations from HIP events.
+
+        Every launch records an event when its kernel completes, and a
+        launch's time is the interval since the previous completion.  Each
+        chunk of steps is queued behind a bounded spin kernel that outlasts
+        the host's enqueueing of the chunk, so the kernels run back to back
+        and those intervals are their durations (the first launch of a chunk,
+        which follows the spin, is not timed).
+        """
+        fo.fastocr_set_timing(h, True)
+        fo.fastocr_reset_timing(h)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            eager_step(h, steps[0], out_hist[0])  # sizing pass (launch count, host time)
+        host_ms = (time.perf_counter() - t0) * 1e3
+        per_step = max(sum(v["launches"] for v in fo.fastocr_get_timing(h).values()), 1)
+        chunk = max(1, EVENT_LAUNCHES_PER_CHUNK // per_step)
+        spin_target = 3.0 * host_ms * chunk + 2.0  # ms; the host needs about host_ms per step
+        spin = int(cycles_per_ms * spin_target)
+        fo.fastocr_reset_timing(h)
+        worst_host = 0.0
+        for c0 in range(1, len(steps), chunk):
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(spin)
+                t0 = time.perf_counter()
+                for i in range(c0, min(c0 + chunk, len(steps))):
+                    eager_step(h, steps[i], out_hist[i])
+                worst_host = max(worst_host, (time.perf_counter() - t0) * 1e3)
+            kt = fo.fastocr_get_timing(h)  # synchronises and accumulates
+        fo.fastocr_set_timing(h, False)
+        log(f"kernel timing: {len(steps) - 1} steps in chunks of {chunk}, each enqueued in at most "
+            f"{worst_host:.1f} ms behind a {spin_target:.1f} ms spin")
+        if worst_host > 0.8 * spin_target:
+            log("warning: the spin may have ended before a chunk was enqueued; kernel times include idle gaps")
+        return kt, len(steps) - 1
+
     results = {}
     outs = {}
     for mode in (["pruned"] if args.profile_only else ["pruned", "full"]):
@@ -160,36 +340,28 @@ def main():
         torch.cuda.synchronize()
         r = {"focal": focal}
         timed_steps = list(range(t_timed, t_events))
-        if not args.no_graph:
-            # capture one step (the capture itself advances the kept set by
-            # one step, so it runs at t_timed - 1's inputs into a scratch copy)
-            g = capture(h)
-            r["graph_ms"] = time_steps(h, timed_steps, g)
-            del g
-        else:
-            with torch.cuda.stream(stream):
-                for t in timed_steps:
-                    eager_step(h, t, out_stage)
-        # per-kernel event timing + recorded outputs on the next K steps
+        # capture one step (the capture itself advances the kept set by one
+        # step, so it runs at t_timed - 1's inputs into a scratch copy)
+        g = capture(h) if not args.no_graph else None
+        r["step_ms"] = time_steps(h, timed_steps, g)
+        del g
+        # per-kernel timing + recorded outputs on the next K steps
         out_hist = torch.empty((K, L, B, Hq, d), dtype=io, device=dev)
-        ev_steps = list(range(t_events, n_steps))
-        fo.fastocr_set_timing(h, True)
-        fo.fastocr_reset_timing(h)
-        with torch.cuda.stream(stream):
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ev0.record(stream)
-            for i, t in enumerate(ev_steps):
-                eager_step(h, t, out_hist[i])
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        r["eager_events_ms"] = ev0.elapsed_time(ev1) / K
-        r["kernels"] = fo.fastocr_get_timing(h)
-        fo.fastocr_set_timing(h, False)
+        r["kernels"], r["kernel_steps"] = kernel_times(h, list(range(t_events, n_steps)), out_hist)
         outs[mode] = out_hist.float()
         fo.fastocr_destroy(h)
         results[mode] = r
-        log(f"{mode}: graph {r.get('graph_ms')} ms/step, eager+events {r['eager_events_ms']:.3f} ms/step")
+        log(f"{mode}: {r['step_ms']:.4f} ms/step ({'eager' if args.no_graph else 'graph'})")
+
+    if args.calibrate_copy:
+        # int64 add: reads and writes CAL_BYTES once each with a kernel of its own
+        src = torch.empty(CAL_BYTES // 8, dtype=torch.int64, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {CAL_BYTES >> 20} MiB done")
 
     focal = results["pruned"]["focal"]
     ev_steps = list(range(t_events, n_steps))
@@ -207,14 +379,22 @@ def main():
     bytes_pruned = R * (C * rows_focal + (L - C) * rows_sparse)
     bytes_full = R * L * rows_focal
 
-    kp = results["pruned"]["kernels"]
-    kernel_sum_ms = sum(v["total_ms"] for v in kp.values()) / K
-    pr_ms = results["pruned"].get("graph_ms") or results["pruned"]["eager_events_ms"]
+    def per_step(r):
+        """Per kernel class: average launch time and launches per step."""
+        out = {}
+        for k, v in r["kernels"].items():
+            if v["timed"]:
+                out[k] = (v["total_ms"] / v["timed"], v["launches"] / r["kernel_steps"])
+        return out
+
+    kp = per_step(results["pruned"])
+    kernel_sum_ms = sum(a * n for a, n in kp.values())
+    pr_ms = results["pruned"]["step_ms"]
     value_us = pr_ms * 1e3
 
     # dominant kernel of the pruned step and its roofline
-    dom = max(kp, key=lambda k: kp[k]["total_ms"])
-    dom_avg_ms = kp[dom]["total_ms"] / max(kp[dom]["launches"], 1)
+    dom = max(kp, key=lambda k: kp[k][0] * kp[k][1])
+    dom_avg_ms = kp[dom][0]
     per_launch_bytes = {
         "focal_split": R * rows_focal,
         "sparse_split": R * rows_sparse,
@@ -224,16 +404,13 @@ def main():
         achieved = per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": None, "avg_launch_us": round(dom_avg_ms * 1e3, 3),
+                    "traffic": read_traffic(dom, wl.name), "avg_launch_us": round(dom_avg_ms * 1e3, 3),
                     "bytes_per_launch": int(per_launch_bytes)}
-    per_kernel = {k: {"avg_us": round(v["total_ms"] / max(v["launches"], 1) * 1e3, 3),
-                      "launches_per_step": v["launches"] / K,
-                      "us_per_step": round(v["total_ms"] / K * 1e3, 3)}
-                  for k, v in kp.items() if v["launches"]}
+    per_kernel = {k: {"avg_us": round(a * 1e3, 3), "launches_per_step": n, "us_per_step": round(a * n * 1e3, 3)}
+                  for k, (a, n) in kp.items()}
     extra = {
         "focal_layers": focal,
         "kernel_sum_us_per_step": round(kernel_sum_ms * 1e3, 2),
-        "eager_events_us_per_step": round(results["pruned"]["eager_events_ms"] * 1e3, 2),
         "algorithmic_MB_per_step": round(bytes_pruned / 1e6, 2),
         "GBps_vs_step_time": round(bytes_pruned / (pr_ms * 1e-3) / 1e9, 1),
         "GBps_vs_kernel_sum": round(bytes_pruned / (kernel_sum_ms * 1e-3) / 1e9, 1),
@@ -241,9 +418,8 @@ def main():
     }
     if "full" in results:
         fr = results["full"]
-        full_ms = fr.get("graph_ms") or fr["eager_events_ms"]
-        kf = fr["kernels"]
-        full_kernel_ms = sum(v["total_ms"] for v in kf.values()) / K
+        full_ms = fr["step_ms"]
+        full_kernel_ms = sum(a * n for a, n in per_step(fr).values())
         extra.update({
             "full_us_per_step": round(full_ms * 1e3, 2),
             "full_kernel_sum_us_per_step": round(full_kernel_ms * 1e3, 2),

@@ -214,7 +214,7 @@ def fastocr_set_timing(h: Handle, enable: bool) -> None:
 def fastocr_get_timing(h: Handle) -> Dict[str, Dict[str, float]]:
     tm = _abi.Timing()
     _check("fastocr_get_timing", lib().fastocr_get_timing(h.ptr, ctypes.byref(tm)))
-    return {name: {"total_ms": tm.total_ms[i], "launches": int(tm.launches[i])}
+    return {name: {"total_ms": tm.total_ms[i], "launches": int(tm.launches[i]), "timed": int(tm.timed[i])}
             for i, name in enumerate(KC_NAMES)}
 
 

@@ -68,7 +68,8 @@ class Info(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("total_ms", c_double * KC_COUNT), ("launches", c_int64 * KC_COUNT)]
+    _fields_ = [("total_ms", c_double * KC_COUNT), ("launches", c_int64 * KC_COUNT),
+                ("timed", c_int64 * KC_COUNT)]
 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfastocr.so")

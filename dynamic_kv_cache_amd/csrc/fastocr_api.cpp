@@ -26,9 +26,9 @@ namespace {
 
 enum Phase : int { PHASE_WARMUP = 0, PHASE_WARMUP_DONE = 1, PHASE_PRUNED = 2, PHASE_FULL = 3 };
 
-struct EventPair {
+struct TimedLaunch {
   int cls;
-  hipEvent_t a, b;
+  hipEvent_t end;  // recorded by the dispatch itself when the kernel completes
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -64,6 +64,7 @@ struct fastocr_handle {
   int device = 0;
   int G = 0, D = 0, n_cap = 0, n_stride = 0, k_max = 0;
   int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
+
   float scale_log2 = 0.f;
 
   int step = 0, next_layer = 0, phase = PHASE_WARMUP;
@@ -87,7 +88,7 @@ struct fastocr_handle {
   int32_t* lens_shadow = nullptr;  // [B, 2] lens of the last warm-up step
 
   bool timing = false;
-  std::vector<EventPair> events;
+  std::vector<TimedLaunch> events;
   size_t ev_used = 0;
   fastocr_timing timing_acc{};
 };
@@ -100,29 +101,24 @@ int fail_hip(fastocr_handle* h, hipError_t e) {
   return FASTOCR_ERR_HIP;
 }
 
-// Launch helper: optional event pair around the launch for kernel timing.
+// Launch helper: with timing on, the dispatch itself records an event when
+// the kernel completes (no marker packet is queued).
 template <typename F>
 int timed(fastocr_handle* h, int cls, F&& launch) {
-  EventPair* ep = nullptr;
+  LaunchTiming lt;
   if (h->timing) {
     if (h->ev_used == h->events.size()) {
-      EventPair np{cls, nullptr, nullptr};
-      if (hipEventCreate(&np.a) != hipSuccess || hipEventCreate(&np.b) != hipSuccess)
+      // timing-only event: no system-scope fence (cache write-back) on record
+      TimedLaunch nl{cls, nullptr};
+      if (hipEventCreateWithFlags(&nl.end, hipEventDisableSystemFence) != hipSuccess)
         return fail_hip(h, hipErrorOutOfMemory);
-      h->events.push_back(np);
+      h->events.push_back(nl);
     }
-    ep = &h->events[h->ev_used++];
-    ep->cls = cls;
-    hipError_t e = hipEventRecord(ep->a, h->stream);
-    if (e != hipSuccess) return fail_hip(h, e);
+    TimedLaunch& tl = h->events[h->ev_used++];
+    tl.cls = cls;
+    lt.stop = tl.end;
   }
-  hipError_t e = launch();
-  if (e != hipSuccess) return fail_hip(h, e);
-  if (ep) {
-    e = hipEventRecord(ep->b, h->stream);
-    if (e != hipSuccess) return fail_hip(h, e);
-  }
-  return FASTOCR_OK;
+  return fail_hip(h, launch(lt));
 }
 
 SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const void* v,
@@ -165,7 +161,7 @@ int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens) {
   t.idx_stride = h->k_max;
   t.cnt = h->sel_cnt;
   t.status = h->status;
-  return timed(h, FASTOCR_KC_TOPK, [&] { return launch_topk(t, h->stream); });
+  return timed(h, FASTOCR_KC_TOPK, [&](const LaunchTiming& lt) { return launch_topk(t, h->stream, lt); });
 }
 
 MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool sparse) {
@@ -199,8 +195,8 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
   const bool focal = scores_dst != nullptr;
   SplitParams sp = split_params(h, q, k, v, lens, out, false);
   sp.direct = 0;
-  int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&] {
-    return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream);
+  int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&](const LaunchTiming& lt) {
+    return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream, lt);
   });
   if (rc) return rc;
   MergeParams mp = merge_params(h, lens, out, false);
@@ -210,7 +206,8 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
     mp.scores = scores_dst;
     mp.score_blocks = (h->n_stride + kMergeThreads - 1) / kMergeThreads;
   }
-  rc = timed(h, FASTOCR_KC_MERGE, [&] { return launch_merge(c.dtype, c.head_dim, mp, h->stream); });
+  rc = timed(h, FASTOCR_KC_MERGE,
+             [&](const LaunchTiming& lt) { return launch_merge(c.dtype, c.head_dim, mp, h->stream, lt); });
   if (rc || !topk) return rc;
   return run_topk(h, scores_dst, lens);
 }
@@ -223,12 +220,13 @@ int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, c
   const fastocr_config& c = h->cfg;
   SplitParams sp = split_params(h, q, k, v, lens, out, true);
   sp.direct = 1;
-  int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&] {
-    return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream);
+  int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&](const LaunchTiming& lt) {
+    return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream, lt);
   });
   if (rc || h->sparse_splits <= 1) return rc;
   MergeParams mp = merge_params(h, lens, out, true);
-  return timed(h, FASTOCR_KC_MERGE, [&] { return launch_merge(c.dtype, c.head_dim, mp, h->stream); });
+  return timed(h, FASTOCR_KC_MERGE,
+               [&](const LaunchTiming& lt) { return launch_merge(c.dtype, c.head_dim, mp, h->stream, lt); });
 }
 
 void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {
@@ -476,10 +474,7 @@ int fastocr_destroy(fastocr_handle* h) {
   if (!h) return FASTOCR_OK;
   int rc = FASTOCR_OK;
   if (hipStreamSynchronize(h->stream) != hipSuccess) rc = FASTOCR_ERR_HIP;
-  for (auto& ep : h->events) {
-    (void)hipEventDestroy(ep.a);
-    (void)hipEventDestroy(ep.b);
-  }
+  for (auto& ev : h->events) (void)hipEventDestroy(ev.end);
   if (h->arena && hipFree(h->arena) != hipSuccess) rc = FASTOCR_ERR_HIP;
   delete h;
   return rc;
@@ -578,12 +573,16 @@ int fastocr_get_timing(fastocr_handle* h, fastocr_timing* out) {
   if (h->poisoned) return FASTOCR_ERR_STATE;
   hipError_t e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) return fail_hip(h, e);
+  // a launch's time: from the previous timed launch's end to its own end
   for (size_t i = 0; i < h->ev_used; ++i) {
+    const int cls = h->events[i].cls;
+    h->timing_acc.launches[cls] += 1;
+    if (i == 0) continue;
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, h->events[i].a, h->events[i].b);
+    e = hipEventElapsedTime(&ms, h->events[i - 1].end, h->events[i].end);
     if (e != hipSuccess) return fail_hip(h, e);
-    h->timing_acc.total_ms[h->events[i].cls] += ms;
-    h->timing_acc.launches[h->events[i].cls] += 1;
+    h->timing_acc.total_ms[cls] += ms;
+    h->timing_acc.timed[cls] += 1;
   }
   h->ev_used = 0;
   *out = h->timing_acc;

@@ -27,6 +27,7 @@ constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keep
 constexpr int kMaxHeads = 128;
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkRegKeys = 16;  // keys per thread the top-k holds in registers
+constexpr int kTopkCand = 64;      // a k-th-key bin this small is ranked pairwise (one wave)
 
 struct SplitParams {
   const void* q;          // [B, Hq, D]
@@ -77,9 +78,18 @@ struct TopkParams {
   int32_t* status;        // may be null
 };
 
+// Optional timing: events recorded by the dispatch itself (start: when the
+// dispatch is processed; stop: when the kernel completes).
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p,
-                        hipStream_t stream);
-hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream);
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+                        hipStream_t stream, const LaunchTiming& timing = LaunchTiming{});
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
+                        const LaunchTiming& timing = LaunchTiming{});
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream,
+                       const LaunchTiming& timing = LaunchTiming{});
 
 }  // namespace fastocr

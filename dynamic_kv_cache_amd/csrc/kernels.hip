@@ -45,6 +45,7 @@
 // before computing any, and rescales its running softmax state once per
 // round.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -197,15 +198,41 @@ __device__ __forceinline__ int device_kept_count(double tau, int n) {
 
 struct TopkShared {
   unsigned int hist[kTopkThreads / 64][256];  // one histogram per wave
-  unsigned int wave_sum[kTopkThreads / 64];
+  alignas(16) unsigned int wave_sum[kTopkThreads / 64];
+  alignas(16) unsigned int wave_sum2[kTopkThreads / 64];
+  unsigned int cand_key[kTopkCand];
+  int cand_idx[kTopkCand];
   unsigned int prefix;
   int remaining;
+  int bin_count;
+  int ncand;
+  unsigned int theta;
+  int need_eq;
 };
+
+// Append (key, index) to the candidate list if the key lies in the k-th
+// key's bin (one LDS atomic per wave).
+__device__ __forceinline__ void gather_key(unsigned int key, bool valid, int index, unsigned int mask,
+                                           unsigned int prefix, TopkShared& sh, int lane) {
+  const bool take = valid && (key & mask) == prefix;
+  const unsigned long long tm = __ballot(take);
+  if (tm == 0ull) return;
+  const int leader = __ffsll((unsigned long long)tm) - 1;
+  int slot0 = 0;
+  if (lane == leader) slot0 = atomicAdd(&sh.ncand, __popcll(tm));
+  slot0 = __builtin_amdgcn_readlane(slot0, leader);
+  if (take) {
+    const int slot = slot0 + __popcll(tm & ((1ull << lane) - 1ull));
+    sh.cand_key[slot] = key;
+    sh.cand_idx[slot] = index;
+  }
+}
 
 // Count one key into this wave's histogram of digit (key >> shift) & 255,
 // if its higher digits match `prefix` under `mask`.  Keys of one wave mostly
 // share their leading digits, so lanes with the first pending lane's digit
-// are counted by one atomic; the remaining lanes add one each.
+// are counted by one atomic; the remaining lanes add one each.  (Repeating
+// the aggregation for further digits measured slower.)
 __device__ __forceinline__ void hist_key(unsigned int key, bool valid, int shift, unsigned int mask,
                                          unsigned int prefix, unsigned int* hist, int lane) {
   const unsigned int dig = (key >> shift) & 255u;
@@ -221,31 +248,44 @@ __device__ __forceinline__ void hist_key(unsigned int key, bool valid, int shift
   }
 }
 
+// Sum of the first `wave` entries of a per-wave array of kTopkThreads / 64
+// values, read as 128-bit words.
+__device__ __forceinline__ unsigned int sum_before(const unsigned int* v, int wave) {
+  unsigned int acc = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkThreads / 256; ++q) {
+    const uint4 w = reinterpret_cast<const uint4*>(v)[q];
+    acc += (4 * q + 0 < wave ? w.x : 0u) + (4 * q + 1 < wave ? w.y : 0u) + (4 * q + 2 < wave ? w.z : 0u) +
+           (4 * q + 3 < wave ? w.w : 0u);
+  }
+  return acc;
+}
+
 // Top-k of the non-negative float keys[0, n) by one kTopkThreads workgroup.
-// Thread t owns keys [t*per, t*per + per), in registers when per is small,
+// Thread t owns keys [t*per, t*per + per) of the row's capacity n_cap >= n,
+// in registers when per is small (loaded before n and k are known),
 // re-read from memory otherwise.  A 4-pass radix select (8 bits per pass,
 // most significant first; the IEEE bits of a non-negative float order like
 // its value) finds the k-th largest key theta and how many keys equal to
 // theta are kept; one workgroup prefix sum then places every kept index, so
 // the output is in ascending index order and ties at theta go to the lowest
 // indices.
-__device__ void block_topk(const unsigned int* __restrict__ keys, int n, int k,
-                           int32_t* __restrict__ out, TopkShared& sh) {
+__device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int n, int k,
+                           int32_t* __restrict__ out, TopkShared& sh, const unsigned int (&reg)[kTopkRegKeys]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
   const int base = tid * per;
   const int mine = max(0, min(per, n - base));
   const bool in_regs = per <= kTopkRegKeys;
-  unsigned int reg[kTopkRegKeys];
-#pragma unroll
-  for (int i = 0; i < kTopkRegKeys; ++i) reg[i] = in_regs ? keys[min(base + i, n - 1)] : 0u;
 
   unsigned int prefix = 0u, mask = 0u;
   int remaining = k;
+  bool ranked = false;
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0u;
+    if (tid == 0) sh.ncand = 0;
     __syncthreads();
     if (in_regs) {
 #pragma unroll
@@ -266,20 +306,64 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n, int k,
     }
     __syncthreads();
     if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += sh.wave_sum[w];
+      incl += sum_before(sh.wave_sum, wave);
       const unsigned int above = incl - c;  // keys with a larger digit
       if (above < (unsigned int)remaining && (unsigned int)remaining <= incl) {
         sh.prefix = prefix | ((unsigned int)(255 - tid) << shift);
         sh.remaining = remaining - (int)above;
+        sh.bin_count = (int)c;
       }
     }
     __syncthreads();
     prefix = sh.prefix;
     remaining = sh.remaining;
     mask |= 255u << shift;
+    if (pass < 3 && sh.bin_count <= kTopkCand) {
+      ranked = true;
+      break;
+    }
   }
-  const unsigned int theta = prefix;  // k-th largest key
-  const int need_eq = remaining;      // keys equal to theta to keep, lowest index first
+
+  if (ranked) {
+    // The k-th key's bin is small: gather it and rank its keys pairwise by
+    // (value descending, index ascending); the key of rank remaining - 1 is
+    // theta.
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kTopkRegKeys; ++i)
+        if (i < per) gather_key(reg[i], i < mine, base + i, mask, prefix, sh, lane);
+    } else {
+#pragma unroll 1
+      for (int i = 0; i < per; ++i)
+        gather_key(keys[min(base + i, n - 1)], i < mine, base + i, mask, prefix, sh, lane);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane c holds candidate c; every candidate is compared with all
+      // others through lane reads (no LDS round trips in the loop)
+      const int nc = __builtin_amdgcn_readfirstlane(sh.ncand);  // uniform
+      const unsigned int kc = lane < nc ? sh.cand_key[lane] : 0u;
+      const int ic = lane < nc ? sh.cand_idx[lane] : 0;
+      int greater = 0, before = 0;
+      for (int j = 0; j < nc; ++j) {
+        const unsigned int kj = (unsigned int)__builtin_amdgcn_readlane((int)kc, j);
+        const int ij = __builtin_amdgcn_readlane(ic, j);
+        greater += kj > kc ? 1 : 0;
+        before += (kj == kc && ij < ic) ? 1 : 0;
+      }
+      if (lane < nc && greater + before == remaining - 1) {
+        sh.theta = kc;
+        sh.need_eq = remaining - greater;
+      }
+    }
+  } else if (tid == 0) {
+    // every digit fixed: the remaining keys all equal theta
+    sh.theta = prefix;
+    sh.need_eq = remaining;
+  }
+  __syncthreads();
+  const unsigned int theta = sh.theta;  // k-th largest key
+  const int need_eq = sh.need_eq;       // keys equal to theta to keep, lowest index first
 
   unsigned int gt = 0, eq = 0;
   if (in_regs) {
@@ -296,16 +380,19 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n, int k,
       eq += key == theta ? 1u : 0u;
     }
   }
-  // both counts stay below 2^16 for n < 65536, so one packed scan serves both
-  const unsigned int v = (gt << 16) | eq;
-  unsigned int incl = wave_incl_scan(v);
+  // exclusive prefix sums of both counts over the workgroup
+  unsigned int gt_incl = wave_incl_scan(gt);
+  unsigned int eq_incl = wave_incl_scan(eq);
   __syncthreads();
-  if (lane == 63) sh.wave_sum[wave] = incl;
+  if (lane == 63) {
+    sh.wave_sum[wave] = gt_incl;
+    sh.wave_sum2[wave] = eq_incl;
+  }
   __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += sh.wave_sum[w];
-  const unsigned int excl = incl - v;
-  int eq_seen = (int)(excl & 0xffffu);
-  int pos = (int)(excl >> 16) + min(eq_seen, need_eq);
+  gt_incl += sum_before(sh.wave_sum, wave);
+  eq_incl += sum_before(sh.wave_sum2, wave);
+  int eq_seen = (int)(eq_incl - eq);
+  int pos = (int)(gt_incl - gt) + min(eq_seen, need_eq);
 #pragma unroll 1
   for (int i = 0; i < mine; ++i) {
     unsigned int key = 0u;
@@ -324,12 +411,26 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n, int k,
   }
 }
 
-__device__ __forceinline__ void topk_sequence(const float* keys, int n, double tau, int idx_stride,
-                                              int32_t* out, int32_t* cnt, TopkShared& sh) {
+// Top-k of one sequence's scores: the keys this thread owns are loaded from
+// the row's capacity before the sequence extent (and so k) is read.
+__device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, const int32_t* lens, int b,
+                                              double tau, int idx_stride, int32_t* out, int32_t* cnt,
+                                              int32_t* status, TopkShared& sh) {
+  const unsigned int* keys = reinterpret_cast<const unsigned int*>(scores);
+  const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
+  const int base = threadIdx.x * per;
+  unsigned int reg[kTopkRegKeys];
+  if (per <= kTopkRegKeys) {
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; ++i) reg[i] = keys[min(base + i, n_cap - 1)];
+  }
+  const int n0 = lens[2 * b];
+  const int n = min(max(n0, 0), min(max(lens[2 * b + 1], 0), n_cap));
+  if (n0 != n && threadIdx.x == 0 && status) atomicOr(status, FASTOCR_FLAG_LENS_CLAMPED);
   const int k = min(device_kept_count(tau, n), idx_stride);
   if (threadIdx.x == 0) *cnt = k;
   if (k == 0) return;
-  block_topk(reinterpret_cast<const unsigned int*>(keys), n, k, out, sh);
+  block_topk(keys, n_cap, n, k, out, sh, reg);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,20 +450,21 @@ __device__ __forceinline__ int split_count(int rows, int rows_per_split, int gri
   return nsplit;
 }
 
-template <typename T, int D, int KIND>
-__global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParams p) {
+template <typename T, int D, int KIND, int NW, int TPW>
+__global__ __launch_bounds__(NW * 64, NW == kSplitWaves ? 3 : 1) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
+  constexpr int NT = NW * 64;                   // threads
+  constexpr int RPR = NW * TPW * kTileRows;     // rows per round
   constexpr int E = D / 4;                      // K/q elements per lane
   constexpr int KW = E * (int)sizeof(T) / 4;    // ... as 32-bit words
   constexpr int NDB = D / 16;                   // PV d-blocks = V elements per row per lane
   constexpr int VW = NDB * (int)sizeof(T) / 4;  // V words per row per lane
-  constexpr int TPW = kTilesPerWave;
   constexpr int HH = 8;                         // heads per LDS merge round
   constexpr int OST = D + 1;                    // padded LDS row of partial outputs
 
-  __shared__ float s_stat[kSplitWaves][16][4];
+  __shared__ float s_stat[NW][16][4];
   __shared__ float4 s_head[16];
-  __shared__ float s_o[kSplitWaves][HH][OST];
+  __shared__ float s_o[NW][HH][OST];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -374,45 +476,17 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
   const int grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
 
-  int n, len;
-  const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
-  const bool reporter = split == 0 && kvh == 0 && tid == 0;
-  if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
-  const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
-  const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
-  const int nsplit = split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
-  const bool direct = p.direct && nsplit <= 1;
   const int begin = split * p.rows_per_split;
-  if (begin >= rows) {
-    if (direct && split == 0) {  // no rows at all: zero output
-      T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
-      for (int i = tid; i < G * D; i += kSplitThreads) store_out<T>(out + i, 0.f);
-    }
-    return;
-  }
-  const int end = min(begin + p.rows_per_split, rows);
-
   const size_t row_base = ((size_t)b * p.Hkv + kvh) * (size_t)p.S;
   const T* __restrict__ Kb = reinterpret_cast<const T*>(p.k) + row_base * D;
   const T* __restrict__ Vb = reinterpret_cast<const T*>(p.v) + row_base * D;
   const int32_t* __restrict__ selb = (KIND == KIND_SPARSE) ? p.sel + (size_t)b * p.k_stride : nullptr;
 
-  // Virtual row -> cache row.  Branch-free, so the index loads of a round
-  // are all in flight together; a kept index outside [0, n) is clamped and
-  // reported once at the end.
-  bool bad_index = false;
-  auto phys = [&](int r) -> int {
-    if (KIND == KIND_SPARSE) {
-      const int j = selb[min(r, p.k_stride - 1)];
-      const bool img = r < kept;
-      bad_index |= img && (j < 0 || j >= n);
-      const int jc = min(max(j, 0), max(n - 1, 0));
-      return img ? jc : n + (r - kept);
-    }
-    return r;
-  };
-
-  // Query operand of this lane: head (kvh*G + col), elements [grp*E, grp*E+E).
+  // Loads that do not depend on the sequence extent are issued before it is
+  // read, so they are in flight together: the query slice and, for the first
+  // round, the kept indices (sparse kind) or the K/V rows themselves (full
+  // kinds).  Any row below S lies inside the cache allocation; rows past the
+  // extent get zero weight and their V values are zeroed once it is known.
   uint32_t qw[KW];
   if (col < G) {
     const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D;
@@ -421,42 +495,87 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
 #pragma unroll
     for (int i = 0; i < KW; ++i) qw[i] = 0u;
   }
+  const int r_first = begin + wave * kTileRows;  // this wave's first tile row
+  uint32_t kw[TPW][KW];
+  uint32_t vw[TPW][4][VW];
+  int jpre[TPW][5];  // sparse: kept indices of the first round's rows
+  if constexpr (KIND == KIND_SPARSE) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r_first + u * NW * kTileRows;
+      jpre[u][0] = selb[min(tile + col, p.k_stride - 1)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) jpre[u][1 + j] = selb[min(tile + 4 * grp + j, p.k_stride - 1)];
+    }
+  } else {
+    const int spec_end = min(begin + p.rows_per_split, p.S);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r_first + u * NW * kTileRows;
+      if (tile < spec_end) {  // uniform over the wave
+        load_slice<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          load_words(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
+      }
+    }
+  }
+
+  int n, len;
+  const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
+  const bool reporter = split == 0 && kvh == 0 && tid == 0;
+  if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
+  const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
+  const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
+  const int nsplit = split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
+  const bool direct = p.direct && nsplit <= 1;
+  if (begin >= rows) {
+    if (direct && split == 0) {  // no rows at all: zero output
+      T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
+      for (int i = tid; i < G * D; i += NT) store_out<T>(out + i, 0.f);
+    }
+    return;
+  }
+  const int end = min(begin + p.rows_per_split, rows);
+
+  // Virtual row -> cache row (sparse kind), given the kept index j loaded
+  // for row r.  Branch-free, so the index loads of a round are all in
+  // flight together; a kept index outside [0, n) is clamped and reported
+  // once at the end.  Rows at or past `end` only need to stay inside the
+  // allocation.
+  bool bad_index = false;
+  auto sparse_row = [&](int r, int j) -> int {
+    const bool img = r < kept;
+    bad_index |= img && r < end && (j < 0 || j >= n);
+    const int jc = min(max(j, 0), max(n - 1, 0));
+    return img ? jc : min(n + (r - kept), p.S - 1);
+  };
 
   float m_run = -INFINITY, z = 0.f, lsum = 0.f, zt = 0.f;
   f32x4_t acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Round r covers rows [begin + r*kRowsPerRound, +kRowsPerRound); tile u of
-  // wave w in a round starts at row (u*kSplitWaves + w)*16, so a split of
-  // 128 / 256 / 512 rows gives every wave 1 / 2 / 4 tiles.
-  for (int r0 = begin + wave * kTileRows; r0 < end; r0 += kRowsPerRound) {
-    // ---- cache rows of this round's tiles, then all their loads
-    int pk[TPW], pvr[TPW][4];
+  // One round: rows [r0, r0 + RPR) of this wave's tiles, whose K/V words
+  // are in kw / vw.
+  auto round = [&](int r0, uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW]) {
+    // V rows past the end of the split carry zero weight: zero them so that
+    // whatever the cache holds there cannot turn 0 * v into NaN
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tile = r0 + u * kSplitWaves * kTileRows;
-      pk[u] = phys(min(tile + col, end - 1));
+    for (int u = 0; u < TPW; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pvr[u][j] = phys(min(tile + 4 * grp + j, end - 1));
-    }
-    uint32_t kw[TPW][KW];
-    uint32_t vw[TPW][4][VW];
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = r0 + u * NW * kTileRows + 4 * grp + j < end;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if (r0 + u * kSplitWaves * kTileRows < end) {  // uniform over the wave
-        load_slice<T, KW>(kw[u], Kb + (size_t)pk[u] * D, grp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) load_words(vw[u][j], Vb + (size_t)pvr[u][j] * D + col * NDB, VW);
+        for (int w = 0; w < VW; ++w) vw[u][j][w] = ok ? vw[u][j][w] : 0u;
       }
-    }
 
     // ---- logits^T = K_tile * Q^T for every tile of the round
     float x[TPW][4];
     float mt = -INFINITY;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const int tile = r0 + u * kSplitWaves * kTileRows;
+      const int tile = r0 + u * NW * kTileRows;
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[u][i] = -INFINITY;
       if (tile >= end) continue;
@@ -507,7 +626,7 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
     // ---- out^T += V_tile^T * P^T (rows past `end` have p = 0)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const int tile = r0 + u * kSplitWaves * kTileRows;
+      const int tile = r0 + u * NW * kTileRows;
       if (tile >= end) continue;
       float pr[4], pu[4];
       uint32_t pb[4];
@@ -547,6 +666,48 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
                                                            0, 0, 0);
       }
     }
+  };
+  // Rows of a round -> loads (the kept index of row r is j(r, i), i = 0 for
+  // the K row of the lane's column, 1 + j for its V rows).
+  auto load_round = [&](int r0, uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW], auto&& j_of) {
+    int pk[TPW], pvr[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r0 + u * NW * kTileRows;
+      if constexpr (KIND == KIND_SPARSE) {
+        pk[u] = sparse_row(tile + col, j_of(u, 0, tile + col));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pvr[u][j] = sparse_row(tile + 4 * grp + j, j_of(u, 1 + j, tile + 4 * grp + j));
+      } else {
+        pk[u] = min(tile + col, p.S - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pvr[u][j] = min(tile + 4 * grp + j, p.S - 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (r0 + u * NW * kTileRows < end) {  // uniform over the wave
+        load_slice<T, KW>(kw[u], Kb + (size_t)pk[u] * D, grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load_words(vw[u][j], Vb + (size_t)pvr[u][j] * D + col * NDB, VW);
+      }
+    }
+  };
+  auto j_loaded = [&](int, int, int r) { return selb[min(r, p.k_stride - 1)]; };
+
+  // Round r covers rows [begin + r*RPR, +RPR); tile u of wave w in a round
+  // starts at row (u*NW + w)*16, so neighbouring waves read neighbouring
+  // tiles.  The first round's loads (full kinds) or indices (sparse kind)
+  // are already in flight.
+  if (r_first < end) {
+    if constexpr (KIND == KIND_SPARSE) load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
+    round(r_first, kw, vw);
+  }
+  for (int r0 = r_first + RPR; r0 < end; r0 += RPR) {
+    uint32_t kw2[TPW][KW];
+    uint32_t vw2[TPW][4][VW];
+    load_round(r0, kw2, vw2, j_loaded);
+    round(r0, kw2, vw2);
   }
 
   if (KIND == KIND_SPARSE && bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
@@ -569,12 +730,12 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
   // ---- merge the waves: head totals, then outputs in rounds of HH heads
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, s_stat[w][col][0]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][col][0]);
   const float e_self = __builtin_amdgcn_exp2f(m_run - M);  // this wave's weight for head col
   if (tid < G) {
     float zz = 0.f, ll = 0.f, tt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float e = __builtin_amdgcn_exp2f(s_stat[w][tid][0] - M);
       zz += s_stat[w][tid][1] * e;
       ll += s_stat[w][tid][2] * e;
@@ -593,12 +754,12 @@ __global__ __launch_bounds__(kSplitThreads, 3) void split_attn_kernel(SplitParam
     }
     __syncthreads();
     const int hn = min(HH, G - h0);
-    for (int idx = tid; idx < hn * D; idx += kSplitThreads) {
+    for (int idx = tid; idx < hn * D; idx += NT) {
       const int h = idx / D;
       const int d = idx - h * D;
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kSplitWaves; ++w) o += s_o[w][h][d];
+      for (int w = 0; w < NW; ++w) o += s_o[w][h][d];
       if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, o / s_head[h0 + h].z);
       else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
     }
@@ -643,13 +804,33 @@ __device__ __forceinline__ int merge_splits(const MergeParams& p, int b, int& n,
 
 // Workgroups [0, Hq): merge head h's split states into its output.  Thread
 // t covers float4 column t / SL of the output and splits s = t % SL (mod SL).
+// The split states of the launched splits are loaded before the sequence
+// extent (which decides how many of them hold rows) is known.
 template <typename T, int D>
 __device__ void merge_head(const MergeParams& p, int b, int h) {
   constexpr int D4 = D / 4;
   constexpr int SL = kMergeThreads / D4;
+  constexpr int NST = kMaxMergeSplits / kMergeThreads;  // split states per thread
+  constexpr int PF = 8;                                  // partial outputs per thread in registers
   __shared__ float s_w[kMaxMergeSplits];
   __shared__ float s_red[kMergeThreads / 64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
+  const int d4 = tid / SL, sl = tid % SL;
+  const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
+  float4 st[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int s = tid + i * kMergeThreads;
+    st[i] = s < p.grid_splits ? p.pstat[slot0 + s] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 pv[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int s = sl + i * SL;
+    pv[i] = s < p.grid_splits ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
   int n, len;
   const int nsplit = merge_splits(p, b, n, len);
   if (p.direct && nsplit <= 1) return;  // finished by the split kernel
@@ -659,9 +840,10 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
     return;
   }
-  const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
   float m = -INFINITY;
-  for (int s = tid; s < nsplit; s += kMergeThreads) m = fmaxf(m, p.pstat[slot0 + s].x);
+#pragma unroll
+  for (int i = 0; i < NST; ++i)
+    if (tid + i * kMergeThreads < nsplit) m = fmaxf(m, st[i].x);
   m = wave_max(m);
   if (lane == 0) s_red[wave][0] = m;
   __syncthreads();
@@ -669,13 +851,16 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
 #pragma unroll
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
   float z = 0.f, l = 0.f, t = 0.f;
-  for (int s = tid; s < nsplit; s += kMergeThreads) {
-    const float4 st = p.pstat[slot0 + s];
-    const float w = __builtin_amdgcn_exp2f(st.x - M);
-    s_w[s] = w;
-    z += st.y * w;
-    l += st.z * w;
-    t += st.w * w;
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int s = tid + i * kMergeThreads;
+    if (s < nsplit) {
+      const float w = __builtin_amdgcn_exp2f(st[i].x - M);
+      s_w[s] = w;
+      z += st[i].y * w;
+      l += st[i].z * w;
+      t += st[i].w * w;
+    }
   }
   z = wave_sum(z);
   l = wave_sum(l);
@@ -693,10 +878,19 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     L += s_red[w][2];
     Zt += s_red[w][3];
   }
-  const int d4 = tid / SL, sl = tid % SL;
-  const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int s = sl; s < nsplit; s += SL) {
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int s = sl + i * SL;
+    if (s < nsplit) {
+      const float w = s_w[s];
+      a0 += pv[i].x * w;
+      a1 += pv[i].y * w;
+      a2 += pv[i].z * w;
+      a3 += pv[i].w * w;
+    }
+  }
+  for (int s = sl + PF * SL; s < nsplit; s += SL) {
     const float4 v = po[(size_t)s * D4];
     const float w = s_w[s];
     a0 += v.x * w;
@@ -720,11 +914,20 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
 
 // Workgroups [Hq, Hq + score_blocks): head-summed probability of
 // kMergeThreads image tokens each.  Each score workgroup derives every
-// head's softmax max and sum from the split states itself (32 lanes per
-// head), so it does not depend on the merge workgroups.
+// head's softmax max and sum from the split states itself (16 lanes per
+// head), so it does not depend on the merge workgroups.  The token's logits
+// of up to kScoreRegHeads heads are loaded before anything else.
+constexpr int kScoreRegHeads = 32;
+
 __device__ void score_block(const MergeParams& p, int b, int sb) {
   __shared__ float2 s_mz[kMaxHeads];
   const int tid = threadIdx.x;
+  const int j = sb * kMergeThreads + tid;
+  const float* lg = p.logits + (size_t)b * p.Hq * p.n_stride + min(j, p.n_stride - 1);
+  float x[kScoreRegHeads];
+#pragma unroll
+  for (int h = 0; h < kScoreRegHeads; ++h) x[h] = h < p.Hq ? lg[(size_t)h * p.n_stride] : 0.f;
+
   int n, len;
   const int nsplit = merge_splits(p, b, n, len);
   const int hl = tid & 15;
@@ -732,33 +935,38 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
     const int h = h0 + (tid >> 4);
     const bool hv = h < p.Hq;
     const float4* ps = p.pstat + ((size_t)b * p.Hq + (hv ? h : 0)) * p.max_splits;
+    float4 st[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = hl + 16 * i;
+      st[i] = (hv && s < nsplit) ? ps[s] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    }
     float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, st[i].x);
     if (hv)
-      for (int s = hl; s < nsplit; s += 16) m = fmaxf(m, ps[s].x);
+      for (int s = hl + 64; s < nsplit; s += 16) m = fmaxf(m, ps[s].x);
     m = row_max16(m);
     float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hl + 16 * i < nsplit) z += st[i].y * __builtin_amdgcn_exp2f(st[i].x - m);
     if (hv)
-      for (int s = hl; s < nsplit; s += 16) {
-        const float4 st = ps[s];
-        z += st.y * __builtin_amdgcn_exp2f(st.x - m);
+      for (int s = hl + 64; s < nsplit; s += 16) {
+        const float4 q = ps[s];
+        z += q.y * __builtin_amdgcn_exp2f(q.x - m);
       }
     z = group_sum<16>(z);
     if (hv && hl == 0) s_mz[h] = make_float2(m, 1.f / z);
   }
   __syncthreads();
-  const int j = sb * kMergeThreads + tid;
   if (j >= n) return;
-  const float* lg = p.logits + (size_t)b * p.Hq * p.n_stride + j;
   float s = 0.f;
-  int h = 0;
-  for (; h + 4 <= p.Hq; h += 4) {
-    float x[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = lg[(size_t)(h + u) * p.n_stride];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) s += __builtin_amdgcn_exp2f(x[u] - s_mz[h + u].x) * s_mz[h + u].y;
-  }
-  for (; h < p.Hq; ++h) s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
+  for (int h = 0; h < kScoreRegHeads; ++h)
+    if (h < p.Hq) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
+  for (int h = kScoreRegHeads; h < p.Hq; ++h)
+    s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
   p.scores[(size_t)b * p.n_stride + j] = s;
 }
 
@@ -772,52 +980,69 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __shared__ TopkShared sh;
   const int b = blockIdx.x;
-  const int n0 = p.lens[2 * b];
-  const int n = min(max(n0, 0), min(max(p.lens[2 * b + 1], 0), p.n_cap));
-  if (n0 != n && threadIdx.x == 0 && p.status) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
-  topk_sequence(p.scores + (size_t)b * p.score_stride, n, p.tau, p.idx_stride,
-                p.idx + (size_t)b * p.idx_stride, p.cnt + b, sh);
+  if (p.n_cap < 1) {
+    if (threadIdx.x == 0) p.cnt[b] = 0;
+    return;
+  }
+  topk_sequence(p.scores + (size_t)b * p.score_stride, p.n_cap, p.lens, b, p.tau, p.idx_stride,
+                p.idx + (size_t)b * p.idx_stride, p.cnt + b, p.status, sh);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
+template <typename P>
+static hipError_t launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream,
+                         const LaunchTiming& timing, const P& p) {
+  if (timing.start || timing.stop) {
+    void* args[] = {const_cast<P*>(&p)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream,
+                              timing.start, timing.stop, 0);
+  }
+  kernel<<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
-static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream) {
-  dim3 grid(p.grid_splits, p.Hkv, p.B), block(kSplitThreads);
+static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream,
+                                 const LaunchTiming& timing) {
+  const dim3 grid(p.grid_splits, p.Hkv, p.B), block(kSplitThreads);
   switch (kind) {
-    case KIND_FULL: split_attn_kernel<T, D, KIND_FULL><<<grid, block, 0, stream>>>(p); break;
-    case KIND_FOCAL: split_attn_kernel<T, D, KIND_FOCAL><<<grid, block, 0, stream>>>(p); break;
-    case KIND_SPARSE: split_attn_kernel<T, D, KIND_SPARSE><<<grid, block, 0, stream>>>(p); break;
+    case KIND_FULL:
+      return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, kTilesPerWave>, grid, block, stream,
+                    timing, p);
+    case KIND_FOCAL:
+      return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, kTilesPerWave>, grid, block, stream,
+                    timing, p);
+    case KIND_SPARSE:
+      return launch(split_attn_kernel<T, D, KIND_SPARSE, kSplitWaves, kTilesPerWave>, grid, block, stream,
+                    timing, p);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p,
-                        hipStream_t stream) {
+hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p, hipStream_t stream,
+                        const LaunchTiming& timing) {
   if (dtype == FASTOCR_DTYPE_BF16)
-    return head_dim == 128 ? launch_split_t<uint16_t, 128>(kind, p, stream)
-                           : launch_split_t<uint16_t, 64>(kind, p, stream);
-  return head_dim == 128 ? launch_split_t<float, 128>(kind, p, stream)
-                         : launch_split_t<float, 64>(kind, p, stream);
+    return head_dim == 128 ? launch_split_t<uint16_t, 128>(kind, p, stream, timing)
+                           : launch_split_t<uint16_t, 64>(kind, p, stream, timing);
+  return head_dim == 128 ? launch_split_t<float, 128>(kind, p, stream, timing)
+                         : launch_split_t<float, 64>(kind, p, stream, timing);
 }
 
-hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream) {
-  dim3 grid(p.Hq + p.score_blocks, p.B), block(kMergeThreads);
-  if (dtype == FASTOCR_DTYPE_BF16) {
-    if (head_dim == 128) merge_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(p);
-    else merge_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(p);
-  } else {
-    if (head_dim == 128) merge_kernel<float, 128><<<grid, block, 0, stream>>>(p);
-    else merge_kernel<float, 64><<<grid, block, 0, stream>>>(p);
-  }
-  return hipGetLastError();
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
+                        const LaunchTiming& timing) {
+  const dim3 grid(p.Hq + p.score_blocks, p.B), block(kMergeThreads);
+  if (dtype == FASTOCR_DTYPE_BF16)
+    return head_dim == 128 ? launch(merge_kernel<uint16_t, 128>, grid, block, stream, timing, p)
+                           : launch(merge_kernel<uint16_t, 64>, grid, block, stream, timing, p);
+  return head_dim == 128 ? launch(merge_kernel<float, 128>, grid, block, stream, timing, p)
+                         : launch(merge_kernel<float, 64>, grid, block, stream, timing, p);
 }
 
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
-  topk_kernel<<<dim3(p.B), dim3(kTopkThreads), 0, stream>>>(p);
-  return hipGetLastError();
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream, const LaunchTiming& timing) {
+  return launch(topk_kernel, dim3(p.B), dim3(kTopkThreads), stream, timing, p);
 }
 
 }  // namespace fastocr

@@ -107,8 +107,9 @@ typedef struct fastocr_info {
 } fastocr_info;
 
 typedef struct fastocr_timing {
-  double total_ms[FASTOCR_KC_COUNT]; /* summed kernel time per class (HIP events) */
-  int64_t launches[FASTOCR_KC_COUNT];
+  double total_ms[FASTOCR_KC_COUNT]; /* summed time of the timed launches per class (HIP events) */
+  int64_t launches[FASTOCR_KC_COUNT]; /* launches recorded */
+  int64_t timed[FASTOCR_KC_COUNT];    /* ... of which timed (all but a batch's first) */
 } fastocr_timing;
 
 typedef struct fastocr_handle fastocr_handle;
@@ -192,9 +193,15 @@ int fastocr_set_selection(fastocr_handle* h, const int32_t* idx_dev, const int32
 
 int fastocr_get_info(fastocr_handle* h, fastocr_info* info);
 
-/* Kernel timing with HIP events on the handle's stream: enable != 0 records an
- * event pair around every launch; fastocr_get_timing synchronises and returns
- * the per-class totals since the last reset; fastocr_reset_timing clears them. */
+/* Kernel timing with HIP events on the handle's stream.  enable != 0 makes
+ * every launch record an event when its kernel completes (bound to the
+ * dispatch: no extra packet is queued).  A launch is timed from the previous
+ * timed launch's end to its own end, which is the kernel's duration when the
+ * launches are queued back to back (the device never waits for the host, as
+ * behind a long-running kernel) and also counts idle time otherwise; the first
+ * launch after enabling, a reset or a fastocr_get_timing call is not counted.
+ * fastocr_get_timing synchronises the stream and returns the per-class totals
+ * since the last reset; fastocr_reset_timing clears them. */
 int fastocr_set_timing(fastocr_handle* h, int32_t enable);
 int fastocr_get_timing(fastocr_handle* h, fastocr_timing* out);
 int fastocr_reset_timing(fastocr_handle* h);

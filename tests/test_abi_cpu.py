@@ -36,7 +36,7 @@ def test_struct_layouts_match_header():
     # double first, then a float and twelve int32 -> 60 bytes, padded to 64
     assert ctypes.sizeof(_abi.Config) == 64
     assert ctypes.sizeof(_abi.Info) == 48
-    assert ctypes.sizeof(_abi.Timing) == 2 * 8 * _abi.KC_COUNT
+    assert ctypes.sizeof(_abi.Timing) == 3 * 8 * _abi.KC_COUNT
 
 
 @pytest.mark.parametrize("tau", [0.02, 0.05, 0.1, 0.2, 0.25, 0.3, 1 / 3, 0.5, 0.7, 1.0])

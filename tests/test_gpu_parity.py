@@ -54,23 +54,27 @@ def _topk_case(rng, B, n_cap, tau):
         n = [0, 1, 7, n_cap, n_cap // 3, 1000, 64, 65][b % 8]
         n = min(n, n_cap)
         ns.append(n)
-        kind = b % 3
+        kind = b % 5
         if kind == 0:  # continuous
             scores[b, :n] = rng.random(n).astype(np.float32) * 3
         elif kind == 1:  # heavy ties
             scores[b, :n] = (rng.integers(0, 5, n) / 4).astype(np.float32)
-        else:  # all equal, zeros mixed in
+        elif kind == 2:  # all equal, zeros mixed in
             scores[b, :n] = np.float32(0.25)
             scores[b, : n // 2] = 0.0
+        elif kind == 3:  # one narrow band: the leading digits do not separate the keys
+            scores[b, :n] = (1.0 + rng.random(n) * 1e-4).astype(np.float32)
+        else:  # head-summed softmax-like: a few large scores, a long tail
+            scores[b, :n] = (rng.exponential(1.0, n) ** 3 / max(n, 1)).astype(np.float32)
     lens = np.stack([np.array(ns), np.array(ns) + 3], axis=1).astype(np.int32)
     return scores, lens
 
 
 @pytest.mark.parametrize("tau", [0.02, 0.05, 0.1, 0.5, 1.0])
-@pytest.mark.parametrize("n_cap", [64, 6400, 16384])
+@pytest.mark.parametrize("n_cap", [64, 6400, 16384, 70000])
 def test_topk_bit_exact(tau, n_cap):
     rng = np.random.default_rng(int(tau * 1000) + n_cap)
-    B = 8
+    B = 10
     scores, lens = _topk_case(rng, B, n_cap, tau)
     k_stride = max(kept_count(tau, n_cap), 1)
     s_d = torch.from_numpy(scores).to(DEV)
@@ -88,10 +92,24 @@ def test_topk_bit_exact(tau, n_cap):
         np.testing.assert_array_equal(idx[b, :k], want, err_msg=f"b={b} n={n} k={k}")
 
 
-def test_sparse_conditioned_on_injected_sets():
-    up = upload(get_workload("7b-b1").with_overrides(num_layers=3, warmup_steps=1, num_focal=1),
+# kept-token pass with several split workgroups per sequence (+ merge
+# launch), and with one split per sequence that writes the output directly
+SPARSE_VARIANTS = pytest.mark.parametrize("rows", ["", "16384"], ids=["split-merge", "direct"])
+
+
+def _sparse_variant(monkeypatch, rows):
+    monkeypatch.setenv("FASTOCR_SPARSE_ROWS", rows)
+
+
+@SPARSE_VARIANTS
+@pytest.mark.parametrize("tau", [0.05, 0.5])
+def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
+    # tau = 0.5 gives a direct split many rounds
+    _sparse_variant(monkeypatch, rows)
+    up = upload(get_workload("7b-b1").with_overrides(num_layers=3, warmup_steps=1, num_focal=1, tau=tau),
                 steps=3)
     h = fo.fastocr_create(make_config(up))
+    assert fo.fastocr_get_info(h)["sparse_direct"] == (1 if rows else 0)
     wl = up.wl
     for l in range(wl.num_layers):  # one warm-up step
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
@@ -122,7 +140,9 @@ def test_sparse_conditioned_on_injected_sets():
     assert fo.fastocr_get_status(h) == 0
 
 
-def test_tau_one_sparse_equals_full():
+@SPARSE_VARIANTS
+def test_tau_one_sparse_equals_full(monkeypatch, rows):
+    _sparse_variant(monkeypatch, rows)
     wl = get_workload("tiny-fp32").with_overrides(tau=1.0)
     up = upload(wl, steps=7)
     rec = run(up, fo.fastocr_create(make_config(up)), 7)
@@ -182,7 +202,9 @@ def test_trajectory_tiny_all_steps():
         f"mean Jaccard {np.mean(chk.jaccard):.3f}")
 
 
-def test_trajectory_ragged_small():
+@SPARSE_VARIANTS
+def test_trajectory_ragged_small(monkeypatch, rows):
+    _sparse_variant(monkeypatch, rows)
     wl = get_workload("7b-b16-ragged").with_overrides(
         batch=4, num_layers=6, focal_band=(2, 3), num_focal=2, warmup_steps=3,
         n_img_range=(100, 700), n_prompt=(5, 40))
