@@ -57,8 +57,9 @@ def parse():
                          "scales hardware byte counters")
     ap.add_argument("--pmc-summary", default=None, nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter CSVs under the DIRs and exit (no GPU use)")
-    ap.add_argument("--trace-summary", default=None, nargs=2, metavar=("DIR", "COMMAND"),
-                    help="summarise a rocprofv3 kernel trace under DIR made by COMMAND and exit")
+    ap.add_argument("--trace-summary", default=None, nargs="+", metavar="ARG",
+                    help="DIR COMMAND [BENCH_JSON]: summarise a rocprofv3 kernel trace under DIR made by "
+                         "COMMAND, beside the event averages of BENCH_JSON, and exit")
     return ap.parse_args()
 
 
@@ -124,21 +125,24 @@ def pmc_summary(directories):
             print(f"{cls}.hbm_bytes_per_launch: {hbm:.0f}")
 
 
-def trace_summary(directory, command):
+def trace_summary(directory, command, bench_json=None):
     """Per-kernel durations from a rocprofv3 --kernel-trace --stats run of
-    this script, beside the averages the same run measured with its own
-    dispatch events (bench.json in the same directory)."""
+    this script, beside the averages that a run of the same command measured
+    with its own completion events: `bench_json` (the same command without
+    the profiler, whose per-dispatch overhead stretches the event intervals)
+    or else bench.json in `directory`."""
     import csv
     import glob
     stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     print(f"# command: {command}")
     print(f"kernel_source_sha256_16: {kernel_source_digest()}")
     bench = {}
-    bj = os.path.join(directory, "bench.json")
+    bj = bench_json or os.path.join(directory, "bench.json")
     if os.path.exists(bj):
         with open(bj) as f:
             bench = json.loads(f.read().strip().splitlines()[-1])
-        print(f"# bench: value {bench.get('value')} {bench.get('unit')}, workload {bench['config'].get('name')}")
+        print(f"# event averages from: {'the same command without the profiler' if bench_json else 'the profiled run'};"
+              f" its value {bench.get('value')} {bench.get('unit')}, workload {bench['config'].get('name')}")
     ev = bench.get("per_kernel", {})
     print(f"# {'kernel class':14s} {'calls':>7s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} "
           f"{'bench_event_avg_us':>18s}  name")
@@ -181,7 +185,7 @@ def main():
         pmc_summary(args.pmc_summary)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary[0], args.trace_summary[1])
+        trace_summary(*args.trace_summary[:3])
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",

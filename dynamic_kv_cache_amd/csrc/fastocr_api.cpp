@@ -325,13 +325,15 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->phase = c.mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
 
   const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
-  const int target = 3 * num_cu;  // three resident split workgroups per CU
-  h->full_R = plan_rows_per_split(pairs, c.max_seq_len, target, "FASTOCR_FULL_ROWS");
+  // about one wave of resident split workgroups per launch
+  h->full_R = plan_rows_per_split(pairs, c.max_seq_len, split_blocks_per_cu(KIND_FULL) * num_cu,
+                                  "FASTOCR_FULL_ROWS");
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
   int sparse_rows = c.max_seq_len;
   if (c.min_img_tokens > 0)
     sparse_rows = std::min(c.max_seq_len, h->k_max + c.max_seq_len - c.min_img_tokens);
-  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, target, "FASTOCR_SPARSE_ROWS");
+  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE) * num_cu,
+                                    "FASTOCR_SPARSE_ROWS");
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
   h->max_splits = std::max(h->full_splits, h->sparse_splits);
 

@@ -22,6 +22,9 @@ constexpr int kSplitWaves = 4;
 constexpr int kTilesPerWave = 2;
 constexpr int kRowsPerRound = kTileRows * kSplitWaves * kTilesPerWave;
 constexpr int kSplitThreads = kSplitWaves * 64;
+// Resident split workgroups per CU the registers allow: full passes keep two
+// rounds of K/V in registers, kept-token passes one.
+constexpr int split_blocks_per_cu(int kind) { return kind == KIND_SPARSE ? 3 : 2; }
 constexpr int kMergeThreads = 256;
 constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
 constexpr int kMaxHeads = 128;

@@ -451,7 +451,7 @@ __device__ __forceinline__ int split_count(int rows, int rows_per_split, int gri
 }
 
 template <typename T, int D, int KIND, int NW, int TPW>
-__global__ __launch_bounds__(NW * 64, NW == kSplitWaves ? 3 : 1) void split_attn_kernel(SplitParams p) {
+__global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
   constexpr int RPR = NW * TPW * kTileRows;     // rows per round
@@ -599,12 +599,18 @@ __global__ __launch_bounds__(NW * 64, NW == kSplitWaves ? 3 : 1) void split_attn
         mt = fmaxf(mt, x[u][i]);
       }
       if constexpr (KIND == KIND_FOCAL) {
+        // this lane's 4 logits are consecutive image rows of one head: one
+        // 16-byte store (rows are a multiple of 4, n_stride too)
         if (col < G) {
           float* lg = p.logits + ((size_t)b * p.Hq + kvh * G + col) * p.n_stride;
+          const int r = tile + 4 * grp;
+          const int lim = min(end, n);
+          if (r + 3 < lim) {
+            *reinterpret_cast<float4*>(lg + r) = make_float4(x[u][0], x[u][1], x[u][2], x[u][3]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = tile + 4 * grp + i;
-            if (r < end && r < n) lg[r] = x[u][i];
+            for (int i = 0; i < 4; ++i)
+              if (r + i < lim) lg[r + i] = x[u][i];
           }
         }
       }
@@ -699,15 +705,31 @@ __global__ __launch_bounds__(NW * 64, NW == kSplitWaves ? 3 : 1) void split_attn
   // starts at row (u*NW + w)*16, so neighbouring waves read neighbouring
   // tiles.  The first round's loads (full kinds) or indices (sparse kind)
   // are already in flight.
-  if (r_first < end) {
-    if constexpr (KIND == KIND_SPARSE) load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
-    round(r_first, kw, vw);
-  }
-  for (int r0 = r_first + RPR; r0 < end; r0 += RPR) {
+  if constexpr (KIND == KIND_SPARSE) {
+    // kept-token passes are short (one or two rounds per split): one
+    // register buffer, higher occupancy
+    if (r_first < end) {
+      load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
+      round(r_first, kw, vw);
+    }
+    for (int r0 = r_first + RPR; r0 < end; r0 += RPR) {
+      uint32_t kw2[TPW][KW];
+      uint32_t vw2[TPW][4][VW];
+      load_round(r0, kw2, vw2, j_loaded);
+      round(r0, kw2, vw2);
+    }
+  } else if (r_first < end) {
+    // full passes: rounds alternate between two register buffers, the next
+    // round's loads are issued before the current round is computed
     uint32_t kw2[TPW][KW];
     uint32_t vw2[TPW][4][VW];
-    load_round(r0, kw2, vw2, j_loaded);
-    round(r0, kw2, vw2);
+    for (int r0 = r_first; r0 < end; r0 += 2 * RPR) {
+      if (r0 + RPR < end) load_round(r0 + RPR, kw2, vw2, j_loaded);
+      round(r0, kw, vw);
+      if (r0 + RPR >= end) break;
+      if (r0 + 2 * RPR < end) load_round(r0 + 2 * RPR, kw, vw, j_loaded);
+      round(r0 + RPR, kw2, vw2);
+    }
   }
 
   if (KIND == KIND_SPARSE && bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
