@@ -181,7 +181,6 @@ MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool
   m.max_splits = h->max_splits;
   m.rows_per_split = sparse ? h->sparse_R : h->full_R;
   m.grid_splits = sparse ? h->sparse_splits : h->full_splits;
-  m.direct = sparse ? 1 : 0;
   m.n_stride = h->n_stride;
   return m;
 }
@@ -213,13 +212,13 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
 }
 
 // Non-focal layer: attention over the kept image rows and every text row.
-// Sequences whose rows fit one split are finished by the split kernel; the
-// merge runs only when some sequence can span several splits.
+// When every sequence fits one split the split kernel writes the outputs;
+// otherwise every launched split writes a state and the merge combines them.
 int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
                void* out) {
   const fastocr_config& c = h->cfg;
   SplitParams sp = split_params(h, q, k, v, lens, out, true);
-  sp.direct = 1;
+  sp.direct = h->sparse_splits <= 1 ? 1 : 0;
   int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream, lt);
   });

@@ -46,7 +46,8 @@ struct SplitParams {
   int32_t* status;
   int32_t B, Hq, Hkv, S, n_cap, n_stride, k_stride, max_splits, rows_per_split;
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
-  int32_t direct;         // a sequence whose rows fit one split writes its output
+  int32_t direct;         // one split per sequence (grid_splits == 1): write outputs here;
+                          // otherwise every launched split writes a state (empty: max -inf)
   float scale_log2;       // logit scale * log2(e)
 };
 
@@ -61,7 +62,6 @@ struct MergeParams {
   float* text_mass;       // [B, Hq] or null
   int32_t* status;
   int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split, grid_splits;
-  int32_t direct;         // sequences with one split were finished by the split kernel
   const float* logits;    // [B, Hq, n_stride]
   float* scores;          // [B, n_stride]
   int32_t n_stride;

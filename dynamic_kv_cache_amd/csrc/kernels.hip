@@ -527,12 +527,16 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
   const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
   const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
-  const int nsplit = split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
-  const bool direct = p.direct && nsplit <= 1;
+  (void)split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
+  const bool direct = p.direct;  // one split per sequence: write the output here
   if (begin >= rows) {
-    if (direct && split == 0) {  // no rows at all: zero output
+    if (direct) {  // no rows at all: zero output
       T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
       for (int i = tid; i < G * D; i += NT) store_out<T>(out + i, 0.f);
+    } else if (tid < G) {
+      // an empty split: a state that carries no weight in the merge
+      p.pstat[((size_t)b * p.Hq + kvh * G + tid) * p.max_splits + split] =
+          make_float4(-INFINITY, 0.f, 0.f, 0.f);
     }
     return;
   }
@@ -818,16 +822,11 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
-__device__ __forceinline__ int merge_splits(const MergeParams& p, int b, int& n, int& len) {
-  seq_extent(p.lens, b, p.S, p.n_cap, n, len);
-  const int rows = p.sel_cnt ? kept_rows(p.sel_cnt, b, n, p.k_stride) + (len - n) : len;
-  return split_count(rows, p.rows_per_split, p.grid_splits, p.status, false);
-}
-
 // Workgroups [0, Hq): merge head h's split states into its output.  Thread
 // t covers float4 column t / SL of the output and splits s = t % SL (mod SL).
-// The split states of the launched splits are loaded before the sequence
-// extent (which decides how many of them hold rows) is known.
+// Every launched split has written a state this launch (an empty split one
+// with max -inf and no weight), so the merge does not read the sequence
+// extent: all its loads are issued at once.
 template <typename T, int D>
 __device__ void merge_head(const MergeParams& p, int b, int h) {
   constexpr int D4 = D / 4;
@@ -853,15 +852,8 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     pv[i] = s < p.grid_splits ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  int n, len;
-  const int nsplit = merge_splits(p, b, n, len);
-  if (p.direct && nsplit <= 1) return;  // finished by the split kernel
+  const int nsplit = p.grid_splits;
   T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
-  if (nsplit == 0) {
-    for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
-    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
-    return;
-  }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NST; ++i)
@@ -872,12 +864,19 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
   float M = s_red[0][0];
 #pragma unroll
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
+  if (M == -INFINITY) {  // no rows at all
+    for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
+    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
+    return;
+  }
   float z = 0.f, l = 0.f, t = 0.f;
 #pragma unroll
   for (int i = 0; i < NST; ++i) {
     const int s = tid + i * kMergeThreads;
     if (s < nsplit) {
-      const float w = __builtin_amdgcn_exp2f(st[i].x - M);
+      // empty splits get weight exactly 0 (and their partial outputs, not
+      // written this launch, are never multiplied)
+      const float w = st[i].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[i].x - M);
       s_w[s] = w;
       z += st[i].y * w;
       l += st[i].z * w;
@@ -904,8 +903,8 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int s = sl + i * SL;
-    if (s < nsplit) {
-      const float w = s_w[s];
+    const float w = s < nsplit ? s_w[s] : 0.f;
+    if (w != 0.f) {
       a0 += pv[i].x * w;
       a1 += pv[i].y * w;
       a2 += pv[i].z * w;
@@ -913,12 +912,14 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     }
   }
   for (int s = sl + PF * SL; s < nsplit; s += SL) {
-    const float4 v = po[(size_t)s * D4];
     const float w = s_w[s];
-    a0 += v.x * w;
-    a1 += v.y * w;
-    a2 += v.z * w;
-    a3 += v.w * w;
+    if (w != 0.f) {
+      const float4 v = po[(size_t)s * D4];
+      a0 += v.x * w;
+      a1 += v.y * w;
+      a2 += v.z * w;
+      a3 += v.w * w;
+    }
   }
   a0 = group_sum<SL>(a0);
   a1 = group_sum<SL>(a1);
@@ -950,8 +951,7 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
 #pragma unroll
   for (int h = 0; h < kScoreRegHeads; ++h) x[h] = h < p.Hq ? lg[(size_t)h * p.n_stride] : 0.f;
 
-  int n, len;
-  const int nsplit = merge_splits(p, b, n, len);
+  const int nsplit = p.grid_splits;
   const int hl = tid & 15;
   for (int h0 = 0; h0 < p.Hq; h0 += kMergeThreads / 16) {
     const int h = h0 + (tid >> 4);
@@ -972,17 +972,19 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (hl + 16 * i < nsplit) z += st[i].y * __builtin_amdgcn_exp2f(st[i].x - m);
+      if (hl + 16 * i < nsplit && st[i].x != -INFINITY) z += st[i].y * __builtin_amdgcn_exp2f(st[i].x - m);
     if (hv)
       for (int s = hl + 64; s < nsplit; s += 16) {
         const float4 q = ps[s];
-        z += q.y * __builtin_amdgcn_exp2f(q.x - m);
+        if (q.x != -INFINITY) z += q.y * __builtin_amdgcn_exp2f(q.x - m);
       }
     z = group_sum<16>(z);
     if (hv && hl == 0) s_mz[h] = make_float2(m, 1.f / z);
   }
   __syncthreads();
-  if (j >= n) return;
+  // tokens past this sequence's image tokens get scores too (from stale
+  // logits); nothing reads them
+  if (j >= p.n_stride) return;
   float s = 0.f;
 #pragma unroll
   for (int h = 0; h < kScoreRegHeads; ++h)
