@@ -233,7 +233,8 @@ def main():
     def make(mode):
         cfg = fo.Config(num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, batch=B,
                         max_seq_len=st.max_seq_len, max_img_tokens=int(st.n_img.max()),
-                        min_img_tokens=int(st.n_img.min()), tau=wl.tau, num_focal=wl.num_focal,
+                        min_img_tokens=int(st.n_img.min()), max_text_tokens=int(st.n_prompt.max()) + wl.steps,
+                        tau=wl.tau, num_focal=wl.num_focal,
                         warmup_steps=w, dtype=wl.dtype, mode=mode)
         return fo.fastocr_create(cfg, stream)
 

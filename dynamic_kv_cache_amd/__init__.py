@@ -56,13 +56,14 @@ class Config:
     mode: str = "pruned"  # "pruned" | "full"
     sm_scale: float = 0.0
     min_img_tokens: int = 0
+    max_text_tokens: int = 0
 
     def to_c(self) -> _abi.Config:
         return _abi.Config(
             tau=float(self.tau), sm_scale=float(self.sm_scale), num_layers=self.num_layers,
             num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
             batch=self.batch, max_seq_len=self.max_seq_len, max_img_tokens=self.max_img_tokens,
-            min_img_tokens=self.min_img_tokens,
+            min_img_tokens=self.min_img_tokens, max_text_tokens=self.max_text_tokens,
             dtype=DTYPE_BF16 if self.dtype == "bf16" else DTYPE_F32,
             num_focal=self.num_focal, warmup_steps=self.warmup_steps,
             mode=MODE_FULL if self.mode == "full" else MODE_PRUNED)

@@ -48,6 +48,7 @@ class Config(ctypes.Structure):
         ("num_focal", c_int32),
         ("warmup_steps", c_int32),
         ("mode", c_int32),
+        ("max_text_tokens", c_int32),
     ]
 
 

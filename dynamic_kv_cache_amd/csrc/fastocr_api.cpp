@@ -245,6 +245,7 @@ bool config_ok(const fastocr_config& c) {
   if (c.max_seq_len < 1) return false;
   if (c.max_img_tokens < 0 || c.max_img_tokens > c.max_seq_len) return false;
   if (c.min_img_tokens < 0 || c.min_img_tokens > c.max_img_tokens) return false;
+  if (c.max_text_tokens < 0 || c.max_text_tokens > c.max_seq_len) return false;
   if (c.dtype != FASTOCR_DTYPE_F32 && c.dtype != FASTOCR_DTYPE_BF16) return false;
   if (c.mode != FASTOCR_MODE_PRUNED && c.mode != FASTOCR_MODE_FULL) return false;
   if (!(c.tau > 0.0 && c.tau <= 1.0)) return false;
@@ -328,9 +329,11 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->full_R = plan_rows_per_split(pairs, c.max_seq_len, split_blocks_per_cu(KIND_FULL) * num_cu,
                                   "FASTOCR_FULL_ROWS");
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
+  // rows of a kept-token pass: kept image rows + text rows
   int sparse_rows = c.max_seq_len;
   if (c.min_img_tokens > 0)
-    sparse_rows = std::min(c.max_seq_len, h->k_max + c.max_seq_len - c.min_img_tokens);
+    sparse_rows = std::min(sparse_rows, h->k_max + c.max_seq_len - c.min_img_tokens);
+  if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, h->k_max + c.max_text_tokens);
   h->sparse_R = plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE) * num_cu,
                                     "FASTOCR_SPARSE_ROWS");
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;

@@ -463,7 +463,6 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   constexpr int OST = D + 1;                    // padded LDS row of partial outputs
 
   __shared__ float s_stat[NW][16][4];
-  __shared__ float4 s_head[16];
   __shared__ float s_o[NW][HH][OST];
 
   const int split = blockIdx.x;
@@ -751,14 +750,47 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
     s_stat[wave][col][2] = lsum;
     s_stat[wave][col][3] = zt;
   }
-  __syncthreads();
 
-  // ---- merge the waves: head totals, then outputs in rounds of HH heads
-  float M = -INFINITY;
+  // ---- merge the waves, in rounds of HH heads: every wave leaves its
+  // unscaled accumulator in LDS, and the reducing threads weight wave w by
+  // exp2(m_w - M) themselves, so one barrier per round suffices
+  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
+  for (int h0 = 0; h0 < G; h0 += HH) {
+    if (h0 > 0) __syncthreads();  // the previous round has read s_o
+    if (col >= h0 && col < h0 + HH) {
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][col][0]);
-  const float e_self = __builtin_amdgcn_exp2f(m_run - M);  // this wave's weight for head col
-  if (tid < G) {
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i];
+    }
+    __syncthreads();
+    const int hn = min(HH, G - h0);
+    for (int idx = tid; idx < hn * D; idx += NT) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float mw[NW];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        mw[w] = s_stat[w][h0 + h][0];
+        M = fmaxf(M, mw[w]);
+      }
+      float o = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float e = __builtin_amdgcn_exp2f(mw[w] - M);
+        o += s_o[w][h][d] * e;
+        L += s_stat[w][h0 + h][2] * e;
+      }
+      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, o / L);
+      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+    }
+  }
+  if (!direct && tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][tid][0]);
     float zz = 0.f, ll = 0.f, tt = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -767,31 +799,8 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
       ll += s_stat[w][tid][2] * e;
       tt += s_stat[w][tid][3] * e;
     }
-    s_head[tid] = make_float4(M, zz, ll, tt);
+    p.pstat[slot0 + (size_t)tid * p.max_splits] = make_float4(M, zz, ll, tt);
   }
-  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
-  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
-  for (int h0 = 0; h0 < G; h0 += HH) {
-    if (col >= h0 && col < h0 + HH) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i] * e_self;
-    }
-    __syncthreads();
-    const int hn = min(HH, G - h0);
-    for (int idx = tid; idx < hn * D; idx += NT) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      float o = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) o += s_o[w][h][d];
-      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, o / s_head[h0 + h].z);
-      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
-    }
-    __syncthreads();
-  }
-  if (!direct && tid < G) p.pstat[slot0 + (size_t)tid * p.max_splits] = s_head[tid];
 }
 
 // ---------------------------------------------------------------------------

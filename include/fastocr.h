@@ -90,6 +90,11 @@ typedef struct fastocr_config {
   int32_t num_focal;      /* |C|, 1 <= |C| <= L */
   int32_t warmup_steps;   /* w >= 1 */
   int32_t mode;           /* FASTOCR_MODE_* */
+  int32_t max_text_tokens; /* upper bound on a sequence's text tokens len_b - n_img_b
+                              (prompt + generated), 0 if unknown; only used to size
+                              the sparse launch.  A sequence beyond the bounds given
+                              by min_img_tokens / max_text_tokens is truncated to
+                              the launched splits and flagged (FASTOCR_FLAG_ROWS_TRUNCATED). */
 } fastocr_config;
 
 typedef struct fastocr_info {

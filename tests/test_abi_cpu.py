@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # double first, then a float and twelve int32 -> 60 bytes, padded to 64
+    # double first, then a float and thirteen int32 -> 64 bytes, no padding
     assert ctypes.sizeof(_abi.Config) == 64
     assert ctypes.sizeof(_abi.Info) == 48
     assert ctypes.sizeof(_abi.Timing) == 3 * 8 * _abi.KC_COUNT
@@ -71,6 +71,7 @@ BAD = [
     dict(num_q_heads=136, num_kv_heads=17), dict(tau=0.0), dict(tau=1.01), dict(num_focal=0),
     dict(num_focal=5), dict(warmup_steps=0), dict(max_img_tokens=305), dict(batch=0),
     dict(max_seq_len=0), dict(num_layers=0), dict(sm_scale=-1.0), dict(min_img_tokens=300),
+    dict(max_text_tokens=-1), dict(max_text_tokens=305),
 ]
 
 

@@ -60,7 +60,8 @@ def run_sampled(wl, sample_steps, all_ratio_layers: bool):
     log(f"[{wl.name}] inputs in {time.time() - t0:.1f}s")
     cfg = fo.Config(num_layers=L, num_q_heads=Hq, num_kv_heads=wl.num_kv_heads, head_dim=d, batch=B,
                     max_seq_len=st.max_seq_len, max_img_tokens=int(st.n_img.max()),
-                    min_img_tokens=int(st.n_img.min()), tau=wl.tau, num_focal=wl.num_focal,
+                    min_img_tokens=int(st.n_img.min()), max_text_tokens=int(st.n_prompt.max()) + T,
+                    tau=wl.tau, num_focal=wl.num_focal,
                     warmup_steps=wl.warmup_steps, dtype=wl.dtype)
     h = fo.fastocr_create(cfg)
     k_max = fo.fastocr_get_info(h)["k_max"]
