@@ -64,6 +64,7 @@ struct fastocr_handle {
   int device = 0;
   int G = 0, D = 0, n_cap = 0, n_stride = 0, k_max = 0;
   int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
+  int full_sure = 0, sparse_sure = 0;  // splits that hold rows for any accepted sequence
 
   float scale_log2 = 0.f;
 
@@ -145,6 +146,7 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   p.max_splits = h->max_splits;
   p.rows_per_split = sparse ? h->sparse_R : h->full_R;
   p.grid_splits = sparse ? h->sparse_splits : h->full_splits;
+  p.sure_splits = sparse ? h->sparse_sure : h->full_sure;
   p.scale_log2 = h->scale_log2;
   return p;
 }
@@ -338,6 +340,14 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
                                     "FASTOCR_SPARSE_ROWS");
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
   h->max_splits = std::max(h->full_splits, h->sparse_splits);
+  // Full passes: every sequence has at least min_img_tokens image rows and
+  // the current token, so splits below that hold rows and load their K/V
+  // ahead; the others (possibly empty for a short sequence of a ragged
+  // batch) wait for the extent.  Kept-token splits only load indices ahead,
+  // which costs an empty split nothing worth saving.
+  const int min_full_rows = c.min_img_tokens + 1;
+  h->full_sure = std::min((min_full_rows + h->full_R - 1) / h->full_R, h->full_splits);
+  h->sparse_sure = h->sparse_splits;
 
   // scratch arena
   const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers, D = c.head_dim;

@@ -46,6 +46,7 @@ struct SplitParams {
   int32_t* status;
   int32_t B, Hq, Hkv, S, n_cap, n_stride, k_stride, max_splits, rows_per_split;
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
+  int32_t sure_splits;    // splits that hold rows for every accepted sequence
   int32_t direct;         // one split per sequence (grid_splits == 1): write outputs here;
                           // otherwise every launched split writes a state (empty: max -inf)
   float scale_log2;       // logit scale * log2(e)

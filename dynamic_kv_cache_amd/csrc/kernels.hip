@@ -498,7 +498,12 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   uint32_t kw[TPW][KW];
   uint32_t vw[TPW][4][VW];
   int jpre[TPW][5];  // sparse: kept indices of the first round's rows
-  if constexpr (KIND == KIND_SPARSE) {
+  // Splits below sure_splits hold rows for every sequence the handle
+  // accepts: they load ahead.  The others may be empty and learn that
+  // from the extent before loading anything.
+  const bool ahead = split < p.sure_splits;
+  if (!ahead) {
+  } else if constexpr (KIND == KIND_SPARSE) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = r_first + u * NW * kTileRows;
@@ -712,7 +717,8 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
     // kept-token passes are short (one or two rounds per split): one
     // register buffer, higher occupancy
     if (r_first < end) {
-      load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
+      if (ahead) load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
+      else load_round(r_first, kw, vw, j_loaded);
       round(r_first, kw, vw);
     }
     for (int r0 = r_first + RPR; r0 < end; r0 += RPR) {
@@ -724,6 +730,7 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   } else if (r_first < end) {
     // full passes: rounds alternate between two register buffers, the next
     // round's loads are issued before the current round is computed
+    if (!ahead) load_round(r_first, kw, vw, j_loaded);
     uint32_t kw2[TPW][KW];
     uint32_t vw2[TPW][4][VW];
     for (int r0 = r_first; r0 < end; r0 += 2 * RPR) {
