@@ -242,6 +242,7 @@ void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {
 bool config_ok(const fastocr_config& c) {
   if (c.num_layers < 1 || c.num_kv_heads < 1 || c.num_q_heads < 1 || c.batch < 1) return false;
   if (c.num_q_heads % c.num_kv_heads != 0) return false;
+  if ((int64_t)c.batch * c.num_kv_heads > 65535) return false;  // one grid dimension
   if (c.num_q_heads / c.num_kv_heads > 16 || c.num_q_heads > 128) return false;
   if (c.head_dim != 64 && c.head_dim != 128) return false;
   if (c.max_seq_len < 1) return false;

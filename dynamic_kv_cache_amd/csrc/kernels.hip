@@ -393,20 +393,29 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
   eq_incl += sum_before(sh.wave_sum2, wave);
   int eq_seen = (int)(eq_incl - eq);
   int pos = (int)(gt_incl - gt) + min(eq_seen, need_eq);
-#pragma unroll 1
-  for (int i = 0; i < mine; ++i) {
-    unsigned int key = 0u;
-    if (in_regs) {
+  if (in_regs) {
+    // unrolled over the register keys: static register indices, one
+    // predicated store per kept key
 #pragma unroll
-      for (int r = 0; r < kTopkRegKeys; ++r) key = (r == i) ? reg[r] : key;
-    } else {
-      key = keys[base + i];
+    for (int i = 0; i < kTopkRegKeys; ++i) {
+      const bool valid = i < mine;
+      const bool gt_i = valid && reg[i] > theta;
+      const bool eq_i = valid && reg[i] == theta;
+      const bool keep = gt_i || (eq_i && eq_seen < need_eq);
+      if (keep) out[pos] = base + i;
+      pos += keep ? 1 : 0;
+      eq_seen += eq_i ? 1 : 0;
     }
-    if (key > theta) {
-      out[pos++] = base + i;
-    } else if (key == theta) {
-      if (eq_seen < need_eq) out[pos++] = base + i;
-      ++eq_seen;
+  } else {
+#pragma unroll 1
+    for (int i = 0; i < mine; ++i) {
+      const unsigned int key = keys[base + i];
+      if (key > theta) {
+        out[pos++] = base + i;
+      } else if (key == theta) {
+        if (eq_seen < need_eq) out[pos++] = base + i;
+        ++eq_seen;
+      }
     }
   }
 }
@@ -465,9 +474,16 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   __shared__ float s_stat[NW][16][4];
   __shared__ float s_o[NW][HH][OST];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // Full passes: x = split, y = (sequence, KV head) pair, so workgroups
+  // dispatched together stream neighbouring rows.  Kept-token passes:
+  // x = pair, y = split, dispatched split-major, so the high splits that
+  // most sequences leave empty (the grid covers the longest text the handle
+  // accepts) come last and exit while the others stream.
+  constexpr bool SPLIT_MAJOR = KIND == KIND_SPARSE;
+  const int pair = SPLIT_MAJOR ? blockIdx.x : blockIdx.y;
+  const int split = SPLIT_MAJOR ? blockIdx.y : blockIdx.x;
+  const int kvh = pair % p.Hkv;
+  const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1047,7 +1063,8 @@ static hipError_t launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
 template <typename T, int D>
 static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream,
                                  const LaunchTiming& timing) {
-  const dim3 grid(p.grid_splits, p.Hkv, p.B), block(kSplitThreads);
+  const dim3 block(kSplitThreads);
+  const dim3 grid = kind == KIND_SPARSE ? dim3(p.Hkv * p.B, p.grid_splits) : dim3(p.grid_splits, p.Hkv * p.B);
   switch (kind) {
     case KIND_FULL:
       return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, kTilesPerWave>, grid, block, stream,

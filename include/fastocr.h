@@ -81,7 +81,7 @@ typedef struct fastocr_config {
   int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads, Hq/Hkv <= 16, Hq <= 128 */
   int32_t num_kv_heads;   /* Hkv >= 1 */
   int32_t head_dim;       /* d: 64 or 128 */
-  int32_t batch;          /* B >= 1 sequences */
+  int32_t batch;          /* B >= 1 sequences, B * num_kv_heads <= 65535 */
   int32_t max_seq_len;    /* S: row stride of the KV cache (capacity per sequence) */
   int32_t max_img_tokens; /* upper bound on image tokens per sequence (<= S) */
   int32_t min_img_tokens; /* lower bound on image tokens per sequence, 0 if unknown;

@@ -71,7 +71,7 @@ BAD = [
     dict(num_q_heads=136, num_kv_heads=17), dict(tau=0.0), dict(tau=1.01), dict(num_focal=0),
     dict(num_focal=5), dict(warmup_steps=0), dict(max_img_tokens=305), dict(batch=0),
     dict(max_seq_len=0), dict(num_layers=0), dict(sm_scale=-1.0), dict(min_img_tokens=300),
-    dict(max_text_tokens=-1), dict(max_text_tokens=305),
+    dict(max_text_tokens=-1), dict(max_text_tokens=305), dict(batch=32768),
 ]
 
 
