@@ -85,6 +85,7 @@ struct fastocr_handle {
   float* text_mass = nullptr;
   int32_t* sel = nullptr;
   int32_t* sel_cnt = nullptr;
+  unsigned int* hist0 = nullptr;  // [B, 256] first-digit histograms, merge -> top-k, zero in between
   int32_t* status = nullptr;
   int32_t* lens_shadow = nullptr;  // [B, 2] lens of the last warm-up step
 
@@ -151,8 +152,9 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   return p;
 }
 
-int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens) {
+int run_topk(fastocr_handle* h, const float* scores, const int32_t* lens, unsigned int* hist0) {
   TopkParams t{};
+  t.hist0 = hist0;
   t.scores = scores;
   t.score_stride = h->n_stride;
   t.n_cap = h->n_cap;
@@ -206,11 +208,12 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
     mp.logits = h->logits;
     mp.scores = scores_dst;
     mp.score_blocks = (h->n_stride + kMergeThreads - 1) / kMergeThreads;
+    if (topk) mp.hist0 = h->hist0;  // the top-k below reads and clears it
   }
   rc = timed(h, FASTOCR_KC_MERGE,
              [&](const LaunchTiming& lt) { return launch_merge(c.dtype, c.head_dim, mp, h->stream, lt); });
   if (rc || !topk) return rc;
-  return run_topk(h, scores_dst, lens);
+  return run_topk(h, scores_dst, lens, h->hist0);
 }
 
 // Non-focal layer: attention over the kept image rows and every text row.
@@ -370,6 +373,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   const size_t o_cnt = take(B * sizeof(int32_t));
   const size_t o_status = take(sizeof(int32_t));
   const size_t o_lens = take(B * 2 * sizeof(int32_t));
+  const size_t o_hist0 = take(pruned ? B * 256 * sizeof(unsigned int) : 0);
   h->arena_bytes = off;
   hipError_t e = hipMalloc(&h->arena, h->arena_bytes);
   if (e != hipSuccess) {
@@ -388,6 +392,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->sel_cnt = reinterpret_cast<int32_t*>(base + o_cnt);
   h->status = reinterpret_cast<int32_t*>(base + o_status);
   h->lens_shadow = reinterpret_cast<int32_t*>(base + o_lens);
+  h->hist0 = pruned ? reinterpret_cast<unsigned int*>(base + o_hist0) : nullptr;
   e = hipMemsetAsync(h->arena, 0, h->arena_bytes, h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) {
@@ -476,7 +481,7 @@ int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out) {
   // Implementation).  The image-token counts come from the lens of the last
   // warm-up step, copied aside when that step ran.
   const int deepest = h->focal.back();
-  int rc = run_topk(h, h->warm_scores + (size_t)deepest * c.batch * h->n_stride, h->lens_shadow);
+  int rc = run_topk(h, h->warm_scores + (size_t)deepest * c.batch * h->n_stride, h->lens_shadow, nullptr);
   if (rc) return rc;
   e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) return fail_hip(h, e);

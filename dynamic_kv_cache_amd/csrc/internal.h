@@ -67,6 +67,8 @@ struct MergeParams {
   float* scores;          // [B, n_stride]
   int32_t n_stride;
   int32_t score_blocks;   // workgroups per sequence for scores (0: none)
+  unsigned int* hist0;    // [B, 256] or null: add each image token's leading score
+                          // byte to its sequence's histogram (the top-k's first pass)
 };
 
 struct TopkParams {
@@ -80,6 +82,8 @@ struct TopkParams {
   int32_t idx_stride;
   int32_t* cnt;
   int32_t* status;        // may be null
+  unsigned int* hist0;    // [B, 256] leading-byte histograms of the scores, or null;
+                          // read and cleared to zero
 };
 
 // Optional timing: events recorded by the dispatch itself (start: when the

@@ -271,7 +271,8 @@ __device__ __forceinline__ unsigned int sum_before(const unsigned int* v, int wa
 // the output is in ascending index order and ties at theta go to the lowest
 // indices.
 __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int n, int k,
-                           int32_t* __restrict__ out, TopkShared& sh, const unsigned int (&reg)[kTopkRegKeys]) {
+                           int32_t* __restrict__ out, TopkShared& sh, const unsigned int (&reg)[kTopkRegKeys],
+                           unsigned int* hist0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
   const int base = tid * per;
@@ -287,7 +288,13 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
     for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0u;
     if (tid == 0) sh.ncand = 0;
     __syncthreads();
-    if (in_regs) {
+    if (pass == 0 && hist0) {
+      // the first digit's histogram was built with the scores
+      for (int i = tid; i < 256; i += kTopkThreads) {
+        sh.hist[0][i] = hist0[i];
+        hist0[i] = 0u;  // ready for the next focal layer
+      }
+    } else if (in_regs) {
 #pragma unroll
       for (int i = 0; i < kTopkRegKeys; ++i)
         if (i < per) hist_key(reg[i], i < mine, shift, mask, prefix, sh.hist[wave], lane);
@@ -424,7 +431,7 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
 // the row's capacity before the sequence extent (and so k) is read.
 __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, const int32_t* lens, int b,
                                               double tau, int idx_stride, int32_t* out, int32_t* cnt,
-                                              int32_t* status, TopkShared& sh) {
+                                              int32_t* status, unsigned int* hist0, TopkShared& sh) {
   const unsigned int* keys = reinterpret_cast<const unsigned int*>(scores);
   const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
   const int base = threadIdx.x * per;
@@ -438,8 +445,12 @@ __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, co
   if (n0 != n && threadIdx.x == 0 && status) atomicOr(status, FASTOCR_FLAG_LENS_CLAMPED);
   const int k = min(device_kept_count(tau, n), idx_stride);
   if (threadIdx.x == 0) *cnt = k;
-  if (k == 0) return;
-  block_topk(keys, n_cap, n, k, out, sh, reg);
+  if (k == 0) {
+    if (hist0)
+      for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist0[i] = 0u;
+    return;
+  }
+  block_topk(keys, n_cap, n, k, out, sh, reg, hist0);
 }
 
 // ---------------------------------------------------------------------------
@@ -976,8 +987,15 @@ constexpr int kScoreRegHeads = 32;
 
 __device__ void score_block(const MergeParams& p, int b, int sb) {
   __shared__ float2 s_mz[kMaxHeads];
+  __shared__ unsigned int s_hist[256];
   const int tid = threadIdx.x;
   const int j = sb * kMergeThreads + tid;
+  int n = 0;  // image tokens, clamped as the top-k clamps them
+  if (p.hist0) {
+    const int n0 = p.lens[2 * b], l0 = p.lens[2 * b + 1];
+    n = min(max(n0, 0), min(max(l0, 0), p.n_cap));
+    for (int i = tid; i < 256; i += kMergeThreads) s_hist[i] = 0u;
+  }
   const float* lg = p.logits + (size_t)b * p.Hq * p.n_stride + min(j, p.n_stride - 1);
   float x[kScoreRegHeads];
 #pragma unroll
@@ -1016,14 +1034,22 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
   __syncthreads();
   // tokens past this sequence's image tokens get scores too (from stale
   // logits); nothing reads them
-  if (j >= p.n_stride) return;
   float s = 0.f;
+  if (j < p.n_stride) {
 #pragma unroll
-  for (int h = 0; h < kScoreRegHeads; ++h)
-    if (h < p.Hq) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
-  for (int h = kScoreRegHeads; h < p.Hq; ++h)
-    s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
-  p.scores[(size_t)b * p.n_stride + j] = s;
+    for (int h = 0; h < kScoreRegHeads; ++h)
+      if (h < p.Hq) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
+    for (int h = kScoreRegHeads; h < p.Hq; ++h)
+      s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
+    p.scores[(size_t)b * p.n_stride + j] = s;
+  }
+  if (p.hist0) {
+    // leading byte of the image tokens' scores, the top-k's first digit
+    hist_key(__float_as_uint(s), j < n, 24, 0u, 0u, s_hist, tid & 63);
+    __syncthreads();
+    for (int i = tid; i < 256; i += kMergeThreads)
+      if (s_hist[i]) atomicAdd(p.hist0 + (size_t)b * 256 + i, s_hist[i]);
+  }
 }
 
 template <typename T, int D>
@@ -1036,12 +1062,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __shared__ TopkShared sh;
   const int b = blockIdx.x;
+  unsigned int* hist0 = p.hist0 ? p.hist0 + (size_t)b * 256 : nullptr;
   if (p.n_cap < 1) {
     if (threadIdx.x == 0) p.cnt[b] = 0;
+    if (hist0)
+      for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist0[i] = 0u;
     return;
   }
   topk_sequence(p.scores + (size_t)b * p.score_stride, p.n_cap, p.lens, b, p.tau, p.idx_stride,
-                p.idx + (size_t)b * p.idx_stride, p.cnt + b, p.status, sh);
+                p.idx + (size_t)b * p.idx_stride, p.cnt + b, p.status, hist0, sh);
 }
 
 // ---------------------------------------------------------------------------

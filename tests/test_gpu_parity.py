@@ -218,6 +218,26 @@ def test_trajectory_ragged_small(monkeypatch, rows):
     log(f"[ragged] n={up.st.n_img.tolist()} focal {rec.focal}, worst out {chk.worst_out:.2e}")
 
 
+@pytest.mark.parametrize("name,dtype,head_dim,steps", [
+    ("tiny-fp32", "bf16", 64, None),    # bf16 kernels at d = 64
+    ("tiny-fp32", "f32", 128, None),    # fp32 kernels at d = 128
+    ("7b-b1", "bf16", 64, 10),          # several splits per sequence at d = 64
+])
+def test_trajectory_other_dtype_and_head_dim(name, dtype, head_dim, steps):
+    wl = get_workload(name).with_overrides(dtype=dtype, head_dim=head_dim)
+    if name == "7b-b1":
+        wl = wl.with_overrides(num_layers=4, focal_band=(1, 2), num_focal=2, warmup_steps=2)
+    up = upload(wl, steps=steps)
+    T = up.wl.steps
+    rec = run(up, fo.fastocr_create(make_config(up)), T)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, T):
+        chk.pruned_step(t)
+    log(f"[{name} {dtype} d={head_dim}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
 def test_trajectory_layer0_focal():
     # Layer 0 is forced focal: the warm start is never used for attention.
     wl = get_workload("tiny-fp32").with_overrides(planted_layers=(0, 2))
