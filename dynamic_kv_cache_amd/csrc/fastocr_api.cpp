@@ -340,8 +340,9 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   if (c.min_img_tokens > 0)
     sparse_rows = std::min(sparse_rows, h->k_max + c.max_seq_len - c.min_img_tokens);
   if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, h->k_max + c.max_text_tokens);
-  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE) * num_cu,
-                                    "FASTOCR_SPARSE_ROWS");
+  // Kept-token passes: one round per split, the most workgroups, dispatched
+  // split-major (measured faster than fewer, longer splits at every batch).
+  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, "FASTOCR_SPARSE_ROWS");
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
   h->max_splits = std::max(h->full_splits, h->sparse_splits);
   // Full passes: every sequence has at least min_img_tokens image rows and
