@@ -20,7 +20,8 @@ from typing import Dict, List, Optional, Sequence
 
 from . import _abi
 from ._abi import (DTYPE_BF16, DTYPE_F32, ERR_HIP, ERR_INVALID_ARG, ERR_OOM, ERR_STATE,  # noqa: F401
-                   FLAG_INDEX_CLAMPED, FLAG_LENS_CLAMPED, KC_NAMES, MODE_FULL, MODE_PRUNED, OK)
+                   FLAG_INDEX_CLAMPED, FLAG_LENS_CLAMPED, FLAG_ROWS_TRUNCATED, KC_NAMES, MODE_FULL, MODE_PRUNED,
+                   OK)
 
 
 class FastOCRError(RuntimeError):

@@ -62,8 +62,9 @@ extern "C" {
 /* ---- device status flags (fastocr_get_status) ---------------------------- */
 #define FASTOCR_FLAG_LENS_CLAMPED 1 /* a lens entry was out of range and was clamped */
 #define FASTOCR_FLAG_INDEX_CLAMPED 2 /* a selected index was out of range and was clamped */
-#define FASTOCR_FLAG_ROWS_TRUNCATED 4 /* a sequence had fewer image tokens than min_img_tokens;
-                                        its sparse rows beyond the launch were not attended */
+#define FASTOCR_FLAG_ROWS_TRUNCATED 4 /* a sequence had fewer image tokens than min_img_tokens
+                                        or more text tokens than max_text_tokens; its kept-token
+                                        rows beyond the launch were not attended */
 
 /* ---- kernel classes timed by fastocr_get_timing -------------------------- */
 #define FASTOCR_KC_FULL_SPLIT 0   /* split-K full attention (warm-up, FULL mode) */

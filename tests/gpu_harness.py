@@ -76,13 +76,14 @@ def upload(wl: Workload, steps: Optional[int] = None, dev="cuda:0") -> Uploaded:
 
 def make_config(up: Uploaded, mode="pruned", tau=None, **kw) -> fo.Config:
     wl, st = up.wl, up.st
-    return fo.Config(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads,
-                     num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, batch=wl.batch,
-                     max_seq_len=st.max_seq_len, max_img_tokens=int(st.n_img.max()),
-                     min_img_tokens=int(st.n_img.min()), max_text_tokens=int(st.n_prompt.max()) + wl.steps,
-                     tau=wl.tau if tau is None else tau,
-                     num_focal=wl.num_focal, warmup_steps=wl.warmup_steps, dtype=wl.dtype,
-                     mode=mode, **kw)
+    args = dict(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads,
+                num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, batch=wl.batch,
+                max_seq_len=st.max_seq_len, max_img_tokens=int(st.n_img.max()),
+                min_img_tokens=int(st.n_img.min()), max_text_tokens=int(st.n_prompt.max()) + wl.steps,
+                tau=wl.tau if tau is None else tau,
+                num_focal=wl.num_focal, warmup_steps=wl.warmup_steps, dtype=wl.dtype, mode=mode)
+    args.update(kw)
+    return fo.Config(**args)
 
 
 @dataclass

@@ -160,6 +160,25 @@ def test_lens_out_of_range_sets_flag():
     assert fo.fastocr_get_status(h) & fo.FLAG_LENS_CLAMPED
 
 
+def test_text_beyond_declared_bound_sets_flag():
+    # max_text_tokens = 1 sizes the kept-token launch for k + 1 rows (three
+    # 128-row splits for k = 320); 66 text rows exceed it: the rows beyond the
+    # launch are dropped and the handle reports it
+    up = upload(get_workload("7b-b1").with_overrides(num_layers=2, warmup_steps=1, num_focal=1), steps=2)
+    h = fo.fastocr_create(make_config(up, max_text_tokens=1))
+    wl = up.wl
+    out = torch.empty((1, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
+    for l in range(wl.num_layers):
+        fo.fastocr_attend(h, l, up.Qd[l][0], up.Kd[l], up.Vd[l], up.lens[0], out)
+    fo.fastocr_profile_warmup(h)
+    assert fo.fastocr_get_status(h) == 0
+    fo.fastocr_set_focal_layers(h, [1])
+    fo.fastocr_attend(h, 0, up.Qd[0][1], up.Kd[0], up.Vd[0], up.lens[1], out)  # non-focal
+    torch.cuda.synchronize()
+    assert fo.fastocr_get_status(h) & fo.FLAG_ROWS_TRUNCATED
+    assert torch.isfinite(out.float()).all()
+
+
 def test_state_machine_errors():
     up = upload(get_workload("tiny-fp32"), steps=5)
     wl = up.wl
