@@ -64,16 +64,19 @@ def parse():
 
 
 CAL_BYTES = 256 << 20
-KERNEL_SRC = os.path.join(ROOT, "dynamic_kv_cache_amd", "csrc", "kernels.hip")
+# the library's kernels and the host code that sizes their launches: counter
+# summaries taken with other sources no longer describe the launches
+LIBRARY_SRC = [os.path.join(ROOT, "dynamic_kv_cache_amd", "csrc", f)
+               for f in ("kernels.hip", "fastocr_api.cpp", "internal.h")]
 
 
-def kernel_source_digest():
+def library_source_digest():
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-KERNEL_CLASSES = ["full_split", "focal_split", "sparse_split", "merge", "topk"]
+    h = hashlib.sha256()
+    for path in LIBRARY_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_class(name):
@@ -107,7 +110,7 @@ def pmc_summary(directories):
     for (name, ctr), vals in acc.items():
         if "add<long>" in name and np.mean(vals) > 0.5 * CAL_BYTES / 1024:
             scale[ctr] = CAL_BYTES / 1024 / np.mean(vals)
-    print(f"kernel_source_sha256_16: {kernel_source_digest()}")
+    print(f"library_source_sha256_16: {library_source_digest()}")
     for ctr, f in sorted(scale.items()):
         print(f"calibration_{ctr}: {f:.4f}  # {CAL_BYTES >> 20} MiB int64 add counts "
               f"{CAL_BYTES / 1024 / f:.0f} KiB")
@@ -135,7 +138,7 @@ def trace_summary(directory, command, bench_json=None):
     import glob
     stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     print(f"# command: {command}")
-    print(f"kernel_source_sha256_16: {kernel_source_digest()}")
+    print(f"library_source_sha256_16: {library_source_digest()}")
     bench = {}
     bj = bench_json or os.path.join(directory, "bench.json")
     if os.path.exists(bj):
@@ -171,7 +174,7 @@ def read_traffic(kernel, workload):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_digest():
+    if vals.get("library_source_sha256_16") != library_source_digest():
         return None
     try:
         return float(vals[f"{kernel}.hbm_bytes_per_launch"])
