@@ -894,9 +894,52 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     const int s = sl + i * SL;
     pv[i] = s < p.grid_splits ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // up to 64 splits: lane s of every wave holds split s's state
+  const float4 q = (p.grid_splits <= 64 && lane < p.grid_splits) ? p.pstat[slot0 + lane]
+                                                                   : make_float4(-INFINITY, 0.f, 0.f, 0.f);
 
   const int nsplit = p.grid_splits;
   T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  if (nsplit <= 64) {
+    // Up to 64 splits: every wave derives the head's softmax totals itself
+    // and takes the weights of its partial outputs by lane permutes: no
+    // workgroup barrier.
+    const float M = wave_max(q.x);
+    if (M == -INFINITY) {  // no rows at all
+      for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
+      if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
+      return;
+    }
+    const float w = q.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(q.x - M);
+    const float Z = wave_sum(q.y * w);
+    const float L = wave_sum(q.z * w);
+    const float Zt = wave_sum(q.w * w);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int s = sl + i * SL;
+      const float ws = __shfl(w, s & 63);
+      if (s < nsplit && ws != 0.f) {
+        a0 += pv[i].x * ws;
+        a1 += pv[i].y * ws;
+        a2 += pv[i].z * ws;
+        a3 += pv[i].w * ws;
+      }
+    }
+    a0 = group_sum<SL>(a0);
+    a1 = group_sum<SL>(a1);
+    a2 = group_sum<SL>(a2);
+    a3 = group_sum<SL>(a3);
+    if (sl == 0) {
+      const float inv = 1.f / L;
+      store_out<T>(out + 4 * d4 + 0, a0 * inv);
+      store_out<T>(out + 4 * d4 + 1, a1 * inv);
+      store_out<T>(out + 4 * d4 + 2, a2 * inv);
+      store_out<T>(out + 4 * d4 + 3, a3 * inv);
+    }
+    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = Zt / Z;
+    return;
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NST; ++i)
