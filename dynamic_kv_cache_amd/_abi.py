@@ -63,7 +63,7 @@ class Info(ctypes.Structure):
         ("sparse_rows_per_split", c_int32),
         ("sparse_max_splits", c_int32),
         ("sparse_direct", c_int32),
-        ("reserved", c_int32),
+        ("sparse_wave_states", c_int32),
         ("scratch_bytes", c_int64),
     ]
 

@@ -43,8 +43,8 @@ int env_int(const char* name, int dflt) {
 // KV head): whole rounds (kRowsPerRound rows, one tile group per wave),
 // the fewest that still give about `target` workgroups, so a small batch
 // spreads over many CUs (one CU streams only ~60 GB/s) and a large one
-// reads long runs per workgroup.  At most kMaxMergeSplits splits.
-int plan_rows_per_split(int64_t pairs, int rows, int target, const char* env) {
+// reads long runs per workgroup.  At most max_splits splits.
+int plan_rows_per_split(int64_t pairs, int rows, int target, int max_splits, const char* env) {
   int R = env_int(env, 0);
   if (R <= 0) {
     const int64_t want = (pairs * (int64_t)std::max(rows, 1) + target - 1) / target;
@@ -52,7 +52,7 @@ int plan_rows_per_split(int64_t pairs, int rows, int target, const char* env) {
   } else {
     R = (int)align_up((size_t)R, kTileRows);
   }
-  while ((rows + R - 1) / R > kMaxMergeSplits) R += kRowsPerRound;
+  while ((rows + R - 1) / R > max_splits) R += kRowsPerRound;
   return R;
 }
 
@@ -65,6 +65,8 @@ struct fastocr_handle {
   int G = 0, D = 0, n_cap = 0, n_stride = 0, k_max = 0;
   int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
   int full_sure = 0, sparse_sure = 0;  // splits that hold rows for any accepted sequence
+  bool wave_states = false;            // kept-token splits write one state per wave
+  int states_per_sparse_split = 1;
 
   float scale_log2 = 0.f;
 
@@ -184,7 +186,7 @@ MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool
   m.k_stride = h->k_max;
   m.max_splits = h->max_splits;
   m.rows_per_split = sparse ? h->sparse_R : h->full_R;
-  m.grid_splits = sparse ? h->sparse_splits : h->full_splits;
+  m.grid_splits = sparse ? h->sparse_splits * h->states_per_sparse_split : h->full_splits;  // states per head
   m.n_stride = h->n_stride;
   return m;
 }
@@ -224,6 +226,7 @@ int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, c
   const fastocr_config& c = h->cfg;
   SplitParams sp = split_params(h, q, k, v, lens, out, true);
   sp.direct = h->sparse_splits <= 1 ? 1 : 0;
+  sp.wave_states = h->wave_states ? 1 : 0;
   int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream, lt);
   });
@@ -333,7 +336,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
   // about one wave of resident split workgroups per launch
   h->full_R = plan_rows_per_split(pairs, c.max_seq_len, split_blocks_per_cu(KIND_FULL) * num_cu,
-                                  "FASTOCR_FULL_ROWS");
+                                  kMaxMergeSplits, "FASTOCR_FULL_ROWS");
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
   // rows of a kept-token pass: kept image rows + text rows
   int sparse_rows = c.max_seq_len;
@@ -342,9 +345,20 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, h->k_max + c.max_text_tokens);
   // Kept-token passes: one round per split, the most workgroups, dispatched
   // split-major (measured faster than fewer, longer splits at every batch).
-  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, "FASTOCR_SPARSE_ROWS");
+  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
+                                    "FASTOCR_SPARSE_ROWS");
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
-  h->max_splits = std::max(h->full_splits, h->sparse_splits);
+  // A kept-token pass of at most one workgroup per CU is latency-bound: its
+  // waves then write their states themselves (no cross-wave combine and
+  // barrier; measured 5.75 against 6.4 us per launch at 7B-like B=1), as
+  // long as the merge keeps one state per lane.  A larger pass streams, and
+  // there the 4x partial-output traffic costs more than the combine.
+  h->wave_states = h->sparse_splits > 1 && pairs * h->sparse_splits <= num_cu &&
+                   h->sparse_splits * kSplitWaves <= 64;
+  h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1;
+  h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
+  // state slots per head (a direct kept-token pass writes none)
+  h->max_splits = std::max(h->full_splits, h->sparse_splits * h->states_per_sparse_split);
   // Full passes: every sequence has at least min_img_tokens image rows and
   // the current token, so splits below that hold rows and load their K/V
   // ahead; the others (possibly empty for a short sequence of a ragged
@@ -578,6 +592,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->full_max_splits = h->full_splits;
   info->sparse_rows_per_split = h->sparse_R;
   info->sparse_max_splits = h->sparse_splits;
+  info->sparse_wave_states = h->wave_states ? 1 : 0;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;

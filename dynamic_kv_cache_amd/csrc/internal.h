@@ -40,7 +40,8 @@ struct SplitParams {
   const int32_t* sel;     // [B, k_stride]   (sparse)
   const int32_t* sel_cnt; // [B]             (sparse)
   float* logits;          // [B, Hq, n_stride] log2-domain scaled logits (focal)
-  float4* pstat;          // [B, Hq, max_splits] (max, sum p, sum rounded p, text sum p)
+  float4* pstat;          // [B, Hq, max_splits] (max, sum p, sum rounded p, text sum p): state
+                          // `split`, or split * kSplitWaves + wave with wave_states
   float* po;              // [B, Hq, max_splits, D] unnormalised partial outputs
   void* out;              // [B, Hq, D] in the io dtype (direct outputs)
   int32_t* status;
@@ -48,7 +49,9 @@ struct SplitParams {
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
   int32_t sure_splits;    // splits that hold rows for every accepted sequence
   int32_t direct;         // one split per sequence (grid_splits == 1): write outputs here;
-                          // otherwise every launched split writes a state (empty: max -inf)
+                          // otherwise every launched split writes its states (empty: max -inf)
+  int32_t wave_states;    // kept-token pass, not direct: one state per wave instead of a
+                          // cross-wave combine per workgroup
   float scale_log2;       // logit scale * log2(e)
 };
 
@@ -62,7 +65,8 @@ struct MergeParams {
   void* out;              // [B, Hq, D] in the io dtype
   float* text_mass;       // [B, Hq] or null
   int32_t* status;
-  int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split, grid_splits;
+  int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split;
+  int32_t grid_splits;    // states per head written by the split pass
   const float* logits;    // [B, Hq, n_stride]
   float* scores;          // [B, n_stride]
   int32_t n_stride;

@@ -564,10 +564,13 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
     if (direct) {  // no rows at all: zero output
       T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
       for (int i = tid; i < G * D; i += NT) store_out<T>(out + i, 0.f);
-    } else if (tid < G) {
-      // an empty split: a state that carries no weight in the merge
-      p.pstat[((size_t)b * p.Hq + kvh * G + tid) * p.max_splits + split] =
-          make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    } else {
+      // an empty split: states that carry no weight in the merge (one per
+      // wave with per-wave states, one per workgroup otherwise)
+      const int SPW = (KIND == KIND_SPARSE && p.wave_states) ? NW : 1;
+      for (int i = tid; i < G * SPW; i += NT)
+        p.pstat[((size_t)b * p.Hq + kvh * G + i / SPW) * p.max_splits + (size_t)split * SPW + i % SPW] =
+            make_float4(-INFINITY, 0.f, 0.f, 0.f);
     }
     return;
   }
@@ -778,6 +781,31 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   lsum += __shfl_xor(lsum, 32);
   zt += __shfl_xor(zt, 16);
   zt += __shfl_xor(zt, 32);
+
+  if constexpr (KIND == KIND_SPARSE) {
+    if (p.wave_states) {
+      // One state per wave (state split * NW + wave), straight from
+      // registers: no cross-wave combine, no barrier.  Lane
+      // (c, g) holds head c's unnormalised outputs for d in [g*D/4, (g+1)*D/4),
+      // element d = (4g + i)*NDB + db in acc[db][i].  A wave without rows
+      // leaves max -inf, which the merge gives weight 0 without reading its
+      // partial output.
+      if (col < G) {
+        const size_t st = ((size_t)b * p.Hq + kvh * G + col) * p.max_splits + (size_t)split * NW + wave;
+        if (grp == 0) p.pstat[st] = make_float4(m_run, z, lsum, zt);
+        if (m_run != -INFINITY) {
+          float4* o = reinterpret_cast<float4*>(p.po + st * D + grp * (D / 4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int d4 = 0; d4 < NDB / 4; ++d4)
+              o[(i * NDB) / 4 + d4] = make_float4(acc[4 * d4][i], acc[4 * d4 + 1][i], acc[4 * d4 + 2][i],
+                                                  acc[4 * d4 + 3][i]);
+        }
+      }
+      return;
+    }
+  }
   if (grp == 0) {
     s_stat[wave][col][0] = m_run;
     s_stat[wave][col][1] = z;

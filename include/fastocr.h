@@ -108,7 +108,7 @@ typedef struct fastocr_info {
   int32_t sparse_rows_per_split;
   int32_t sparse_max_splits;
   int32_t sparse_direct;  /* 1: non-focal layers finish in one split (no merge launch) */
-  int32_t reserved;
+  int32_t sparse_wave_states; /* 1: kept-token splits write one merge state per wave */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
 

@@ -94,11 +94,15 @@ def test_topk_bit_exact(tau, n_cap):
 
 # kept-token pass with several split workgroups per sequence (+ merge
 # launch), and with one split per sequence that writes the output directly
-SPARSE_VARIANTS = pytest.mark.parametrize("rows", ["", "16384"], ids=["split-merge", "direct"])
+# kept-token pass variants: split + merge with one state per workgroup (a
+# cross-wave combine) or one per wave, and one split per sequence (no merge)
+SPARSE_VARIANTS = pytest.mark.parametrize("rows", [("", "0"), ("", "1"), ("16384", "")],
+                                          ids=["split-merge", "wave-states", "direct"])
 
 
 def _sparse_variant(monkeypatch, rows):
-    monkeypatch.setenv("FASTOCR_SPARSE_ROWS", rows)
+    monkeypatch.setenv("FASTOCR_SPARSE_ROWS", rows[0])
+    monkeypatch.setenv("FASTOCR_WAVE_STATES", rows[1])
 
 
 @SPARSE_VARIANTS
@@ -109,7 +113,9 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
     up = upload(get_workload("7b-b1").with_overrides(num_layers=3, warmup_steps=1, num_focal=1, tau=tau),
                 steps=3)
     h = fo.fastocr_create(make_config(up))
-    assert fo.fastocr_get_info(h)["sparse_direct"] == (1 if rows else 0)
+    info = fo.fastocr_get_info(h)
+    assert info["sparse_direct"] == (1 if rows[0] else 0)
+    assert info["sparse_wave_states"] == (1 if rows[1] == "1" else 0)
     wl = up.wl
     for l in range(wl.num_layers):  # one warm-up step
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
