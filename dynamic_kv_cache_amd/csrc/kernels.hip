@@ -197,6 +197,9 @@ __device__ __forceinline__ int device_kept_count(double tau, int n) {
 }
 
 struct TopkShared {
+  // keys staged from coalesced loads: thread t's keys [t*per, t*per + per)
+  // at [t*(per+1), ...), padded so the per-thread reads hit distinct banks
+  unsigned int stage[kTopkThreads * (kTopkRegKeys + 1)];
   unsigned int hist[kTopkThreads / 64][256];  // one histogram per wave
   alignas(16) unsigned int wave_sum[kTopkThreads / 64];
   alignas(16) unsigned int wave_sum2[kTopkThreads / 64];
@@ -262,52 +265,76 @@ __device__ __forceinline__ unsigned int sum_before(const unsigned int* v, int wa
 }
 
 // Top-k of the non-negative float keys[0, n) by one kTopkThreads workgroup.
-// Thread t owns keys [t*per, t*per + per) of the row's capacity n_cap >= n,
-// in registers when per is small (loaded before n and k are known),
-// re-read from memory otherwise.  A 4-pass radix select (8 bits per pass,
-// most significant first; the IEEE bits of a non-negative float order like
-// its value) finds the k-th largest key theta and how many keys equal to
-// theta are kept; one workgroup prefix sum then places every kept index, so
-// the output is in ascending index order and ties at theta go to the lowest
-// indices.
-__device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int n, int k,
-                           int32_t* __restrict__ out, TopkShared& sh, const unsigned int (&reg)[kTopkRegKeys],
-                           unsigned int* hist0) {
+// Thread t owns keys [t*per, t*per + per) of the row's capacity n_cap >= n.
+// With PER > 0 they are held in registers (per = PER, a power of two up to
+// kTopkRegKeys): loaded coalesced (key tid + i * kTopkThreads) before n and
+// k are known, and moved to their owners through LDS when a pass first needs
+// them.  With PER = 0 they are re-read from memory per pass.  A 4-pass
+// radix select (8 bits per pass, most significant first; the IEEE bits of a
+// non-negative float order like its value) finds the k-th largest key theta
+// and how many keys equal to theta are kept; one workgroup prefix sum then
+// places every kept index, so the output is in ascending index order and
+// ties at theta go to the lowest indices.
+template <int PER>
+__device__ void block_topk(const unsigned int* __restrict__ keys, int per, int n, int k,
+                           int32_t* __restrict__ out, TopkShared& sh, unsigned int (&reg)[PER > 0 ? PER : 1],
+                           bool have_c0, unsigned int c0) {
+  constexpr bool IN_REGS = PER > 0;
+  constexpr int R = IN_REGS ? PER : 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
+  if (IN_REGS) per = PER;
   const int base = tid * per;
   const int mine = max(0, min(per, n - base));
-  const bool in_regs = per <= kTopkRegKeys;
+  // in-register keys: load order -> owners (thread t's keys at
+  // stage[t*(PER+1) ...], padded so the owners' reads hit distinct banks)
+  bool staged = !IN_REGS;
+  auto stage_write = [&]() {
+    constexpr int LP = __builtin_ctz((unsigned int)R);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int j = tid + i * kTopkThreads;
+      sh.stage[(j >> LP) * (R + 1) + (j & (R - 1))] = reg[i];
+    }
+  };
+  auto stage_read = [&]() {  // after a barrier
+#pragma unroll
+    for (int i = 0; i < R; ++i) reg[i] = sh.stage[tid * (R + 1) + i];
+    staged = true;
+  };
 
   unsigned int prefix = 0u, mask = 0u;
   int remaining = k;
   bool ranked = false;
+  if (tid == 0) sh.ncand = 0;
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0u;
-    if (tid == 0) sh.ncand = 0;
-    __syncthreads();
-    if (pass == 0 && hist0) {
-      // the first digit's histogram was built with the scores
-      for (int i = tid; i < 256; i += kTopkThreads) {
-        sh.hist[0][i] = hist0[i];
-        hist0[i] = 0u;  // ready for the next focal layer
-      }
-    } else if (in_regs) {
+    // the first digit's counts may come with the scores (thread t < 256
+    // holds digit 255 - t): then the first pass builds no histogram
+    const bool from_c0 = pass == 0 && have_c0;
+    if (!from_c0) {
+      if (IN_REGS && !staged) stage_write();
+      for (int i = tid; i < (kTopkThreads / 64) * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0u;
+      __syncthreads();
+      if (IN_REGS && !staged) stage_read();
+      if constexpr (IN_REGS) {
 #pragma unroll
-      for (int i = 0; i < kTopkRegKeys; ++i)
-        if (i < per) hist_key(reg[i], i < mine, shift, mask, prefix, sh.hist[wave], lane);
-    } else {
+        for (int i = 0; i < R; ++i) hist_key(reg[i], i < mine, shift, mask, prefix, sh.hist[wave], lane);
+      } else {
 #pragma unroll 1
-      for (int i = 0; i < per; ++i)
-        hist_key(keys[min(base + i, n - 1)], i < mine, shift, mask, prefix, sh.hist[wave], lane);
+        for (int i = 0; i < per; ++i)
+          hist_key(keys[min(base + i, n - 1)], i < mine, shift, mask, prefix, sh.hist[wave], lane);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // thread t < 256 owns digit 255 - t: inclusive count in descending digit order
     unsigned int c = 0, incl = 0;
     if (tid < 256) {
-      for (int w = 0; w < kTopkThreads / 64; ++w) c += sh.hist[w][255 - tid];
+      if (from_c0) {
+        c = c0;
+      } else {
+        for (int w = 0; w < kTopkThreads / 64; ++w) c += sh.hist[w][255 - tid];
+      }
       incl = wave_incl_scan(c);
       if (lane == 63) sh.wave_sum[wave] = incl;
     }
@@ -331,14 +358,18 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
     }
   }
 
+  if (IN_REGS && !staged) {
+    stage_write();
+    __syncthreads();
+    stage_read();
+  }
   if (ranked) {
     // The k-th key's bin is small: gather it and rank its keys pairwise by
     // (value descending, index ascending); the key of rank remaining - 1 is
     // theta.
-    if (in_regs) {
+    if constexpr (IN_REGS) {
 #pragma unroll
-      for (int i = 0; i < kTopkRegKeys; ++i)
-        if (i < per) gather_key(reg[i], i < mine, base + i, mask, prefix, sh, lane);
+      for (int i = 0; i < R; ++i) gather_key(reg[i], i < mine, base + i, mask, prefix, sh, lane);
     } else {
 #pragma unroll 1
       for (int i = 0; i < per; ++i)
@@ -373,9 +404,9 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
   const int need_eq = sh.need_eq;       // keys equal to theta to keep, lowest index first
 
   unsigned int gt = 0, eq = 0;
-  if (in_regs) {
+  if constexpr (IN_REGS) {
 #pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i) {
+    for (int i = 0; i < R; ++i) {
       gt += (i < mine && reg[i] > theta) ? 1u : 0u;
       eq += (i < mine && reg[i] == theta) ? 1u : 0u;
     }
@@ -387,10 +418,10 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
       eq += key == theta ? 1u : 0u;
     }
   }
-  // exclusive prefix sums of both counts over the workgroup
+  // exclusive prefix sums of both counts over the workgroup (wave_sum was
+  // last read before the barrier above)
   unsigned int gt_incl = wave_incl_scan(gt);
   unsigned int eq_incl = wave_incl_scan(eq);
-  __syncthreads();
   if (lane == 63) {
     sh.wave_sum[wave] = gt_incl;
     sh.wave_sum2[wave] = eq_incl;
@@ -400,19 +431,22 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
   eq_incl += sum_before(sh.wave_sum2, wave);
   int eq_seen = (int)(eq_incl - eq);
   int pos = (int)(gt_incl - gt) + min(eq_seen, need_eq);
-  if (in_regs) {
-    // unrolled over the register keys: static register indices, one
-    // predicated store per kept key
+  if constexpr (IN_REGS) {
+    // kept indices land in LDS (the staging area, free by now) and leave in
+    // one coalesced copy
+    int* kept = reinterpret_cast<int*>(sh.stage);
 #pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i) {
+    for (int i = 0; i < R; ++i) {
       const bool valid = i < mine;
       const bool gt_i = valid && reg[i] > theta;
       const bool eq_i = valid && reg[i] == theta;
       const bool keep = gt_i || (eq_i && eq_seen < need_eq);
-      if (keep) out[pos] = base + i;
+      if (keep) kept[pos] = base + i;
       pos += keep ? 1 : 0;
       eq_seen += eq_i ? 1 : 0;
     }
+    __syncthreads();
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = kept[i];
   } else {
 #pragma unroll 1
     for (int i = 0; i < mine; ++i) {
@@ -427,30 +461,37 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int n_cap, int
   }
 }
 
-// Top-k of one sequence's scores: the keys this thread owns are loaded from
-// the row's capacity before the sequence extent (and so k) is read.
+// Top-k of one sequence's scores.  The sequence extent is read first (no
+// store precedes it, so it can come through the scalar cache), then the
+// first digit's counts and the keys this thread loads, all before k is known.
+template <int PER>
 __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, const int32_t* lens, int b,
                                               double tau, int idx_stride, int32_t* out, int32_t* cnt,
                                               int32_t* status, unsigned int* hist0, TopkShared& sh) {
+  constexpr int R = PER > 0 ? PER : 1;
   const unsigned int* keys = reinterpret_cast<const unsigned int*>(scores);
-  const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
-  const int base = threadIdx.x * per;
-  unsigned int reg[kTopkRegKeys];
-  if (per <= kTopkRegKeys) {
-#pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i) reg[i] = keys[min(base + i, n_cap - 1)];
-  }
+  const int tid = threadIdx.x;
   const int n0 = lens[2 * b];
-  const int n = min(max(n0, 0), min(max(lens[2 * b + 1], 0), n_cap));
-  if (n0 != n && threadIdx.x == 0 && status) atomicOr(status, FASTOCR_FLAG_LENS_CLAMPED);
-  const int k = min(device_kept_count(tau, n), idx_stride);
-  if (threadIdx.x == 0) *cnt = k;
-  if (k == 0) {
-    if (hist0)
-      for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist0[i] = 0u;
-    return;
+  const int l0 = lens[2 * b + 1];
+  // the first digit's counts (thread t < 256: digit 255 - t) are the first
+  // thing the select needs; every thread issues one load (no branch, so the
+  // wait for it does not also wait for the keys)
+  const unsigned int* c0_src = hist0 ? hist0 + (255 - (tid & 255)) : keys;
+  unsigned int c0 = *c0_src;
+  unsigned int reg[R];
+  if constexpr (PER > 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) reg[i] = keys[min(tid + i * kTopkThreads, n_cap - 1)];
   }
-  block_topk(keys, n_cap, n, k, out, sh, reg, hist0);
+  const int n = min(max(n0, 0), min(max(l0, 0), n_cap));
+  if (n0 != n && tid == 0 && status) atomicOr(status, FASTOCR_FLAG_LENS_CLAMPED);
+  const int k = min(device_kept_count(tau, n), idx_stride);
+  if (tid == 0) *cnt = k;
+  // cleared for the next focal layer (this thread's own load of it is older)
+  if (hist0 && tid < 256) hist0[255 - tid] = 0u;
+  if (k == 0) return;
+  const int per = (n_cap + kTopkThreads - 1) / kTopkThreads;
+  block_topk<PER>(keys, per, n, k, out, sh, reg, hist0 != nullptr, tid < 256 ? c0 : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -1130,6 +1171,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   else score_block(p, b, blockIdx.x - p.Hq);
 }
 
+// PER: keys per thread held in registers (a power of two up to
+// kTopkRegKeys), or 0 for rows longer than kTopkRegKeys * kTopkThreads.
+template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __shared__ TopkShared sh;
   const int b = blockIdx.x;
@@ -1140,8 +1184,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
       for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist0[i] = 0u;
     return;
   }
-  topk_sequence(p.scores + (size_t)b * p.score_stride, p.n_cap, p.lens, b, p.tau, p.idx_stride,
-                p.idx + (size_t)b * p.idx_stride, p.cnt + b, p.status, hist0, sh);
+  topk_sequence<PER>(p.scores + (size_t)b * p.score_stride, p.n_cap, p.lens, b, p.tau, p.idx_stride,
+                     p.idx + (size_t)b * p.idx_stride, p.cnt + b, p.status, hist0, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1199,7 +1243,14 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream, const LaunchTiming& timing) {
-  return launch(topk_kernel, dim3(p.B), dim3(kTopkThreads), stream, timing, p);
+  const dim3 grid(p.B), block(kTopkThreads);
+  const int per = (p.n_cap + kTopkThreads - 1) / kTopkThreads;
+  if (per <= 1) return launch(topk_kernel<1>, grid, block, stream, timing, p);
+  if (per <= 2) return launch(topk_kernel<2>, grid, block, stream, timing, p);
+  if (per <= 4) return launch(topk_kernel<4>, grid, block, stream, timing, p);
+  if (per <= 8) return launch(topk_kernel<8>, grid, block, stream, timing, p);
+  if (per <= kTopkRegKeys) return launch(topk_kernel<kTopkRegKeys>, grid, block, stream, timing, p);
+  return launch(topk_kernel<0>, grid, block, stream, timing, p);
 }
 
 }  // namespace fastocr
