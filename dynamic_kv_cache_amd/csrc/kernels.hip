@@ -376,22 +376,36 @@ __device__ void block_topk(const unsigned int* __restrict__ keys, int per, int n
         gather_key(keys[min(base + i, n - 1)], i < mine, base + i, mask, prefix, sh, lane);
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane c holds candidate c; every candidate is compared with all
-      // others through lane reads (no LDS round trips in the loop)
-      const int nc = __builtin_amdgcn_readfirstlane(sh.ncand);  // uniform
-      const unsigned int kc = lane < nc ? sh.cand_key[lane] : 0u;
-      const int ic = lane < nc ? sh.cand_idx[lane] : 0;
-      int greater = 0, before = 0;
-      for (int j = 0; j < nc; ++j) {
-        const unsigned int kj = (unsigned int)__builtin_amdgcn_readlane((int)kc, j);
-        const int ij = __builtin_amdgcn_readlane(ic, j);
+    // lane c of every wave holds candidate c; wave w compares it with
+    // candidates [w*CPW, (w+1)*CPW) (broadcast LDS reads) and leaves the
+    // two partial counts, packed, in the histogram area (free by now)
+    constexpr int NWV = kTopkThreads / 64;
+    constexpr int CPW = (kTopkCand + NWV - 1) / NWV;
+    const int nc = sh.ncand;
+    const unsigned int kc = lane < nc ? sh.cand_key[lane] : 0u;
+    const int ic = lane < nc ? sh.cand_idx[lane] : 0;
+    int greater = 0, before = 0;
+#pragma unroll
+    for (int jj = 0; jj < CPW; ++jj) {
+      const int j = wave * CPW + jj;
+      if (j < nc) {  // uniform over the wave
+        const unsigned int kj = sh.cand_key[j];
+        const int ij = sh.cand_idx[j];
         greater += kj > kc ? 1 : 0;
         before += (kj == kc && ij < ic) ? 1 : 0;
       }
-      if (lane < nc && greater + before == remaining - 1) {
+    }
+    unsigned int* part = &sh.hist[0][0];  // [NWV][64]
+    part[wave * 64 + lane] = (unsigned int)greater | ((unsigned int)before << 16);
+    __syncthreads();
+    if (wave == 0 && lane < nc) {
+      unsigned int acc = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) acc += part[w * 64 + lane];
+      const int g = (int)(acc & 0xffffu), bf = (int)(acc >> 16);
+      if (g + bf == remaining - 1) {
         sh.theta = kc;
-        sh.need_eq = remaining - greater;
+        sh.need_eq = remaining - g;
       }
     }
   } else if (tid == 0) {
