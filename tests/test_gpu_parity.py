@@ -71,7 +71,9 @@ def _topk_case(rng, B, n_cap, tau):
 
 
 @pytest.mark.parametrize("tau", [0.02, 0.05, 0.1, 0.5, 1.0])
-@pytest.mark.parametrize("n_cap", [64, 6400, 16384, 70000])
+# row capacities for every keys-per-thread specialisation of the kernel:
+# 1, 2, 4, 8, 16 in registers, and re-read from memory
+@pytest.mark.parametrize("n_cap", [64, 2000, 4000, 6400, 16384, 70000])
 def test_topk_bit_exact(tau, n_cap):
     rng = np.random.default_rng(int(tau * 1000) + n_cap)
     B = 10
@@ -92,8 +94,6 @@ def test_topk_bit_exact(tau, n_cap):
         np.testing.assert_array_equal(idx[b, :k], want, err_msg=f"b={b} n={n} k={k}")
 
 
-# kept-token pass with several split workgroups per sequence (+ merge
-# launch), and with one split per sequence that writes the output directly
 # kept-token pass variants: split + merge with one state per workgroup (a
 # cross-wave combine) or one per wave, and one split per sequence (no merge)
 SPARSE_VARIANTS = pytest.mark.parametrize("rows", [("", "0"), ("", "1"), ("16384", "")],
