@@ -52,6 +52,9 @@ def parse():
                     help="budget of the CPU oracle baseline sample (0 disables it)")
     ap.add_argument("--profile-only", action="store_true",
                     help="skip the CPU baseline and the FULL comparison (for profiler runs)")
+    ap.add_argument("--scrub-mb", type=int, default=512,
+                    help="also time steps after a read pass over this many MiB that evicts the 256 MB "
+                         "MALL (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 256 MiB device-to-device copy, the reference kernel that "
                          "scales hardware byte counters")
@@ -215,10 +218,12 @@ def main():
     gen = DeviceGenerator(wl, st, device=dev)
     L, B, Hq, Hkv, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     w, W, K = wl.warmup_steps, args.warmup, args.steps
-    # decode steps used: warm-up, untimed pruned, timed (graph), timed (per-kernel events)
+    # decode steps used: warm-up, untimed pruned, timed (graph), timed (per-kernel
+    # events), timed again (graph replays after a MALL scrub)
     t_timed = w + W
     t_events = t_timed + K
-    n_steps = t_events + K
+    t_scrub = t_events + K
+    n_steps = t_scrub + (K if args.scrub_mb > 0 and not args.profile_only else 0)
     assert n_steps <= wl.steps, f"--steps/--warmup too large for {wl.steps} decode steps"
     io = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
@@ -271,6 +276,46 @@ def main():
             ev1.record(stream)
             torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / len(steps)
+
+    scrub = None
+    if args.scrub_mb > 0 and not args.profile_only:
+        scrub = torch.ones((args.scrub_mb << 20) // 8, dtype=torch.int64, device=dev)
+        scrub_out = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def time_steps_scrubbed(steps, graph):
+        """Mean time of single replays: every other one right after a read
+        pass over `scrub` (a reduction, which evicts the cache rows and
+        indices of the previous step from the MALL and leaves no dirty lines
+        to write back), the others right after a spin kernel as long as that
+        pass (the control: same launch, warm MALL).  The preceding kernel
+        keeps the GPU busy while the host enqueues the replay and lies
+        outside the timed interval."""
+        torch.sum(scrub, dim=0, out=scrub_out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(scrub, dim=0, out=scrub_out)
+        b.record()
+        torch.cuda.synchronize()
+        spin = int(cycles_per_ms * a.elapsed_time(b))
+        evs = {True: [], False: []}
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            for i, t in enumerate(steps):
+                q_stage.copy_(Qall[t])
+                lens_stage.copy_(lens_all[t])
+                scrubbed = i % 2 == 0
+                if scrubbed:
+                    torch.sum(scrub, dim=0, out=scrub_out)
+                else:
+                    torch.cuda._sleep(spin)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                graph.replay()
+                b.record(stream)
+                evs[scrubbed].append((a, b))
+            torch.cuda.synchronize()
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in evs.items()}
 
     def capture(h):
         g = torch.cuda.CUDAGraph()
@@ -355,10 +400,12 @@ def main():
         # step, so it runs at t_timed - 1's inputs into a scratch copy)
         g = capture(h) if not args.no_graph else None
         r["step_ms"] = time_steps(h, timed_steps, g)
-        del g
         # per-kernel timing + recorded outputs on the next K steps
         out_hist = torch.empty((K, L, B, Hq, d), dtype=io, device=dev)
-        r["kernels"], r["kernel_steps"] = kernel_times(h, list(range(t_events, n_steps)), out_hist)
+        r["kernels"], r["kernel_steps"] = kernel_times(h, list(range(t_events, t_scrub)), out_hist)
+        if g is not None and scrub is not None:
+            r["scrubbed_step_ms"] = time_steps_scrubbed(list(range(t_scrub, n_steps)), g)
+        del g
         outs[mode] = out_hist.float()
         fo.fastocr_destroy(h)
         results[mode] = r
@@ -375,7 +422,7 @@ def main():
         log(f"calibration copy of {CAL_BYTES >> 20} MiB done")
 
     focal = results["pruned"]["focal"]
-    ev_steps = list(range(t_events, n_steps))
+    ev_steps = list(range(t_events, t_scrub))
 
     # algorithmic K/V bytes (rows read x 2*Hkv*d*e)
     e = 2 if wl.dtype == "bf16" else 4
@@ -417,8 +464,21 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic(dom, wl.name), "avg_launch_us": round(dom_avg_ms * 1e3, 3),
                     "bytes_per_launch": int(per_launch_bytes)}
-    per_kernel = {k: {"avg_us": round(a * 1e3, 3), "launches_per_step": n, "us_per_step": round(a * n * 1e3, 3)}
-                  for k, (a, n) in kp.items()}
+    split_bytes = {"focal_split": R * rows_focal, "sparse_split": R * rows_sparse, "full_split": R * rows_focal}
+
+    def kernel_table(kr):
+        """Per kernel class: launch time, launches and time per step; for the
+        split kernels also the algorithmic K/V bytes per launch and the rate."""
+        tab = {}
+        for k, (a, n) in kr.items():
+            e = {"avg_us": round(a * 1e3, 3), "launches_per_step": n, "us_per_step": round(a * n * 1e3, 3)}
+            if k in split_bytes:
+                e["alg_bytes_per_launch"] = int(split_bytes[k])
+                e["GBps"] = round(split_bytes[k] / (a * 1e-3) / 1e9, 1)
+            tab[k] = e
+        return tab
+
+    per_kernel = kernel_table(kp)
     extra = {
         "focal_layers": focal,
         "kernel_sum_us_per_step": round(kernel_sum_ms * 1e3, 2),
@@ -436,6 +496,7 @@ def main():
             "full_kernel_sum_us_per_step": round(full_kernel_ms * 1e3, 2),
             "full_algorithmic_MB_per_step": round(bytes_full / 1e6, 2),
             "full_GBps_vs_step_time": round(bytes_full / (full_ms * 1e-3) / 1e9, 1),
+            "full_per_kernel": kernel_table(per_step(fr)),
             "speedup_vs_full": round(full_ms / pr_ms, 3),
             "speedup_vs_full_kernel_sum": round(full_kernel_ms / kernel_sum_ms, 3),
         })
@@ -448,6 +509,21 @@ def main():
             "rel_l2": round(float(diff.norm() / b[:, nf].norm()), 4)}
         fl = (a[:, focal] - b[:, focal]).abs().max()
         extra["deviation_focal_max_abs"] = float(fl)
+
+    if "scrubbed_step_ms" in results["pruned"]:
+        # single replays, each after a MALL scrub or after a spin of the same
+        # length (control)
+        sc = {"scrub_MiB": args.scrub_mb}
+        for mode in ("pruned", "full"):
+            if mode in results and "scrubbed_step_ms" in results[mode]:
+                v = results[mode]["scrubbed_step_ms"]
+                sc[f"{mode}_us_per_step"] = round(v[True] * 1e3, 2)
+                sc[f"{mode}_control_us_per_step"] = round(v[False] * 1e3, 2)
+        if "full_us_per_step" in sc:
+            sc["speedup_vs_full"] = round(sc["full_us_per_step"] / sc["pruned_us_per_step"], 3)
+        extra["mall_scrubbed"] = sc
+    if not args.profile_only:
+        extra["platform"] = platform_probe(torch, stream)
 
     cpu = None
     if args.cpu_seconds > 0 and not args.profile_only:
@@ -475,6 +551,52 @@ def main():
         **extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):
+    """Context for the kernel times: the per-launch floor of back-to-back
+    graph-replayed null kernels, and a device-to-device copy rate."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    try:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(launches):
+                torch.cuda._sleep(0)
+        best = None
+        with torch.cuda.stream(stream):
+            for _ in range(4):
+                a, b = ev(), ev()
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                t = a.elapsed_time(b)
+                best = t if best is None else min(best, t)
+        out["null_kernel_graph_us"] = round(best * 1e3 / launches, 3)
+        del g
+    except RuntimeError as exc:  # the spin kernel could not be captured
+        out["null_kernel_graph_us"] = None
+        log(f"null-kernel probe skipped: {exc}")
+    src = torch.ones(copy_bytes // 8, dtype=torch.int64, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    with torch.cuda.stream(stream):
+        for _ in range(4):
+            a, b = ev(), ev()
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+    out["copy_GBps"] = round(2 * copy_bytes / (best * 1e-3) / 1e9, 1)  # read + write
+    out["copy_MiB"] = copy_bytes >> 20
+    del src, dst
+    return out
 
 
 def cpu_baseline(wl, st, Kd, Vd, Qall, focal_gpu, budget_s):
