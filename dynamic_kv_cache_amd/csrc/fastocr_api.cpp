@@ -66,6 +66,7 @@ struct fastocr_handle {
   int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
   int full_sure = 0, sparse_sure = 0;  // splits that hold rows for any accepted sequence
   bool wave_states = false;            // kept-token splits write one state per wave
+  bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   int states_per_sparse_split = 1;
 
   float scale_log2 = 0.f;
@@ -357,6 +358,8 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
                    h->sparse_splits * kSplitWaves <= 64;
   h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1;
   h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
+  // k_b = n_b for every n_b exactly when tau = 1
+  h->keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
   // state slots per head (a direct kept-token pass writes none)
   h->max_splits = std::max(h->full_splits, h->sparse_splits * h->states_per_sparse_split);
   // Full passes: every sequence has at least min_img_tokens image rows and
@@ -452,6 +455,10 @@ int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* 
     case PHASE_PRUNED:
       if (h->is_focal[layer]) {
         rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores, true);
+      } else if (h->keeps_all) {
+        // tau = 1 keeps every image token: the kept set plus the text is the
+        // whole sequence, which the full pass reads without the gather
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
       } else {
         rc = run_sparse(h, q, k_cache, v_cache, lens, out);
       }

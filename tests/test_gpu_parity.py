@@ -148,12 +148,31 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
 
 @SPARSE_VARIANTS
 def test_tau_one_sparse_equals_full(monkeypatch, rows):
+    # the kept-token kernels themselves (by default tau = 1 runs the full pass)
     _sparse_variant(monkeypatch, rows)
+    monkeypatch.setenv("FASTOCR_KEPT_ALL_AS_FULL", "0")
     wl = get_workload("tiny-fp32").with_overrides(tau=1.0)
     up = upload(wl, steps=7)
     rec = run(up, fo.fastocr_create(make_config(up)), 7)
     full = run(up, fo.fastocr_create(make_config(up, mode="full")), 7)
     np.testing.assert_allclose(rec.outs, full.outs, rtol=0, atol=1e-5)
+
+
+def test_tau_one_non_focal_layers_take_full_pass(monkeypatch):
+    # tau = 1 keeps every image token, so non-focal layers run the full pass;
+    # the focal layers still select (every index, ascending)
+    monkeypatch.delenv("FASTOCR_KEPT_ALL_AS_FULL", raising=False)
+    wl = get_workload("tiny-fp32").with_overrides(tau=1.0)
+    up = upload(wl, steps=7)
+    rec = run(up, fo.fastocr_create(make_config(up)), 7)
+    full = run(up, fo.fastocr_create(make_config(up, mode="full")), 7)
+    np.testing.assert_allclose(rec.outs, full.outs, rtol=0, atol=1e-5)
+    assert rec.status == 0
+    n = int(up.st.n_img[0])
+    for t in range(wl.warmup_steps, 7):
+        for l in rec.focal:
+            assert rec.cnts[t, l + 1, 0] == n
+            np.testing.assert_array_equal(rec.sets[t, l + 1, 0, :n], np.arange(n))
 
 
 def test_lens_out_of_range_sets_flag():
