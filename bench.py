@@ -453,10 +453,10 @@ def main():
     # dominant kernel of the pruned step and its roofline
     dom = max(kp, key=lambda k: kp[k][0] * kp[k][1])
     dom_avg_ms = kp[dom][0]
-    per_launch_bytes = {
-        "focal_split": R * rows_focal,
-        "sparse_split": R * rows_sparse,
-    }.get(dom)
+    # algorithmic K/V bytes per launch of the split kernels (a non-focal
+    # layer at tau = 1 runs the full pass)
+    split_bytes = {"focal_split": R * rows_focal, "sparse_split": R * rows_sparse, "full_split": R * rows_focal}
+    per_launch_bytes = split_bytes.get(dom)
     roofline = None
     if per_launch_bytes is not None:
         achieved = per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9
@@ -464,8 +464,6 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic(dom, wl.name), "avg_launch_us": round(dom_avg_ms * 1e3, 3),
                     "bytes_per_launch": int(per_launch_bytes)}
-    split_bytes = {"focal_split": R * rows_focal, "sparse_split": R * rows_sparse, "full_split": R * rows_focal}
-
     def kernel_table(kr):
         """Per kernel class: launch time, launches and time per step; for the
         split kernels also the algorithmic K/V bytes per launch and the rate."""
