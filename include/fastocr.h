@@ -34,6 +34,19 @@
  *     handle is not thread-safe.
  *   - After FASTOCR_ERR_HIP the handle is poisoned: every later call except
  *     fastocr_destroy returns FASTOCR_ERR_STATE.
+ *
+ * Launch-plan overrides, read once by fastocr_create (for measurement and
+ * tests; results do not depend on them beyond rounding order):
+ *   FASTOCR_FULL_ROWS=R     rows per split of full passes (multiple of 16)
+ *   FASTOCR_SPARSE_ROWS=R   rows per split of kept-token passes; R at least the
+ *                           longest kept-token pass gives one split per
+ *                           sequence that writes the output (no merge)
+ *   FASTOCR_WAVE_STATES=0|1 kept-token splits write one merge state per wave
+ *                           (default: only for passes of at most one workgroup
+ *                           per CU)
+ *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
+ *                           pass (default 1) or the kept-token pass over
+ *                           every image token (0)
  */
 #ifndef FASTOCR_H
 #define FASTOCR_H
