@@ -64,6 +64,8 @@ class Info(ctypes.Structure):
         ("sparse_max_splits", c_int32),
         ("sparse_direct", c_int32),
         ("sparse_wave_states", c_int32),
+        ("sparse_pipe", c_int32),
+        ("reserved", c_int32),
         ("scratch_bytes", c_int64),
     ]
 

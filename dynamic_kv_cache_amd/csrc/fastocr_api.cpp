@@ -67,6 +67,7 @@ struct fastocr_handle {
   int full_sure = 0, sparse_sure = 0;  // splits that hold rows for any accepted sequence
   bool wave_states = false;            // kept-token splits write one state per wave
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
+  bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
   int states_per_sparse_split = 1;
 
   float scale_log2 = 0.f;
@@ -228,6 +229,7 @@ int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, c
   SplitParams sp = split_params(h, q, k, v, lens, out, true);
   sp.direct = h->sparse_splits <= 1 ? 1 : 0;
   sp.wave_states = h->wave_states ? 1 : 0;
+  sp.pipe = h->sparse_pipe ? 1 : 0;
   int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream, lt);
   });
@@ -345,9 +347,25 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
     sparse_rows = std::min(sparse_rows, h->k_max + c.max_seq_len - c.min_img_tokens);
   if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, h->k_max + c.max_text_tokens);
   // Kept-token passes: one round per split, the most workgroups, dispatched
-  // split-major (measured faster than fewer, longer splits at every batch).
-  h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
-                                    "FASTOCR_SPARSE_ROWS");
+  // split-major (measured faster than fewer, longer splits at every batch),
+  // or, pipelined, splits sized like a full pass's (whole rounds, about one
+  // wave of resident workgroups, at most kMaxPipeRows rows).
+  // Pipelined when the kept rows of all (sequence, KV head) pairs reach
+  // 64 x 2048: measured 2837 against 3104 us per step at 72B-like B=8,
+  // tau = 0.2 (2560 kept rows), but slower at tau <= 0.1 and at every
+  // smaller configuration.
+  const bool pipe_default = pairs * (int64_t)h->k_max >= 64 * 2048;
+  h->sparse_pipe = c.mode == FASTOCR_MODE_PRUNED && env_int("FASTOCR_SPARSE_PIPE", pipe_default ? 1 : 0) != 0;
+  if (h->sparse_pipe) {
+    h->sparse_R = std::min(plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE, true) * num_cu,
+                                               kMaxMergeSplits, "FASTOCR_SPARSE_ROWS"),
+                           kMaxPipeRows);
+    h->sparse_R = (int)align_up((size_t)h->sparse_R, kRowsPerRound);
+    if (h->sparse_R > kMaxPipeRows) h->sparse_R = kMaxPipeRows;
+  } else {
+    h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
+                                      "FASTOCR_SPARSE_ROWS");
+  }
   h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
   // A kept-token pass of at most one workgroup per CU is latency-bound: its
   // waves then write their states themselves (no cross-wave combine and
@@ -356,7 +374,8 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   // there the 4x partial-output traffic costs more than the combine.
   h->wave_states = h->sparse_splits > 1 && pairs * h->sparse_splits <= num_cu &&
                    h->sparse_splits * kSplitWaves <= 64;
-  h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1;
+  h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1 &&
+                   !h->sparse_pipe;
   h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
   // k_b = n_b for every n_b exactly when tau = 1
   h->keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
@@ -600,6 +619,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->sparse_rows_per_split = h->sparse_R;
   info->sparse_max_splits = h->sparse_splits;
   info->sparse_wave_states = h->wave_states ? 1 : 0;
+  info->sparse_pipe = h->sparse_pipe ? 1 : 0;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;

@@ -24,7 +24,11 @@ constexpr int kRowsPerRound = kTileRows * kSplitWaves * kTilesPerWave;
 constexpr int kSplitThreads = kSplitWaves * 64;
 // Resident split workgroups per CU the registers allow: full passes keep two
 // rounds of K/V in registers, kept-token passes one.
-constexpr int split_blocks_per_cu(int kind) { return kind == KIND_SPARSE ? 3 : 2; }
+// Resident workgroups per CU a split kernel is compiled for: one register
+// buffer (single-round kept-token splits) or two (pipelined passes).
+constexpr int split_blocks_per_cu(int kind, bool pipe = false) { return kind == KIND_SPARSE && !pipe ? 3 : 2; }
+// Longest split of a pipelined kept-token pass (its row map lives in LDS).
+constexpr int kMaxPipeRows = 2048;
 constexpr int kMergeThreads = 256;
 constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
 constexpr int kMaxHeads = 128;
@@ -52,6 +56,8 @@ struct SplitParams {
                           // otherwise every launched split writes its states (empty: max -inf)
   int32_t wave_states;    // kept-token pass, not direct: one state per wave instead of a
                           // cross-wave combine per workgroup
+  int32_t pipe;           // kept-token pass of multi-round splits (rows_per_split <=
+                          // kMaxPipeRows): row map in LDS, rounds double-buffered
   float scale_log2;       // logit scale * log2(e)
 };
 

@@ -525,8 +525,12 @@ __device__ __forceinline__ int split_count(int rows, int rows_per_split, int gri
   return nsplit;
 }
 
-template <typename T, int D, int KIND, int NW, int TPW>
-__global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn_kernel(SplitParams p) {
+// PIPE (kept-token kind only): the split's kept-row map is built once in LDS
+// (coalesced index loads), then the rounds run double-buffered like a full
+// pass, their cache rows read from LDS, so no vector index load stands
+// between one round's K/V loads and the next's.
+template <typename T, int D, int KIND, int NW, int TPW, bool PIPE = false>
+__global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
   constexpr int RPR = NW * TPW * kTileRows;     // rows per round
@@ -539,6 +543,9 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
 
   __shared__ float s_stat[NW][16][4];
   __shared__ float s_o[NW][HH][OST];
+  static_assert(!PIPE || KIND == KIND_SPARSE, "pipelined passes gather kept rows");
+  constexpr int PMAP = PIPE ? kMaxPipeRows : 1;
+  __shared__ int s_rowmap[PMAP];  // cache row of virtual row begin + i (PIPE)
 
   // Full passes: x = split, y = (sequence, KV head) pair, so workgroups
   // dispatched together stream neighbouring rows.  Kept-token passes:
@@ -583,7 +590,16 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   // Splits below sure_splits hold rows for every sequence the handle
   // accepts: they load ahead.  The others may be empty and learn that
   // from the extent before loading anything.
-  const bool ahead = split < p.sure_splits;
+  const bool ahead = !PIPE && split < p.sure_splits;
+  // pipelined kept-token pass: this thread's share of the split's kept
+  // indices (virtual rows begin + tid + i*NT), coalesced
+  constexpr int PI = PIPE ? kMaxPipeRows / NT : 1;
+  int jmap[PI];
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int i = 0; i < PI; ++i)
+      jmap[i] = tid + i * NT < p.rows_per_split ? selb[min(begin + tid + i * NT, p.k_stride - 1)] : 0;
+  }
   if (!ahead) {
   } else if constexpr (KIND == KIND_SPARSE) {
 #pragma unroll
@@ -643,6 +659,17 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
     const int jc = min(max(j, 0), max(n - 1, 0));
     return img ? jc : min(n + (r - kept), p.S - 1);
   };
+
+  if constexpr (PIPE) {
+    // the split's row map: cache row of virtual row begin + o (rows past
+    // the end map to row 0, inside the allocation; they carry no weight)
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      const int o = tid + i * NT;
+      if (o < p.rows_per_split) s_rowmap[o] = begin + o < end ? sparse_row(begin + o, jmap[i]) : 0;
+    }
+    __syncthreads();
+  }
 
   float m_run = -INFINITY, z = 0.f, lsum = 0.f, zt = 0.f;
   f32x4_t acc[NDB];
@@ -773,7 +800,11 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = r0 + u * NW * kTileRows;
-      if constexpr (KIND == KIND_SPARSE) {
+      if constexpr (PIPE) {
+        pk[u] = s_rowmap[tile + col - begin];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pvr[u][j] = s_rowmap[tile + 4 * grp + j - begin];
+      } else if constexpr (KIND == KIND_SPARSE) {
         pk[u] = sparse_row(tile + col, j_of(u, 0, tile + col));
 #pragma unroll
         for (int j = 0; j < 4; ++j) pvr[u][j] = sparse_row(tile + 4 * grp + j, j_of(u, 1 + j, tile + 4 * grp + j));
@@ -798,7 +829,7 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
   // starts at row (u*NW + w)*16, so neighbouring waves read neighbouring
   // tiles.  The first round's loads (full kinds) or indices (sparse kind)
   // are already in flight.
-  if constexpr (KIND == KIND_SPARSE) {
+  if constexpr (KIND == KIND_SPARSE && !PIPE) {
     // kept-token passes are short (one or two rounds per split): one
     // register buffer, higher occupancy
     if (r_first < end) {
@@ -813,8 +844,9 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND)) void split_attn
       round(r0, kw2, vw2);
     }
   } else if (r_first < end) {
-    // full passes: rounds alternate between two register buffers, the next
-    // round's loads are issued before the current round is computed
+    // full and pipelined kept-token passes: rounds alternate between two
+    // register buffers, the next round's loads are issued before the
+    // current round is computed
     if (!ahead) load_round(r_first, kw, vw, j_loaded);
     uint32_t kw2[TPW][KW];
     uint32_t vw2[TPW][4][VW];
@@ -1231,6 +1263,9 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
       return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, kTilesPerWave>, grid, block, stream,
                     timing, p);
     case KIND_SPARSE:
+      if (p.pipe)
+        return launch(split_attn_kernel<T, D, KIND_SPARSE, kSplitWaves, kTilesPerWave, true>, grid, block,
+                      stream, timing, p);
       return launch(split_attn_kernel<T, D, KIND_SPARSE, kSplitWaves, kTilesPerWave>, grid, block, stream,
                     timing, p);
   }

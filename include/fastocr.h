@@ -44,6 +44,9 @@
  *   FASTOCR_WAVE_STATES=0|1 kept-token splits write one merge state per wave
  *                           (default: only for passes of at most one workgroup
  *                           per CU)
+ *   FASTOCR_SPARSE_PIPE=0|1 kept-token passes of multi-round splits sized like
+ *                           a full pass's, the split's row map in LDS (default:
+ *                           when batch x num_kv_heads x k_max >= 131072)
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
@@ -122,6 +125,8 @@ typedef struct fastocr_info {
   int32_t sparse_max_splits;
   int32_t sparse_direct;  /* 1: non-focal layers finish in one split (no merge launch) */
   int32_t sparse_wave_states; /* 1: kept-token splits write one merge state per wave */
+  int32_t sparse_pipe;    /* 1: kept-token passes run pipelined multi-round splits */
+  int32_t reserved;
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     # double first, then a float and thirteen int32 -> 64 bytes, no padding
     assert ctypes.sizeof(_abi.Config) == 64
-    assert ctypes.sizeof(_abi.Info) == 48
+    assert ctypes.sizeof(_abi.Info) == 56
     assert ctypes.sizeof(_abi.Timing) == 3 * 8 * _abi.KC_COUNT
 
 

@@ -95,14 +95,17 @@ def test_topk_bit_exact(tau, n_cap):
 
 
 # kept-token pass variants: split + merge with one state per workgroup (a
-# cross-wave combine) or one per wave, and one split per sequence (no merge)
-SPARSE_VARIANTS = pytest.mark.parametrize("rows", [("", "0"), ("", "1"), ("16384", "")],
-                                          ids=["split-merge", "wave-states", "direct"])
+# cross-wave combine) or one per wave, one split per sequence (no merge), and
+# pipelined multi-round splits (row map in LDS) with and without a merge
+SPARSE_VARIANTS = pytest.mark.parametrize(
+    "rows", [("", "0", "0"), ("", "1", "0"), ("16384", "", "0"), ("384", "0", "1"), ("16384", "", "1")],
+    ids=["split-merge", "wave-states", "direct", "pipelined", "pipelined-direct"])
 
 
 def _sparse_variant(monkeypatch, rows):
     monkeypatch.setenv("FASTOCR_SPARSE_ROWS", rows[0])
     monkeypatch.setenv("FASTOCR_WAVE_STATES", rows[1])
+    monkeypatch.setenv("FASTOCR_SPARSE_PIPE", rows[2])
 
 
 @SPARSE_VARIANTS
@@ -114,8 +117,10 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
                 steps=3)
     h = fo.fastocr_create(make_config(up))
     info = fo.fastocr_get_info(h)
-    assert info["sparse_direct"] == (1 if rows[0] else 0)
+    if rows[2] != "1":  # a pipelined split holds at most 2048 rows
+        assert info["sparse_direct"] == (1 if rows[0] == "16384" else 0)
     assert info["sparse_wave_states"] == (1 if rows[1] == "1" else 0)
+    assert info["sparse_pipe"] == (1 if rows[2] == "1" else 0)
     wl = up.wl
     for l in range(wl.num_layers):  # one warm-up step
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
