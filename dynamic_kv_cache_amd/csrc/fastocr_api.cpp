@@ -338,8 +338,22 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
 
   const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
   // about one wave of resident split workgroups per launch
-  h->full_R = plan_rows_per_split(pairs, c.max_seq_len, split_blocks_per_cu(KIND_FULL) * num_cu,
-                                  kMaxMergeSplits, "FASTOCR_FULL_ROWS");
+  // A ragged batch (image counts between min_img_tokens and max_img_tokens)
+  // is planned for the middle of that range, not for the longest sequence,
+  // whose plan would leave most splits of the shorter sequences empty and
+  // fill few CUs; each pair's last split is partly empty, so the plan keeps
+  // half a workgroup per pair of the resident slots free (a launch just
+  // over the slots runs a second wave).  7B-like B=16, 2169-6682 image
+  // tokens, full step: 768-row splits (440 workgroups with rows) 1067 us,
+  // 640 (516) 1247, 1024 (336) 1178, 1152 (304) 1224.
+  int full_rows_est = c.max_seq_len;
+  int full_target = split_blocks_per_cu(KIND_FULL) * num_cu;
+  if (c.min_img_tokens > 0 && c.min_img_tokens < c.max_img_tokens) {
+    full_rows_est = (c.min_img_tokens + c.max_img_tokens) / 2 + (c.max_seq_len - c.max_img_tokens);
+    full_target = (int)std::max<int64_t>(full_target - pairs / 2, full_target / 2);
+  }
+  h->full_R = plan_rows_per_split(pairs, full_rows_est, full_target, kMaxMergeSplits, "FASTOCR_FULL_ROWS");
+  while ((c.max_seq_len + h->full_R - 1) / h->full_R > kMaxMergeSplits) h->full_R += kRowsPerRound;
   h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
   // rows of a kept-token pass: kept image rows + text rows
   int sparse_rows = c.max_seq_len;
