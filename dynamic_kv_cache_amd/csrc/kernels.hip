@@ -1142,6 +1142,7 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
 // head), so it does not depend on the merge workgroups.  The token's logits
 // of up to kScoreRegHeads heads are loaded before anything else.
 constexpr int kScoreRegHeads = 32;
+constexpr int kScorePrefetchPasses = 4;  // heads whose split states load up front: 4 x 16
 
 __device__ void score_block(const MergeParams& p, int b, int sb) {
   __shared__ float2 s_mz[kMaxHeads];
@@ -1159,28 +1160,36 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
 #pragma unroll
   for (int h = 0; h < kScoreRegHeads; ++h) x[h] = h < p.Hq ? lg[(size_t)h * p.n_stride] : 0.f;
 
+  // Every head's softmax max and 1/sum from the split states, 16 lanes per
+  // head and 16 heads per pass; the states of the first kScorePrefetchPasses
+  // passes are loaded before any is reduced.
   const int nsplit = p.grid_splits;
   const int hl = tid & 15;
-  for (int h0 = 0; h0 < p.Hq; h0 += kMergeThreads / 16) {
-    const int h = h0 + (tid >> 4);
-    const bool hv = h < p.Hq;
-    const float4* ps = p.pstat + ((size_t)b * p.Hq + (hv ? h : 0)) * p.max_splits;
-    float4 st[4];
+  constexpr int HPP = kMergeThreads / 16;
+  float4 st[kScorePrefetchPasses][4];
+#pragma unroll
+  for (int pass = 0; pass < kScorePrefetchPasses; ++pass) {
+    const int h = pass * HPP + (tid >> 4);
+    const float4* ps = p.pstat + ((size_t)b * p.Hq + min(h, p.Hq - 1)) * p.max_splits;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = hl + 16 * i;
-      st[i] = (hv && s < nsplit) ? ps[s] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      st[pass][i] = (h < p.Hq && s < nsplit) ? ps[s] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
     }
+  }
+  auto head_totals = [&](int h, const float4 (&sv)[4]) {
+    const bool hv = h < p.Hq;
+    const float4* ps = p.pstat + ((size_t)b * p.Hq + (hv ? h : 0)) * p.max_splits;
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, st[i].x);
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, sv[i].x);
     if (hv)
       for (int s = hl + 64; s < nsplit; s += 16) m = fmaxf(m, ps[s].x);
     m = row_max16(m);
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (hl + 16 * i < nsplit && st[i].x != -INFINITY) z += st[i].y * __builtin_amdgcn_exp2f(st[i].x - m);
+      if (hl + 16 * i < nsplit && sv[i].x != -INFINITY) z += sv[i].y * __builtin_amdgcn_exp2f(sv[i].x - m);
     if (hv)
       for (int s = hl + 64; s < nsplit; s += 16) {
         const float4 q = ps[s];
@@ -1188,15 +1197,30 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
       }
     z = group_sum<16>(z);
     if (hv && hl == 0) s_mz[h] = make_float2(m, 1.f / z);
+  };
+#pragma unroll
+  for (int pass = 0; pass < kScorePrefetchPasses; ++pass)
+    if (pass * HPP < p.Hq) head_totals(pass * HPP + (tid >> 4), st[pass]);
+  for (int h0 = kScorePrefetchPasses * HPP; h0 < p.Hq; h0 += HPP) {
+    const int h = h0 + (tid >> 4);
+    const float4* ps = p.pstat + ((size_t)b * p.Hq + min(h, p.Hq - 1)) * p.max_splits;
+    float4 sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = hl + 16 * i;
+      sv[i] = (h < p.Hq && s < nsplit) ? ps[s] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    }
+    head_totals(h, sv);
   }
+  // heads past Hq up to the register heads add exactly 0 (logit 0, weight 0)
+  if (tid >= p.Hq && tid < kScoreRegHeads) s_mz[tid] = make_float2(0.f, 0.f);
   __syncthreads();
   // tokens past this sequence's image tokens get scores too (from stale
   // logits); nothing reads them
   float s = 0.f;
   if (j < p.n_stride) {
 #pragma unroll
-    for (int h = 0; h < kScoreRegHeads; ++h)
-      if (h < p.Hq) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
+    for (int h = 0; h < kScoreRegHeads; ++h) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
     for (int h = kScoreRegHeads; h < p.Hq; ++h)
       s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
     p.scores[(size_t)b * p.n_stride + j] = s;
