@@ -1004,10 +1004,12 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     st[i] = s < p.grid_splits ? p.pstat[slot0 + s] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 pv[PF];
+  float mxs[PF];  // maxima of the splits this thread accumulates
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int s = sl + i * SL;
     pv[i] = s < p.grid_splits ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    mxs[i] = s < p.grid_splits ? p.pstat[slot0 + s].x : -INFINITY;
   }
   // up to 64 splits: lane s of every wave holds split s's state
   const float4 q = (p.grid_splits <= 64 && lane < p.grid_splits) ? p.pstat[slot0 + lane]
@@ -1029,17 +1031,20 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     const float Z = wave_sum(q.y * w);
     const float L = wave_sum(q.z * w);
     const float Zt = wave_sum(q.w * w);
+    // the weights of this thread's splits, from their own maxima (no lane
+    // exchange), then branch-free sums: a state of weight 0 adds exactly 0
+    // whatever its partial output holds
+    float wsv[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) wsv[i] = mxs[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mxs[i] - M);
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int s = sl + i * SL;
-      const float ws = __shfl(w, s & 63);
-      if (s < nsplit && ws != 0.f) {
-        a0 += pv[i].x * ws;
-        a1 += pv[i].y * ws;
-        a2 += pv[i].z * ws;
-        a3 += pv[i].w * ws;
-      }
+      const bool use = sl + i * SL < nsplit && wsv[i] != 0.f;
+      a0 += use ? pv[i].x * wsv[i] : 0.f;
+      a1 += use ? pv[i].y * wsv[i] : 0.f;
+      a2 += use ? pv[i].z * wsv[i] : 0.f;
+      a3 += use ? pv[i].w * wsv[i] : 0.f;
     }
     a0 = group_sum<SL>(a0);
     a1 = group_sum<SL>(a1);
