@@ -267,6 +267,24 @@ def test_trajectory_ragged_small(monkeypatch, rows):
     log(f"[ragged] n={up.st.n_img.tolist()} focal {rec.focal}, worst out {chk.worst_out:.2e}")
 
 
+@SPARSE_VARIANTS
+def test_trajectory_tiny_images(monkeypatch, rows):
+    # sequences with 1-40 image tokens (k = 1 or 2) beside longer prompts:
+    # kept-token passes that are mostly text, empty high splits
+    _sparse_variant(monkeypatch, rows)
+    wl = get_workload("7b-b16-ragged").with_overrides(
+        batch=5, num_layers=4, focal_band=(1, 2), num_focal=1, warmup_steps=2,
+        n_img_range=(1, 40), n_prompt=(1, 90))
+    up = upload(wl, steps=7)
+    rec = run(up, fo.fastocr_create(make_config(up)), 7)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 7):
+        chk.pruned_step(t)
+    log(f"[tiny images] n={up.st.n_img.tolist()} focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
 @pytest.mark.parametrize("name,dtype,head_dim,steps", [
     ("tiny-fp32", "bf16", 64, None),    # bf16 kernels at d = 64
     ("tiny-fp32", "f32", 128, None),    # fp32 kernels at d = 128
