@@ -151,6 +151,24 @@ def fastocr_attend(h: Handle, layer: int, q, k_cache, v_cache, lens, out) -> Non
     _check("fastocr_attend", lib().fastocr_attend(h.ptr, int(layer), *args))
 
 
+def fastocr_attend_append(h: Handle, layer: int, q, k_new, v_new, k_cache, v_cache, lens, out) -> None:
+    c = h.cfg
+    t = _torch()
+    qs = (c.batch, c.num_q_heads, c.head_dim)
+    ns = (c.batch, c.num_kv_heads, c.head_dim)
+    ks = (c.batch, c.num_kv_heads, c.max_seq_len, c.head_dim)
+    args = (
+        _dev_ptr(q, h.io_dtype, qs, "q"),
+        _dev_ptr(k_new, h.io_dtype, ns, "k_new"),
+        _dev_ptr(v_new, h.io_dtype, ns, "v_new"),
+        _dev_ptr(k_cache, h.io_dtype, ks, "k_cache"),
+        _dev_ptr(v_cache, h.io_dtype, ks, "v_cache"),
+        _dev_ptr(lens, t.int32, (c.batch, 2), "lens", 4),
+        _dev_ptr(out, h.io_dtype, qs, "out"),
+    )
+    _check("fastocr_attend_append", lib().fastocr_attend_append(h.ptr, int(layer), *args))
+
+
 def fastocr_profile_warmup(h: Handle) -> List[int]:
     arr = (ctypes.c_int32 * h.cfg.num_focal)()
     _check("fastocr_profile_warmup", lib().fastocr_profile_warmup(h.ptr, arr))

@@ -81,6 +81,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfastocr.
 SIGNATURES = [
     ("fastocr_create", c_int32, [ctypes.POINTER(Config), c_void_p, ctypes.POINTER(c_void_p)]),
     ("fastocr_attend", c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    ("fastocr_attend_append", c_int32,
+     [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     ("fastocr_profile_warmup", c_int32, [c_void_p, ctypes.POINTER(c_int32)]),
     ("fastocr_destroy", c_int32, [c_void_p]),
     ("fastocr_get_status", c_int32, [c_void_p, ctypes.POINTER(c_int32)]),

@@ -68,6 +68,8 @@ struct fastocr_handle {
   bool wave_states = false;            // kept-token splits write one state per wave
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
+  const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
+  const void* app_v = nullptr;
   int states_per_sparse_split = 1;
 
   float scale_log2 = 0.f;
@@ -134,6 +136,12 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   p.q = q;
   p.k = k;
   p.v = v;
+  if (h->app_k) {  // fastocr_attend_append: the caches are the caller's writable buffers
+    p.k_new = h->app_k;
+    p.v_new = h->app_v;
+    p.k_w = const_cast<void*>(k);
+    p.v_w = const_cast<void*>(v);
+  }
   p.lens = lens;
   p.sel = h->sel;
   p.sel_cnt = h->sel_cnt;
@@ -456,9 +464,9 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   return FASTOCR_OK;
 }
 
-int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
-                   const void* v_cache, const int32_t* lens, void* out) {
-  if (!h) return FASTOCR_ERR_INVALID_ARG;
+// One layer of the current step (fastocr_attend, fastocr_attend_append).
+static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* lens, void* out) {
   if (h->poisoned) return FASTOCR_ERR_STATE;
   if (!q || !k_cache || !v_cache || !lens || !out) return FASTOCR_ERR_INVALID_ARG;
   const fastocr_config& c = h->cfg;
@@ -506,6 +514,25 @@ int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* 
     if (h->phase == PHASE_WARMUP && h->step == c.warmup_steps) h->phase = PHASE_WARMUP_DONE;
   }
   return FASTOCR_OK;
+}
+
+int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* lens, void* out) {
+  if (!h) return FASTOCR_ERR_INVALID_ARG;
+  h->app_k = h->app_v = nullptr;
+  return attend_impl(h, layer, q, k_cache, v_cache, lens, out);
+}
+
+int fastocr_attend_append(fastocr_handle* h, int32_t layer, const void* q, const void* k_new,
+                          const void* v_new, void* k_cache, void* v_cache, const int32_t* lens,
+                          void* out) {
+  if (!h) return FASTOCR_ERR_INVALID_ARG;
+  if (!k_new || !v_new) return FASTOCR_ERR_INVALID_ARG;
+  h->app_k = k_new;
+  h->app_v = v_new;
+  const int rc = attend_impl(h, layer, q, k_cache, v_cache, lens, out);
+  h->app_k = h->app_v = nullptr;
+  return rc;
 }
 
 int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out) {

@@ -56,6 +56,10 @@ struct SplitParams {
                           // otherwise every launched split writes its states (empty: max -inf)
   int32_t wave_states;    // kept-token pass, not direct: one state per wave instead of a
                           // cross-wave combine per workgroup
+  const void* k_new;      // [B, Hkv, D] the current token's key and value, or null: when
+  const void* v_new;      // set, cache row len-1 is read from here and written into the
+  void* k_w;              // caches (k_w, v_w: the same buffers as k, v) by each pair's
+  void* v_w;              // split 0
   int32_t pipe;           // kept-token pass of multi-round splits (rows_per_split <=
                           // kMaxPipeRows): row map in LDS, rounds double-buffered
   float scale_log2;       // logit scale * log2(e)

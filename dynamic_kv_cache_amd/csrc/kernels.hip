@@ -626,6 +626,37 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
   int n, len;
   const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
   const bool reporter = split == 0 && kvh == 0 && tid == 0;
+
+  // Fused append: the current token (cache row len - 1) comes from k_new /
+  // v_new in every load of this launch, and split 0 of the pair writes it
+  // into the caches for later steps (no workgroup of this launch reads that
+  // cache row).
+  const int cur = len - 1;
+  const bool app = p.k_new != nullptr && len > 0;
+  const T* __restrict__ knew = app ? reinterpret_cast<const T*>(p.k_new) + ((size_t)b * p.Hkv + kvh) * D : nullptr;
+  const T* __restrict__ vnew = app ? reinterpret_cast<const T*>(p.v_new) + ((size_t)b * p.Hkv + kvh) * D : nullptr;
+  if (app && split == 0) {
+    constexpr int C16 = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    T* kc = reinterpret_cast<T*>(p.k_w) + (row_base + cur) * D;
+    T* vc = reinterpret_cast<T*>(p.v_w) + (row_base + cur) * D;
+    if (tid < C16) reinterpret_cast<uint4*>(kc)[tid] = reinterpret_cast<const uint4*>(knew)[tid];
+    else if (tid < 2 * C16) reinterpret_cast<uint4*>(vc)[tid - C16] = reinterpret_cast<const uint4*>(vnew)[tid - C16];
+  }
+  if (KIND != KIND_SPARSE && app && ahead) {
+    // a full pass loaded this wave's first-round rows before the extent was
+    // known: the current token's row, if among them, is reloaded from
+    // k_new / v_new
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = r_first + u * NW * kTileRows;
+      if (tile <= cur && cur < tile + kTileRows) {  // uniform over the wave
+        if (tile + col == cur) load_slice<T, KW>(kw[u], knew, grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (tile + 4 * grp + j == cur) load_words(vw[u][j], vnew + col * NDB, VW);
+      }
+    }
+  }
   if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
   const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
   const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
@@ -817,9 +848,10 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (r0 + u * NW * kTileRows < end) {  // uniform over the wave
-        load_slice<T, KW>(kw[u], Kb + (size_t)pk[u] * D, grp);
+        load_slice<T, KW>(kw[u], app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D, grp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) load_words(vw[u][j], Vb + (size_t)pvr[u][j] * D + col * NDB, VW);
+        for (int j = 0; j < 4; ++j)
+          load_words(vw[u][j], (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB, VW);
       }
     }
   };

@@ -175,6 +175,24 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
 int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* lens, void* out);
 
+/* fastocr_attend_append: fastocr_attend with the current token's key/value
+ * appended by the same launches instead of by a separate kernel before the
+ * call (the decode step appends the new token before attending: Method).
+ *   k_new, v_new  device [B, Hkv, d] of dtype: the current token's key and
+ *            value.  They are written into k_cache / v_cache at row len_b - 1
+ *            (len_b after clamping; nothing for len_b = 0), and that row's
+ *            attention uses them, so the row's previous content never
+ *            matters.  The caches must be writable device memory; no other
+ *            row is written.
+ * Everything else, including outputs and the state machine, is exactly
+ * fastocr_attend's: the results equal those of writing the row first and
+ * calling fastocr_attend (same operations in the same order).  The cache
+ * row is visible to later work on the handle's stream.  Errors: as
+ * fastocr_attend, and INVALID_ARG for null k_new / v_new. */
+int fastocr_attend_append(fastocr_handle* h, int32_t layer, const void* q, const void* k_new,
+                          const void* v_new, void* k_cache, void* v_cache, const int32_t* lens,
+                          void* out);
+
 /* fastocr_profile_warmup: after exactly w completed warm-up steps, pick the
  * focal layers (Focal Layer Selection): the |C| layers with the largest mean
  * image-attention mass over heads, sequences and warm-up steps (ties to the

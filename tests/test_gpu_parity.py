@@ -350,3 +350,55 @@ def test_trajectory_7b_all_steps(traj_7b, chunk):
         chk.pruned_step(t)
     log(f"[7b] steps {edges[chunk]}..{edges[chunk + 1] - 1} ok; worst out {chk.worst_out:.3e}, "
         f"mean Jaccard {np.mean(chk.jaccard):.3f}")
+
+
+APPEND_CASES = {
+    "tiny-full": ("tiny-fp32", dict(), "full", 6, {}),
+    "tiny-pruned": ("tiny-fp32", dict(), "pruned", 7, {}),
+    "7b-pruned": ("7b-b1", dict(num_layers=3, warmup_steps=1, num_focal=1), "pruned", 4, {}),
+    "ragged-pipelined": ("7b-b16-ragged", dict(batch=4, num_layers=4, focal_band=(1, 2), num_focal=1,
+                                               warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
+                         "pruned", 5, {"FASTOCR_SPARSE_PIPE": "1", "FASTOCR_SPARSE_ROWS": "384"}),
+    "ragged-wave-states": ("7b-b16-ragged", dict(batch=2, num_layers=4, focal_band=(1, 2), num_focal=1,
+                                                 warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
+                           "pruned", 5, {"FASTOCR_WAVE_STATES": "1"}),
+}
+
+
+@pytest.mark.parametrize("case", list(APPEND_CASES))
+def test_attend_append_equals_prewritten_row(monkeypatch, case):
+    # the current token's K/V given to fastocr_attend_append (its cache row
+    # holding NaN before the call) gives the outputs of fastocr_attend on a
+    # cache that already holds the row, bit for bit, and writes the row
+    name, over, mode, steps, env = APPEND_CASES[case]
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = get_workload(name).with_overrides(**over)
+    up = upload(wl, steps=steps)
+    L, B, Hq, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim
+    ha = fo.fastocr_create(make_config(up, mode=mode))
+    hb = fo.fastocr_create(make_config(up, mode=mode))
+    kb = [k.clone() for k in up.Kd]
+    vb = [v.clone() for v in up.Vd]
+    out_a = torch.empty((B, Hq, d), dtype=up.io_dtype, device=DEV)
+    out_b = torch.empty_like(out_a)
+    for t in range(steps):
+        if mode == "pruned" and t == wl.warmup_steps:
+            assert fo.fastocr_profile_warmup(ha) == fo.fastocr_profile_warmup(hb)
+        cur = up.st.lens(t)[:, 1] - 1
+        for l in range(L):
+            bi = torch.arange(B, device=DEV)
+            ci = torch.from_numpy(cur.astype(np.int64)).to(DEV)
+            k_new = up.Kd[l][bi, :, ci].contiguous()  # [B, Hkv, d]
+            v_new = up.Vd[l][bi, :, ci].contiguous()
+            kb[l][bi, :, ci] = float("nan")
+            vb[l][bi, :, ci] = float("nan")
+            fo.fastocr_attend(ha, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out_a)
+            fo.fastocr_attend_append(hb, l, up.Qd[l][t], k_new, v_new, kb[l], vb[l], up.lens[t], out_b)
+            torch.cuda.synchronize()
+            assert torch.equal(out_a, out_b), f"step {t} layer {l}"
+    for l in range(L):
+        assert torch.equal(kb[l], up.Kd[l]) and torch.equal(vb[l], up.Vd[l]), f"layer {l} cache"
+    assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
+    fo.fastocr_destroy(ha)
+    fo.fastocr_destroy(hb)
