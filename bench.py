@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--scrub-mb", type=int, default=512,
                     help="also time steps after a read pass over this many MiB that evicts the 256 MB "
                          "MALL (0 disables it)")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the comparison of a separate K/V append kernel with fastocr_attend_append")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 256 MiB device-to-device copy, the reference kernel that "
                          "scales hardware byte counters")
@@ -223,7 +225,9 @@ def main():
     t_timed = w + W
     t_events = t_timed + K
     t_scrub = t_events + K
-    n_steps = t_scrub + (K if args.scrub_mb > 0 and not args.profile_only else 0)
+    t_append = t_scrub + (K if args.scrub_mb > 0 and not args.profile_only else 0)
+    do_append = not args.no_append and not args.profile_only and not args.no_graph
+    n_steps = t_append + (2 * K if do_append else 0)
     assert n_steps <= wl.steps, f"--steps/--warmup too large for {wl.steps} decode steps"
     io = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
@@ -317,6 +321,58 @@ def main():
             torch.cuda.synchronize()
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in evs.items()}
 
+    # the current token's K/V of every layer at the append-timing steps (the
+    # cache already holds them: the appends rewrite the same values)
+    if do_append:
+        app_steps = list(range(t_append, n_steps))
+        bi = torch.arange(B, device=dev)
+        cur_all = (lens_all[app_steps, :, 1] - 1).long()  # [S, B]
+        kn_all = torch.stack([torch.stack([Kd[l][bi, :, cur_all[i]] for l in range(L)]) for i in range(len(app_steps))])
+        vn_all = torch.stack([torch.stack([Vd[l][bi, :, cur_all[i]] for l in range(L)]) for i in range(len(app_steps))])
+        kn_stage = torch.empty_like(kn_all[0])  # [L, B, Hkv, d]
+        vn_stage = torch.empty_like(vn_all[0])
+
+    def capture_append(h, fused):
+        """One step with the current token's K/V appended: by an indexed copy
+        kernel per layer before fastocr_attend, or by fastocr_attend_append."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            q_stage.copy_(Qall[app_steps[0]])
+            lens_stage.copy_(lens_all[app_steps[0]])
+            kn_stage.copy_(kn_all[0])
+            vn_stage.copy_(vn_all[0])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            if not fused:
+                ci = (lens_stage[:, 1] - 1).long()
+            for l in range(L):
+                if fused:
+                    fo.fastocr_attend_append(h, l, q_stage[l], kn_stage[l], vn_stage[l], Kd[l], Vd[l],
+                                             lens_stage, out_stage[l])
+                else:
+                    Kd[l][bi, :, ci] = kn_stage[l]
+                    Vd[l][bi, :, ci] = vn_stage[l]
+                    fo.fastocr_attend(h, l, q_stage[l], Kd[l], Vd[l], lens_stage, out_stage[l])
+        torch.cuda.synchronize()
+        return g
+
+    def time_append(h, steps, idx0, fused):
+        g = capture_append(h, fused)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i, t in enumerate(steps):
+                q_stage.copy_(Qall[t])
+                lens_stage.copy_(lens_all[t])
+                kn_stage.copy_(kn_all[idx0 + i])
+                vn_stage.copy_(vn_all[idx0 + i])
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / len(steps)
+
     def capture(h):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
@@ -404,8 +460,13 @@ def main():
         out_hist = torch.empty((K, L, B, Hq, d), dtype=io, device=dev)
         r["kernels"], r["kernel_steps"] = kernel_times(h, list(range(t_events, t_scrub)), out_hist)
         if g is not None and scrub is not None:
-            r["scrubbed_step_ms"] = time_steps_scrubbed(list(range(t_scrub, n_steps)), g)
+            r["scrubbed_step_ms"] = time_steps_scrubbed(list(range(t_scrub, t_append)), g)
         del g
+        if do_append:
+            # each capture advances the kept set by one step, so the two
+            # variants run on consecutive step ranges
+            r["append_separate_ms"] = time_append(h, list(range(t_append, t_append + K)), 0, False)
+            r["append_fused_ms"] = time_append(h, list(range(t_append + K, n_steps)), K, True)
         outs[mode] = out_hist.float()
         fo.fastocr_destroy(h)
         results[mode] = r
@@ -520,6 +581,13 @@ def main():
         if "full_us_per_step" in sc:
             sc["speedup_vs_full"] = round(sc["full_us_per_step"] / sc["pruned_us_per_step"], 3)
         extra["mall_scrubbed"] = sc
+    if "append_fused_ms" in results["pruned"]:
+        ap = {}
+        for mode in ("pruned", "full"):
+            if mode in results and "append_fused_ms" in results[mode]:
+                ap[f"{mode}_separate_append_us_per_step"] = round(results[mode]["append_separate_ms"] * 1e3, 2)
+                ap[f"{mode}_fused_append_us_per_step"] = round(results[mode]["append_fused_ms"] * 1e3, 2)
+        extra["append"] = ap
     if not args.profile_only:
         extra["platform"] = platform_probe(torch, stream)
 
