@@ -220,25 +220,34 @@ def main():
     gen = DeviceGenerator(wl, st, device=dev)
     L, B, Hq, Hkv, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     w, W, K = wl.warmup_steps, args.warmup, args.steps
-    # decode steps used: warm-up, untimed pruned, timed (graph), timed (per-kernel
-    # events), timed again (graph replays after a MALL scrub)
-    t_timed = w + W
-    t_events = t_timed + K
-    t_scrub = t_events + K
-    t_append = t_scrub + (K if args.scrub_mb > 0 and not args.profile_only else 0)
+    # Decode steps used: the w warm-up steps and W untimed pruned steps run
+    # in order; then each timing phase (graph replays, per-kernel events,
+    # replays after a MALL scrub, the two append variants) runs K steps
+    # spread over the rest of the trajectory [w + W, T), the phases
+    # interleaved, so every phase sees short and long text alike.
+    do_scrub = args.scrub_mb > 0 and not args.profile_only and not args.no_graph
     do_append = not args.no_append and not args.profile_only and not args.no_graph
-    n_steps = t_append + (2 * K if do_append else 0)
-    assert n_steps <= wl.steps, f"--steps/--warmup too large for {wl.steps} decode steps"
+    phases = ["graph", "events"] + (["scrub"] if do_scrub else []) + (
+        ["append_separate", "append_fused"] if do_append else [])
+    t_timed = w + W
+    assert t_timed < wl.steps, f"--warmup too large for {wl.steps} decode steps"
+    span, n_log = wl.steps - t_timed, len(phases) * K
+    phase_steps = {ph: [t_timed + ((k * len(phases) + i) * span) // n_log for k in range(K)]
+                   for i, ph in enumerate(phases)}
+    used = sorted(set(range(t_timed)).union(*phase_steps.values()))
+    slot = {t: i for i, t in enumerate(used)}
     io = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
     t0 = time.time()
-    Kd, Vd, Qall = [], [], torch.empty((n_steps, L, B, Hq, d), dtype=io, device=dev)
+    Kd, Vd, Qall = [], [], torch.empty((len(used), L, B, Hq, d), dtype=io, device=dev)
     for l in range(L):
         k, v = gen.layer_kv(l)
         Kd.append(k)
         Vd.append(v)
-        Qall[:, l] = gen.layer_queries(l, range(n_steps), k)
-    lens_all = torch.from_numpy(np.stack([st.lens(t) for t in range(n_steps)])).to(dev)
+        Qall[:, l] = gen.layer_queries(l, used, k)
+    lens_all = torch.from_numpy(np.stack([st.lens(t) for t in used])).to(dev)
+    q_at = lambda t: Qall[slot[t]]  # noqa: E731  [L, B, Hq, d] of decode step t
+    lens_at = lambda t: lens_all[slot[t]]  # noqa: E731
     torch.cuda.synchronize()
     log(f"inputs for {wl.name} ready in {time.time() - t0:.1f}s "
         f"(KV {2 * L * B * Hkv * st.max_seq_len * d * Kd[0].element_size() / 1e9:.2f} GB)")
@@ -259,21 +268,21 @@ def main():
 
     def eager_step(h, t, out):
         for l in range(L):
-            fo.fastocr_attend(h, l, Qall[t, l], Kd[l], Vd[l], lens_all[t], out[l])
+            fo.fastocr_attend(h, l, q_at(t)[l], Kd[l], Vd[l], lens_at(t), out[l])
 
     def time_steps(h, steps, graph):
         """Wall time per step over `steps` (HIP events on the library stream)."""
         with torch.cuda.stream(stream):
             if graph is not None:
-                q_stage.copy_(Qall[steps[0]])
-                lens_stage.copy_(lens_all[steps[0]])
+                q_stage.copy_(q_at(steps[0]))
+                lens_stage.copy_(lens_at(steps[0]))
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             ev0.record(stream)
             for t in steps:
                 if graph is not None:
-                    q_stage.copy_(Qall[t])
-                    lens_stage.copy_(lens_all[t])
+                    q_stage.copy_(q_at(t))
+                    lens_stage.copy_(lens_at(t))
                     graph.replay()
                 else:
                     eager_step(h, t, out_stage)
@@ -282,7 +291,7 @@ def main():
         return ev0.elapsed_time(ev1) / len(steps)
 
     scrub = None
-    if args.scrub_mb > 0 and not args.profile_only:
+    if do_scrub:
         scrub = torch.ones((args.scrub_mb << 20) // 8, dtype=torch.int64, device=dev)
         scrub_out = torch.zeros((), dtype=torch.int64, device=dev)
 
@@ -306,8 +315,8 @@ def main():
         with torch.cuda.stream(stream):
             torch.cuda.synchronize()
             for i, t in enumerate(steps):
-                q_stage.copy_(Qall[t])
-                lens_stage.copy_(lens_all[t])
+                q_stage.copy_(q_at(t))
+                lens_stage.copy_(lens_at(t))
                 scrubbed = i % 2 == 0
                 if scrubbed:
                     torch.sum(scrub, dim=0, out=scrub_out)
@@ -324,9 +333,9 @@ def main():
     # the current token's K/V of every layer at the append-timing steps (the
     # cache already holds them: the appends rewrite the same values)
     if do_append:
-        app_steps = list(range(t_append, n_steps))
+        app_steps = phase_steps["append_separate"] + phase_steps["append_fused"]
         bi = torch.arange(B, device=dev)
-        cur_all = (lens_all[app_steps, :, 1] - 1).long()  # [S, B]
+        cur_all = (lens_all[[slot[t] for t in app_steps], :, 1] - 1).long()  # [S, B]
         kn_all = torch.stack([torch.stack([Kd[l][bi, :, cur_all[i]] for l in range(L)]) for i in range(len(app_steps))])
         vn_all = torch.stack([torch.stack([Vd[l][bi, :, cur_all[i]] for l in range(L)]) for i in range(len(app_steps))])
         kn_stage = torch.empty_like(kn_all[0])  # [L, B, Hkv, d]
@@ -337,8 +346,8 @@ def main():
         kernel per layer before fastocr_attend, or by fastocr_attend_append."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            q_stage.copy_(Qall[app_steps[0]])
-            lens_stage.copy_(lens_all[app_steps[0]])
+            q_stage.copy_(q_at(app_steps[0]))
+            lens_stage.copy_(lens_at(app_steps[0]))
             kn_stage.copy_(kn_all[0])
             vn_stage.copy_(vn_all[0])
         torch.cuda.synchronize()
@@ -363,8 +372,8 @@ def main():
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for i, t in enumerate(steps):
-                q_stage.copy_(Qall[t])
-                lens_stage.copy_(lens_all[t])
+                q_stage.copy_(q_at(t))
+                lens_stage.copy_(lens_at(t))
                 kn_stage.copy_(kn_all[idx0 + i])
                 vn_stage.copy_(vn_all[idx0 + i])
                 g.replay()
@@ -376,8 +385,8 @@ def main():
     def capture(h):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            q_stage.copy_(Qall[t_timed])
-            lens_stage.copy_(lens_all[t_timed])
+            q_stage.copy_(q_at(phase_steps["graph"][0]))
+            lens_stage.copy_(lens_at(phase_steps["graph"][0]))
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=stream):
             for l in range(L):
@@ -451,22 +460,22 @@ def main():
                 eager_step(h, t, out_stage)
         torch.cuda.synchronize()
         r = {"focal": focal}
-        timed_steps = list(range(t_timed, t_events))
+        timed_steps = phase_steps["graph"]
         # capture one step (the capture itself advances the kept set by one
         # step, so it runs at t_timed - 1's inputs into a scratch copy)
         g = capture(h) if not args.no_graph else None
         r["step_ms"] = time_steps(h, timed_steps, g)
         # per-kernel timing + recorded outputs on the next K steps
         out_hist = torch.empty((K, L, B, Hq, d), dtype=io, device=dev)
-        r["kernels"], r["kernel_steps"] = kernel_times(h, list(range(t_events, t_scrub)), out_hist)
-        if g is not None and scrub is not None:
-            r["scrubbed_step_ms"] = time_steps_scrubbed(list(range(t_scrub, t_append)), g)
+        r["kernels"], r["kernel_steps"] = kernel_times(h, phase_steps["events"], out_hist)
+        if do_scrub:
+            r["scrubbed_step_ms"] = time_steps_scrubbed(phase_steps["scrub"], g)
         del g
         if do_append:
             # each capture advances the kept set by one step, so the two
             # variants run on consecutive step ranges
-            r["append_separate_ms"] = time_append(h, list(range(t_append, t_append + K)), 0, False)
-            r["append_fused_ms"] = time_append(h, list(range(t_append + K, n_steps)), K, True)
+            r["append_separate_ms"] = time_append(h, phase_steps["append_separate"], 0, False)
+            r["append_fused_ms"] = time_append(h, phase_steps["append_fused"], K, True)
         outs[mode] = out_hist.float()
         fo.fastocr_destroy(h)
         results[mode] = r
@@ -483,7 +492,7 @@ def main():
         log(f"calibration copy of {CAL_BYTES >> 20} MiB done")
 
     focal = results["pruned"]["focal"]
-    ev_steps = list(range(t_events, t_scrub))
+    ev_steps = phase_steps["events"]
 
     # algorithmic K/V bytes (rows read x 2*Hkv*d*e)
     e = 2 if wl.dtype == "bf16" else 4
@@ -593,7 +602,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0 and not args.profile_only:
-        cpu = cpu_baseline(wl, st, Kd, Vd, Qall, focal, args.cpu_seconds)
+        cpu = cpu_baseline(wl, st, Kd, Vd, Qall, used, focal, args.cpu_seconds)
 
     line = {
         "metric": "decode-step attention us (all layers) + HBM GB/s, tau=0.05 vs full attention",
@@ -611,7 +620,9 @@ def main():
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "layers": L,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "tau": wl.tau,
                    "num_focal": wl.num_focal, "warmup_steps": w,
-                   "timing": "hip graph replay" if not args.no_graph else "eager"},
+                   "timing": "hip graph replay" if not args.no_graph else "eager",
+                   "decode_steps": wl.steps,
+                   "timed_steps": f"{K} per phase, spread over decode steps {t_timed}..{wl.steps - 1}"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,
@@ -665,13 +676,14 @@ def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):
     return out
 
 
-def cpu_baseline(wl, st, Kd, Vd, Qall, focal_gpu, budget_s):
+def cpu_baseline(wl, st, Kd, Vd, Qall, used, focal_gpu, budget_s):
     """The CPU oracle, as written, timed on a bounded sample of the same run.
 
     Whole decode steps when every layer's cache fits comfortably in host
     memory as float64 (the 7B-like workloads); otherwise one focal and one
     non-focal layer of one pruned step are timed and the step time is
-    extrapolated to all layers.
+    extrapolated to all layers.  Qall[i] holds the queries of decode step
+    used[i] (the warm-up steps first, in order).
     """
     try:
         from threadpoolctl import threadpool_info
@@ -685,7 +697,7 @@ def cpu_baseline(wl, st, Kd, Vd, Qall, focal_gpu, budget_s):
     layer_bytes = Kd[0].numel() * 8 * 2
     if L * layer_bytes < 4e9:
         kv64 = [(host(k), host(v)) for k, v in zip(Kd, Vd)]
-        q_of = lambda t: (lambda l: host(Qall[t, l]))  # noqa: E731
+        q_of = lambda i: (lambda l: host(Qall[i, l]))  # noqa: E731
         orc = DecodeOracle(num_layers=L, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
                            head_dim=wl.head_dim, tau=wl.tau, num_focal=wl.num_focal,
                            warmup_steps=wl.warmup_steps)
@@ -694,18 +706,19 @@ def cpu_baseline(wl, st, Kd, Vd, Qall, focal_gpu, budget_s):
             orc.step(t, q_of(t), lambda l: kv64[l], st.lens(t))
         warm_s = time.time() - t0
         times = []
-        t = wl.warmup_steps
+        i = wl.warmup_steps  # pruned steps in the order the GPU ran them
         begin = time.time()
-        while time.time() - begin < budget_s and t < Qall.shape[0]:
+        while time.time() - begin < budget_s and i < len(used):
             s0 = time.time()
-            orc.step(t, q_of(t), lambda l: kv64[l], st.lens(t))
+            orc.step(used[i], q_of(i), lambda l: kv64[l], st.lens(used[i]))
             times.append(time.time() - s0)
-            t += 1
+            i += 1
         us = float(np.median(times)) * 1e6 if times else None
         log(f"cpu oracle: warm-up {warm_s:.1f}s, {len(times)} pruned steps, median {us:.0f} us/step, "
             f"focal {[int(c) for c in orc.focal]} (gpu {focal_gpu})")
         sample = (f"float64 numpy oracle: {wl.warmup_steps} warm-up steps then {len(times)} pruned "
-                  f"decode steps (all {L} layers) of the same workload; median per pruned step")
+                  f"decode steps (all {L} layers; the GPU run's steps in its order) of the same "
+                  f"workload; median per pruned step")
     else:
         t = wl.warmup_steps
         lens = st.lens(t)
