@@ -455,7 +455,10 @@ def main():
             for t in range(w):  # warm-up steps (full attention on every layer in both modes)
                 eager_step(h, t, out_stage)
             if mode == "pruned":
+                torch.cuda.synchronize()
+                p0 = time.perf_counter()
                 focal = fo.fastocr_profile_warmup(h)
+                profile_ms = (time.perf_counter() - p0) * 1e3
             for t in range(w, t_timed):  # untimed steps
                 eager_step(h, t, out_stage)
         torch.cuda.synchronize()
@@ -597,6 +600,13 @@ def main():
                 ap[f"{mode}_separate_append_us_per_step"] = round(results[mode]["append_separate_ms"] * 1e3, 2)
                 ap[f"{mode}_fused_append_us_per_step"] = round(results[mode]["append_fused_ms"] * 1e3, 2)
         extra["append"] = ap
+    if "full" in results:
+        # periodic re-selection (reprofile_every = R): every R pruned steps
+        # cost a window of w full-attention steps plus one profile call
+        R = 256
+        over = (w * (results["full"]["step_ms"] - pr_ms) + profile_ms) / (R + w)
+        extra["reselection"] = {"profile_call_us": round(profile_ms * 1e3, 1), "every_R": R,
+                                "amortized_us_per_step": round(over * 1e3, 2)}
     if not args.profile_only:
         extra["platform"] = platform_probe(torch, stream)
 

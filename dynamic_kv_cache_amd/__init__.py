@@ -58,6 +58,7 @@ class Config:
     sm_scale: float = 0.0
     min_img_tokens: int = 0
     max_text_tokens: int = 0
+    reprofile_every: int = 0  # R > 0: re-pick the focal layers after every R pruned steps
 
     def to_c(self) -> _abi.Config:
         return _abi.Config(
@@ -67,7 +68,8 @@ class Config:
             min_img_tokens=self.min_img_tokens, max_text_tokens=self.max_text_tokens,
             dtype=DTYPE_BF16 if self.dtype == "bf16" else DTYPE_F32,
             num_focal=self.num_focal, warmup_steps=self.warmup_steps,
-            mode=MODE_FULL if self.mode == "full" else MODE_PRUNED)
+            mode=MODE_FULL if self.mode == "full" else MODE_PRUNED,
+            reprofile_every=self.reprofile_every)
 
 
 # ---------------------------------------------------------------------------
@@ -172,6 +174,12 @@ def fastocr_attend_append(h: Handle, layer: int, q, k_new, v_new, k_cache, v_cac
 def fastocr_profile_warmup(h: Handle) -> List[int]:
     arr = (ctypes.c_int32 * h.cfg.num_focal)()
     _check("fastocr_profile_warmup", lib().fastocr_profile_warmup(h.ptr, arr))
+    return list(arr)
+
+
+def fastocr_get_focal_layers(h: Handle) -> List[int]:
+    arr = (ctypes.c_int32 * h.cfg.num_focal)()
+    _check("fastocr_get_focal_layers", lib().fastocr_get_focal_layers(h.ptr, arr))
     return list(arr)
 
 

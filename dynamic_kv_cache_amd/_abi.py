@@ -49,6 +49,7 @@ class Config(ctypes.Structure):
         ("warmup_steps", c_int32),
         ("mode", c_int32),
         ("max_text_tokens", c_int32),
+        ("reprofile_every", c_int32),
     ]
 
 
@@ -65,7 +66,7 @@ class Info(ctypes.Structure):
         ("sparse_direct", c_int32),
         ("sparse_wave_states", c_int32),
         ("sparse_pipe", c_int32),
-        ("reserved", c_int32),
+        ("profiles", c_int32),
         ("scratch_bytes", c_int64),
     ]
 
@@ -84,6 +85,7 @@ SIGNATURES = [
     ("fastocr_attend_append", c_int32,
      [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     ("fastocr_profile_warmup", c_int32, [c_void_p, ctypes.POINTER(c_int32)]),
+    ("fastocr_get_focal_layers", c_int32, [c_void_p, ctypes.POINTER(c_int32)]),
     ("fastocr_destroy", c_int32, [c_void_p]),
     ("fastocr_get_status", c_int32, [c_void_p, ctypes.POINTER(c_int32)]),
     ("fastocr_get_selection", c_int32, [c_void_p, c_void_p, c_void_p]),

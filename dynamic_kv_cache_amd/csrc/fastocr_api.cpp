@@ -75,6 +75,9 @@ struct fastocr_handle {
   float scale_log2 = 0.f;
 
   int step = 0, next_layer = 0, phase = PHASE_WARMUP;
+  int warm_pos = 0;       // step index inside the current warm-up window
+  int pruned_since = 0;   // pruned steps since the last profile
+  int profiles = 0;       // completed profiles (first warm-up and re-selections)
   bool poisoned = false;
   std::vector<int32_t> focal;
   std::vector<char> is_focal;
@@ -274,6 +277,7 @@ bool config_ok(const fastocr_config& c) {
     if (c.num_focal < 1 || c.num_focal > c.num_layers) return false;
     if (c.warmup_steps < 1) return false;
   }
+  if (c.reprofile_every < 0) return false;
   // every cache index must fit comfortably in 64-bit byte offsets
   const double cache_elems = (double)c.batch * c.num_kv_heads * c.max_seq_len * c.head_dim;
   if (cache_elems > 4.0e15) return false;
@@ -464,6 +468,45 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   return FASTOCR_OK;
 }
 
+// Focal Layer Selection at the end of a warm-up window (the first one, or a
+// periodic re-selection window): synchronises the stream.
+static int profile_impl(fastocr_handle* h) {
+  const fastocr_config& c = h->cfg;
+  const size_t BH = (size_t)c.batch * c.num_q_heads;
+  const size_t per_layer = (size_t)c.warmup_steps * BH;
+  std::vector<float> tm((size_t)c.num_layers * per_layer);
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(tm.data(), h->text_mass, tm.size() * sizeof(float), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(h, e);
+  // Image-attention ratio of a layer: mean over the window's steps, sequences
+  // and heads of the image probability mass, 1 - text mass (Focal Layer
+  // Selection).
+  h->ratios.assign(c.num_layers, 0.0);
+  for (int l = 0; l < c.num_layers; ++l) {
+    double s = 0.0;
+    for (size_t i = 0; i < per_layer; ++i) s += 1.0 - (double)tm[l * per_layer + i];
+    h->ratios[l] = s / (double)per_layer;
+  }
+  h->focal.assign(c.num_focal, 0);
+  select_focal(h->ratios.data(), c.num_layers, c.num_focal, h->focal.data());
+  h->is_focal.assign(c.num_layers, 0);
+  for (int32_t l : h->focal) h->is_focal[l] = 1;
+  // The first pruned step inherits the set picked from the window's last
+  // step's scores at the deepest focal layer (Cross-Step Fixation Reuse /
+  // Implementation).  The image-token counts come from the lens of that
+  // step, copied aside when it ran.
+  const int deepest = h->focal.back();
+  int rc = run_topk(h, h->warm_scores + (size_t)deepest * c.batch * h->n_stride, h->lens_shadow, nullptr);
+  if (rc) return rc;
+  e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return fail_hip(h, e);
+  h->phase = PHASE_PRUNED;
+  h->pruned_since = 0;
+  ++h->profiles;
+  return FASTOCR_OK;
+}
+
 // One layer of the current step (fastocr_attend, fastocr_attend_append).
 static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* lens, void* out) {
@@ -472,17 +515,23 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
   const fastocr_config& c = h->cfg;
   if (layer < 0 || layer >= c.num_layers) return FASTOCR_ERR_INVALID_ARG;
   if (layer != h->next_layer) return FASTOCR_ERR_STATE;
-  if (h->phase == PHASE_WARMUP_DONE) return FASTOCR_ERR_STATE;
-
   int rc = FASTOCR_OK;
+  if (h->phase == PHASE_WARMUP_DONE) {
+    // the first warm-up ends with an explicit fastocr_profile_warmup; a
+    // re-selection window profiles itself here, before the step's first layer
+    if (h->profiles == 0) return FASTOCR_ERR_STATE;
+    rc = profile_impl(h);
+    if (rc) return rc;
+  }
+
   const size_t BH = (size_t)c.batch * c.num_q_heads;
   switch (h->phase) {
     case PHASE_FULL:
       rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
       break;
     case PHASE_WARMUP: {
-      float* tm = h->text_mass + ((size_t)layer * c.warmup_steps + h->step) * BH;
-      float* sc = (h->step == c.warmup_steps - 1)
+      float* tm = h->text_mass + ((size_t)layer * c.warmup_steps + h->warm_pos) * BH;
+      float* sc = (h->warm_pos == c.warmup_steps - 1)
                       ? h->warm_scores + (size_t)layer * c.batch * h->n_stride
                       : nullptr;
       rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc, false);
@@ -511,7 +560,13 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
   if (++h->next_layer == c.num_layers) {
     h->next_layer = 0;
     ++h->step;
-    if (h->phase == PHASE_WARMUP && h->step == c.warmup_steps) h->phase = PHASE_WARMUP_DONE;
+    if (h->phase == PHASE_WARMUP && ++h->warm_pos == c.warmup_steps) h->phase = PHASE_WARMUP_DONE;
+    if (h->phase == PHASE_PRUNED && ++h->pruned_since == c.reprofile_every) {
+      // periodic re-selection: a new warm-up window of w full steps, whose
+      // statistics alone pick the next focal set
+      h->phase = PHASE_WARMUP;
+      h->warm_pos = 0;
+    }
   }
   return FASTOCR_OK;
 }
@@ -538,37 +593,16 @@ int fastocr_attend_append(fastocr_handle* h, int32_t layer, const void* q, const
 int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out) {
   if (!h || !focal_layers_out) return FASTOCR_ERR_INVALID_ARG;
   if (h->poisoned || h->phase != PHASE_WARMUP_DONE) return FASTOCR_ERR_STATE;
-  const fastocr_config& c = h->cfg;
-  const size_t BH = (size_t)c.batch * c.num_q_heads;
-  const size_t per_layer = (size_t)c.warmup_steps * BH;
-  std::vector<float> tm((size_t)c.num_layers * per_layer);
-  hipError_t e = hipStreamSynchronize(h->stream);
-  if (e == hipSuccess)
-    e = hipMemcpy(tm.data(), h->text_mass, tm.size() * sizeof(float), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail_hip(h, e);
-  // Image-attention ratio of a layer: mean over warm-up steps, sequences and
-  // heads of the image probability mass, 1 - text mass (Focal Layer Selection).
-  h->ratios.assign(c.num_layers, 0.0);
-  for (int l = 0; l < c.num_layers; ++l) {
-    double s = 0.0;
-    for (size_t i = 0; i < per_layer; ++i) s += 1.0 - (double)tm[l * per_layer + i];
-    h->ratios[l] = s / (double)per_layer;
-  }
-  h->focal.assign(c.num_focal, 0);
-  select_focal(h->ratios.data(), c.num_layers, c.num_focal, h->focal.data());
-  h->is_focal.assign(c.num_layers, 0);
-  for (int32_t l : h->focal) h->is_focal[l] = 1;
-  // The first pruned step inherits the set picked from the last warm-up
-  // step's scores at the deepest focal layer (Cross-Step Fixation Reuse /
-  // Implementation).  The image-token counts come from the lens of the last
-  // warm-up step, copied aside when that step ran.
-  const int deepest = h->focal.back();
-  int rc = run_topk(h, h->warm_scores + (size_t)deepest * c.batch * h->n_stride, h->lens_shadow, nullptr);
+  const int rc = profile_impl(h);
   if (rc) return rc;
-  e = hipStreamSynchronize(h->stream);
-  if (e != hipSuccess) return fail_hip(h, e);
-  h->phase = PHASE_PRUNED;
-  std::memcpy(focal_layers_out, h->focal.data(), sizeof(int32_t) * c.num_focal);
+  std::memcpy(focal_layers_out, h->focal.data(), sizeof(int32_t) * h->cfg.num_focal);
+  return FASTOCR_OK;
+}
+
+int fastocr_get_focal_layers(fastocr_handle* h, int32_t* layers_host) {
+  if (!h || !layers_host) return FASTOCR_ERR_INVALID_ARG;
+  if (h->focal.empty()) return FASTOCR_ERR_STATE;
+  std::memcpy(layers_host, h->focal.data(), sizeof(int32_t) * h->focal.size());
   return FASTOCR_OK;
 }
 
@@ -645,6 +679,7 @@ int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int3
   for (int l = 0; l < L; ++l)
     if (seen[l]) h->focal.push_back(l);
   h->is_focal = seen;
+  if (h->phase == PHASE_WARMUP_DONE) h->pruned_since = 0;
   h->phase = PHASE_PRUNED;
   return FASTOCR_OK;
 }
@@ -662,6 +697,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->sparse_wave_states = h->wave_states ? 1 : 0;
   info->sparse_pipe = h->sparse_pipe ? 1 : 0;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
+  info->profiles = h->profiles;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;
 }

@@ -112,6 +112,9 @@ typedef struct fastocr_config {
                               the sparse launch.  A sequence beyond the bounds given
                               by min_img_tokens / max_text_tokens is truncated to
                               the launched splits and flagged (FASTOCR_FLAG_ROWS_TRUNCATED). */
+  int32_t reprofile_every; /* R >= 0: after every R pruned steps the next w steps are a new
+                              warm-up window and the focal set is picked again from that
+                              window alone (periodic re-selection; 0 = pick once) */
 } fastocr_config;
 
 typedef struct fastocr_info {
@@ -126,7 +129,7 @@ typedef struct fastocr_info {
   int32_t sparse_direct;  /* 1: non-focal layers finish in one split (no merge launch) */
   int32_t sparse_wave_states; /* 1: kept-token splits write one merge state per wave */
   int32_t sparse_pipe;    /* 1: kept-token passes run pipelined multi-round splits */
-  int32_t reserved;
+  int32_t profiles;       /* focal-set picks so far (first warm-up and re-selections) */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
 
@@ -161,17 +164,27 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
  *   out      device [B, Hq, d] of dtype; attention output.
  * Query head h reads KV head h / (Hq / Hkv).  Which computation runs:
  *   FULL mode: full attention.
- *   PRUNED mode, step < w: full attention; records each head's image mass
- *            and, at step w-1, every layer's image-token scores.
- *   PRUNED mode, step >= w, layer in C: full attention, then per sequence the
- *            head-summed attention probability of every image token, then the
- *            k_b = clamp(ceil(tau*n_img_b - 1e-9), 1, n_img_b) highest
+ *   PRUNED mode, warm-up window (the first w steps, and with reprofile_every
+ *            = R > 0 the w steps after every R pruned steps): full
+ *            attention; records each head's image mass and, at the window's
+ *            last step, every layer's image-token scores.
+ *   PRUNED mode, pruned step, layer in C: full attention, then per sequence
+ *            the head-summed attention probability of every image token, then
+ *            the k_b = clamp(ceil(tau*n_img_b - 1e-9), 1, n_img_b) highest
  *            (ties to the lower index) replace the kept set.
- *   PRUNED mode, step >= w, layer not in C: attention over the kept set plus
- *            rows [n_img_b, len_b).
- * Asynchronous: enqueues on the handle's stream and returns.  Errors:
- * INVALID_ARG (null pointer, layer out of range), STATE (layer out of order,
- * step >= w before fastocr_profile_warmup, poisoned handle), HIP. */
+ *   PRUNED mode, pruned step, layer not in C: attention over the kept set
+ *            plus rows [n_img_b, len_b).
+ * The first window ends with fastocr_profile_warmup.  A re-selection window
+ * (R > 0) is profiled by the layer-0 call of the step after it, exactly as
+ * fastocr_profile_warmup would (that call synchronises the stream); the new
+ * focal set is read with fastocr_get_focal_layers.  The focal layers are
+ * chosen as the summary's Focal Layer Selection describes; repeating the
+ * choice periodically is this library's reading of the adaptive layer
+ * selection that the summary's conclusion lists as future work.
+ * Asynchronous otherwise: enqueues on the handle's stream and returns.
+ * Errors: INVALID_ARG (null pointer, layer out of range), STATE (layer out
+ * of order, a pruned step before the first fastocr_profile_warmup, poisoned
+ * handle), HIP. */
 int fastocr_attend(fastocr_handle* h, int32_t layer, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* lens, void* out);
 
@@ -193,14 +206,20 @@ int fastocr_attend_append(fastocr_handle* h, int32_t layer, const void* q, const
                           const void* v_new, void* k_cache, void* v_cache, const int32_t* lens,
                           void* out);
 
-/* fastocr_profile_warmup: after exactly w completed warm-up steps, pick the
- * focal layers (Focal Layer Selection): the |C| layers with the largest mean
- * image-attention mass over heads, sequences and warm-up steps (ties to the
- * lower layer), written ascending to focal_layers_out (host, |C| entries).
- * Initialises the kept set from step w-1's scores at the deepest focal layer
- * and switches the handle to pruned steps.  Synchronises the stream.
- * Errors: INVALID_ARG (null), STATE (not exactly after the warm-up), HIP. */
+/* fastocr_profile_warmup: after a completed warm-up window (exactly w
+ * steps), pick the focal layers (Focal Layer Selection): the |C| layers with
+ * the largest mean image-attention mass over heads, sequences and the
+ * window's steps (ties to the lower layer), written ascending to
+ * focal_layers_out (host, |C| entries).  Initialises the kept set from the
+ * window's last step's scores at the deepest focal layer and switches the
+ * handle to pruned steps.  Synchronises the stream.  Errors: INVALID_ARG
+ * (null), STATE (not exactly after a window), HIP. */
 int fastocr_profile_warmup(fastocr_handle* h, int32_t* focal_layers_out);
+
+/* fastocr_get_focal_layers: the current focal set C, ascending, into
+ * layers_host (host int32, num_focal entries).  Errors: INVALID_ARG (null),
+ * STATE (no focal set picked or set yet). */
+int fastocr_get_focal_layers(fastocr_handle* h, int32_t* layers_host);
 
 /* fastocr_destroy: synchronise the stream and free the handle's scratch.
  * NULL is accepted.  Returns HIP if the final synchronisation failed (the

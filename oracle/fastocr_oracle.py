@@ -203,18 +203,26 @@ class DecodeOracle:
       kv_of(l) -> (K, V) of layer l, each [B, Hkv, S, d]
       lens     -> [B, 2] (image tokens, valid rows)
 
-    Steps 0..w-1 are the warm-up: every layer runs full attention and its
-    image mass is recorded (Focal Layer Selection).  After step w-1 the focal
-    set C is chosen and F_last is initialised from that step's scores at the
-    deepest focal layer.  Later steps start from S = F_last (Cross-Step
-    Fixation Reuse / Implementation); a focal layer runs full attention and
-    replaces S with its top-k pick; a non-focal layer attends to S plus all
-    text rows; at the end of the step F_last = S.
+    The first w steps are the warm-up: every layer runs full attention and
+    its image mass is recorded (Focal Layer Selection).  After the last of
+    them the focal set C is chosen and F_last is initialised from that step's
+    scores at the deepest focal layer.  Later steps start from S = F_last
+    (Cross-Step Fixation Reuse / Implementation); a focal layer runs full
+    attention and replaces S with its top-k pick; a non-focal layer attends to
+    S plus all text rows; at the end of the step F_last = S.
+
+    Periodic re-selection (``reprofile_every`` = R > 0; the summary names
+    adaptive layer selection as a direction its conclusion leaves open, and
+    the reading here is the plainest one built from the warm-up itself):
+    after every R pruned steps the next w steps are a new warm-up window, and
+    C and F_last are chosen again from that window alone, exactly as after
+    the first one.  Phases follow the number of steps run, not ``t``.
     """
 
     def __init__(self, *, num_layers: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, tau: float, num_focal: int, warmup_steps: int,
-                 scale: Optional[float] = None, full_mode: bool = False):
+                 scale: Optional[float] = None, full_mode: bool = False,
+                 reprofile_every: int = 0):
         self.L = num_layers
         self.Hq = num_q_heads
         self.Hkv = num_kv_heads
@@ -224,11 +232,15 @@ class DecodeOracle:
         self.w = warmup_steps
         self.scale = (1.0 / math.sqrt(head_dim)) if not scale else float(scale)
         self.full_mode = full_mode
+        self.reprofile_every = reprofile_every
         self.mass: Dict[int, List[np.ndarray]] = {l: [] for l in range(num_layers)}
         self.warm_scores: Dict[int, List[np.ndarray]] = {}
         self.ratios: Optional[np.ndarray] = None
         self.focal: Optional[np.ndarray] = None
         self.f_last: Optional[List[np.ndarray]] = None
+        self.window_pos: Optional[int] = 0  # step index inside a warm-up window, None when pruning
+        self.pruned_since = 0  # pruned steps since the last profile
+        self.profiles: List[Tuple[int, np.ndarray]] = []  # (t of the first pruned step, C)
 
     # -- warm-up profiler (Focal Layer Selection) --------------------------
     def layer_ratios(self) -> np.ndarray:
@@ -250,10 +262,15 @@ class DecodeOracle:
         B = lens.shape[0]
         if self.full_mode:
             return self._full_step(t, q_of, kv_of, lens, "full")
-        if t < self.w:
-            rec = self._full_step(t, q_of, kv_of, lens, "warmup")
-            if t == self.w - 1:
+        if self.window_pos is not None:
+            last = self.window_pos == self.w - 1
+            rec = self._full_step(t, q_of, kv_of, lens, "warmup", keep_scores=last)
+            self.window_pos += 1
+            if last:
                 self._finish_warmup(lens)
+                self.window_pos = None
+                self.pruned_since = 0
+                self.profiles.append((t + 1, self.focal.copy()))
             return rec
 
         rec = StepRecord(t=t, phase="pruned")
@@ -280,9 +297,15 @@ class DecodeOracle:
                     out[b] = sparse_attention(q[b], K[b], V[b], current[b], n, length, self.scale)
             rec.outs.append(out)
         self.f_last = current
+        self.pruned_since += 1
+        if self.reprofile_every > 0 and self.pruned_since == self.reprofile_every:
+            # a new warm-up window: statistics of that window alone
+            self.window_pos = 0
+            self.mass = {l: [] for l in range(self.L)}
+            self.warm_scores = {}
         return rec
 
-    def _full_step(self, t, q_of, kv_of, lens, phase) -> StepRecord:
+    def _full_step(self, t, q_of, kv_of, lens, phase, keep_scores=False) -> StepRecord:
         B = lens.shape[0]
         rec = StepRecord(t=t, phase=phase)
         for l in range(self.L):
@@ -297,7 +320,7 @@ class DecodeOracle:
                 scores.append(image_scores(p, n))
             if phase == "warmup":
                 self.mass[l].append(np.stack(masses))
-                if t == self.w - 1:
+                if keep_scores:
                     self.warm_scores[l] = scores
             rec.scores[l] = scores
             rec.outs.append(out)

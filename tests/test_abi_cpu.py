@@ -32,11 +32,34 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(n for n, _, _ in _abi.SIGNATURES)
 
 
-def test_struct_layouts_match_header():
-    # double first, then a float and thirteen int32 -> 64 bytes, no padding
-    assert ctypes.sizeof(_abi.Config) == 64
-    assert ctypes.sizeof(_abi.Info) == 56
-    assert ctypes.sizeof(_abi.Timing) == 3 * 8 * _abi.KC_COUNT
+def test_struct_layouts_match_header(tmp_path):
+    # the header compiled by the host C compiler gives every field's offset
+    # and each struct's size; the ctypes mirrors must agree
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"fastocr_config": _abi.Config, "fastocr_info": _abi.Info, "fastocr_timing": _abi.Timing}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "fastocr.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    include = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", include, "-o", str(exe), str(src)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, value = line.split()
+        got[(cname, field)] = int(value)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
 
 
 @pytest.mark.parametrize("tau", [0.02, 0.05, 0.1, 0.2, 0.25, 0.3, 1 / 3, 0.5, 0.7, 1.0])
@@ -72,6 +95,7 @@ BAD = [
     dict(num_focal=5), dict(warmup_steps=0), dict(max_img_tokens=305), dict(batch=0),
     dict(max_seq_len=0), dict(num_layers=0), dict(sm_scale=-1.0), dict(min_img_tokens=300),
     dict(max_text_tokens=-1), dict(max_text_tokens=305), dict(batch=32768),
+    dict(reprofile_every=-1),
 ]
 
 
@@ -91,6 +115,7 @@ def test_null_arguments():
     assert lib.fastocr_create(ctypes.byref(c), None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_attend(None, 0, None, None, None, None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_profile_warmup(None, None) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_get_focal_layers(None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_destroy(None) == fo.OK
     assert lib.fastocr_select_topk(None, 4, None, 1, 0.5, None, 4, None, None) == fo.ERR_INVALID_ARG
 

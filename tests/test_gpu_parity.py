@@ -402,3 +402,78 @@ def test_attend_append_equals_prewritten_row(monkeypatch, case):
     assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
     fo.fastocr_destroy(ha)
     fo.fastocr_destroy(hb)
+
+
+# ---------------------------------------------------------------------------
+# periodic re-selection of the focal layers
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name,over,R", [
+    # planted strong layers {1, 3} -> {0, 2} at step 20; windows at steps
+    # 0-3, 12-15, 24-27, 36-39
+    ("tiny-fp32", dict(steps=40, drift=(20, (0, 2))), 8),
+    # strong band 14-22 -> layers {3, 7, 11, 25} at step 20; windows at
+    # steps 0-7, 20-27, 40-47
+    ("7b-b1", dict(steps=50, drift=(20, (3, 7, 11, 25))), 12),
+])
+def test_reprofile_follows_drift(name, over, R):
+    from oracle import DecodeOracle
+    wl = get_workload(name).with_overrides(**over)
+    up = upload(wl)
+    L, B, Hq, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim
+    h = fo.fastocr_create(make_config(up, reprofile_every=R))
+    orc = DecodeOracle(num_layers=L, num_q_heads=Hq, num_kv_heads=wl.num_kv_heads, head_dim=d,
+                       tau=wl.tau, num_focal=wl.num_focal, warmup_steps=wl.warmup_steps,
+                       reprofile_every=R)
+    scale = 1 / math.sqrt(d)
+    k_max = fo.fastocr_get_info(h)["k_max"]
+    sel = torch.zeros((B, k_max), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=up.io_dtype, device=DEV)
+    picks, prev, worst, jac = [], None, 0.0, []
+    for t in range(wl.steps):
+        lens = up.st.lens(t)
+        rec = orc.step(t, lambda l: up.q[l][t].astype(np.float64), up.kv64, lens)
+        phase = fo.fastocr_get_info(h)["phase"]
+        if t == wl.warmup_steps:
+            assert phase == 1
+            fo.fastocr_profile_warmup(h)
+        assert (phase == 0) == (rec.phase == "warmup"), (t, phase, rec.phase)
+        for l in range(L):
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out)
+            got = out.float().cpu().numpy().astype(np.float64)
+            what = f"t={t} l={l}"
+            if l == 0 and rec.phase == "pruned":
+                # a window that just ended was profiled by this call
+                focal = fo.fastocr_get_focal_layers(h)
+                assert focal == [int(x) for x in orc.focal], (t, focal, list(orc.focal))
+                if prev.phase == "warmup":
+                    picks.append((t, focal))
+            if rec.phase == "warmup" or l in orc.focal:
+                worst = max(worst, check_out(got, rec.outs[l], wl.dtype, what))
+            if rec.phase == "pruned":
+                fo.fastocr_get_selection(h, sel, cnt)
+                c, s = cnt.cpu().numpy(), sel.cpu().numpy()
+                for b in range(B):
+                    n, length = int(lens[b, 0]), int(lens[b, 1])
+                    k = kept_count(wl.tau, n)
+                    if l in orc.focal:
+                        jac.append(check_set(s[b, :c[b]], rec.scores[l][b], k, f"set {what} b={b}"))
+                    else:
+                        if l == 0 and prev.phase == "warmup":
+                            # warm start right after a (re-)profile: the
+                            # window's last step at the deepest focal layer
+                            jac.append(check_set(s[b, :c[b]], prev.scores[max(orc.focal)][b], k,
+                                                 f"warm start {what} b={b}"))
+                        want = sparse_attention(up.q[l][t][b].astype(np.float64), up.kv64(l)[0][b],
+                                                up.kv64(l)[1][b], s[b, :c[b]], n, length, scale)
+                        worst = max(worst, check_out(got[b], want, wl.dtype, f"{what} b={b}"))
+        prev = rec
+    want_picks = [(t, [int(x) for x in c]) for t, c in orc.profiles if t < wl.steps]
+    assert picks == want_picks, (picks, want_picks)
+    assert len(picks) >= 3 and picks[0][1] != picks[-1][1], picks  # the drift was followed
+    assert fo.fastocr_get_info(h)["profiles"] == len(want_picks)
+    assert fo.fastocr_get_status(h) == 0
+    fo.fastocr_destroy(h)
+    log(f"[reprofile] {name}: picks {picks}, worst out {worst:.2e}, mean Jaccard {np.mean(jac):.3f}")

@@ -353,6 +353,61 @@ def test_no_eviction_token_reselected_later():
 # ---------------------------------------------------------------------------
 
 
+
+# ---------------------------------------------------------------------------
+# periodic re-selection of the focal layers
+# ---------------------------------------------------------------------------
+
+
+def _drift_run(reprofile_every, oracle_cls=None):
+    # tiny page read for 40 steps; the planted strong layers move from {1, 3}
+    # to {0, 2} at step 20
+    wl = get_workload("tiny-fp32").with_overrides(steps=40, drift=(20, (0, 2)))
+    st, kv, qs = _tiny_inputs(wl)
+    cls = oracle_cls or ofo.DecodeOracle
+    orc = cls(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+              head_dim=wl.head_dim, tau=wl.tau, num_focal=wl.num_focal,
+              warmup_steps=wl.warmup_steps, reprofile_every=reprofile_every)
+    recs = [orc.step(t, lambda l: qs[l][t], lambda l: kv[l], st.lens(t)) for t in range(wl.steps)]
+    return wl, st, orc, recs
+
+
+def test_reprofile_follows_planted_drift():
+    # windows of w = 4 steps after every 8 pruned steps: steps 0-3, 12-15,
+    # 24-27, 36-39; only the window after the drift sees the new layers
+    wl, st, orc, recs = _drift_run(8)
+    assert [r.phase for r in recs] == (["warmup"] * 4 + ["pruned"] * 8) * 3 + ["warmup"] * 4
+    assert [(t, list(c)) for t, c in orc.profiles] == [(4, [1, 3]), (16, [1, 3]), (28, [0, 2]),
+                                                       (40, [0, 2])]
+    # each re-profile restarts the warm start from its window's last step
+    for first in (16, 28):
+        focal = [list(c) for t, c in orc.profiles if t == first][0]
+        last = recs[first - 1]
+        k = ofo.kept_count(wl.tau, int(st.n_img[0]))
+        want = ofo.select_top(last.scores[max(focal)][0], k)
+        np.testing.assert_array_equal(recs[first].warm_start[0], want)
+    # without re-selection the drift is missed
+    _, _, orc0, recs0 = _drift_run(0)
+    assert [(t, list(c)) for t, c in orc0.profiles] == [(4, [1, 3])]
+    assert all(r.phase == "pruned" for r in recs0[4:])
+
+
+def test_reprofile_pin_catches_pooled_windows():
+    # planted mistake: a re-profile that pools every window's statistics
+    # instead of using its own window only
+    class Pooled(ofo.DecodeOracle):
+        def step(self, *a, **k):
+            keep = {l: list(v) for l, v in self.mass.items()}
+            rec = super().step(*a, **k)
+            if self.window_pos == 0 and rec.phase == "pruned":
+                self.mass = keep
+            return rec
+
+    with pytest.raises(AssertionError):
+        _, _, orc, _ = _drift_run(8, oracle_cls=Pooled)
+        assert [list(c) for _, c in orc.profiles][2] == [0, 2]
+
+
 def _mut_gqa_modulo(h, Hq, Hkv):
     return h % Hkv
 

@@ -88,6 +88,10 @@ class Workload:
     alpha_lo: Optional[float]  # fixed low alpha, else U[0.3, 1] per layer
     sigma: float
     seed: int
+    # (t, layers): from decode step t on, the strong alpha sits on these layers
+    # and the layers that had it before take the low alpha (a focal set that
+    # drifts during decoding); None = no drift
+    drift: Optional[Tuple[int, Tuple[int, ...]]] = None
 
     @property
     def group(self) -> int:
@@ -185,9 +189,19 @@ class Structure:
     grid_w: np.ndarray  # [B] columns of each page grid
     grid_h: np.ndarray  # [B] rows of each page grid
     centre: np.ndarray  # [T, B] window centre cell (image-token index)
-    alpha: np.ndarray  # [L] float32
+    alpha: np.ndarray  # [L] float32, query alignment of each layer
     max_seq_len: int  # cache row stride S_max
     windows: List[List[np.ndarray]] = field(default_factory=list)  # [B][T] token ids
+    alpha_late: Optional[np.ndarray] = None  # [L] alpha from drift_step on (drifting workloads)
+    drift_step: int = 0
+
+    def alpha_at(self, l: int, steps) -> np.ndarray:
+        """[len(steps)] float32: query alignment of layer l at each step."""
+        steps = np.asarray(list(steps), dtype=np.int64)
+        a = np.full(len(steps), self.alpha[l], dtype=np.float32)
+        if self.alpha_late is not None:
+            a[steps >= self.drift_step] = self.alpha_late[l]
+        return a
 
     def lens(self, t: int) -> np.ndarray:
         """[B, 2] int32: (image tokens, valid cache rows) at decode step t.
@@ -267,9 +281,18 @@ def make_structure(wl: Workload) -> Structure:
             alpha[l] = wl.alpha_hi
     if wl.focal_band is not None:
         alpha[wl.focal_band[0]: wl.focal_band[1] + 1] = wl.alpha_hi
+    alpha_late = None
+    if wl.drift is not None:
+        low = (np.full(L, wl.alpha_lo, dtype=np.float64) if wl.alpha_lo is not None
+               else arng.uniform(0.3, 1.0, size=L))
+        alpha_late = np.where(alpha == wl.alpha_hi, low, alpha)
+        for l in wl.drift[1]:
+            alpha_late[l] = wl.alpha_hi
+        alpha_late = alpha_late.astype(np.float32)
     s_max = int(np.max(n_img + n_prompt)) + T
     st = Structure(n_img=n_img, n_prompt=n_prompt, grid_w=grid_w, grid_h=grid_h,
-                   centre=centre, alpha=alpha.astype(np.float32), max_seq_len=s_max)
+                   centre=centre, alpha=alpha.astype(np.float32), max_seq_len=s_max,
+                   alpha_late=alpha_late, drift_step=0 if wl.drift is None else int(wl.drift[0]))
     st.windows = [[_window_tokens(centre[t, b], int(n_img[b]), int(grid_w[b]), wl.window)
                    for t in range(T)] for b in range(B)]
     return st
@@ -342,7 +365,7 @@ class Generator:
             gathered = K[b][:, idx, :]  # [Hkv, S, wmax, d]
             mean = np.einsum("hswd,sw->shd", gathered, wgt, optimize=True)  # [S, Hkv, d]
             mean_q = np.repeat(mean, g, axis=1)  # [S, Hq, d], head h -> kv head h // g
-            q[:, b] = st.alpha[l] * mean_q + np.float32(wl.sigma) * eps[:, b]
+            q[:, b] = st.alpha_at(l, steps)[:, None, None] * mean_q + np.float32(wl.sigma) * eps[:, b]
         return _to_dtype(q, wl.dtype)
 
 
@@ -412,5 +435,6 @@ class DeviceGenerator:
             gathered = Kb[:, idx_t.reshape(-1)].reshape(Hkv, len(steps), wmax, d)
             mean = (gathered * wgt_t[None, :, :, None]).sum(dim=2)  # [Hkv, S, d]
             mean_q = mean.permute(1, 0, 2).repeat_interleave(g_, dim=1)  # [S, Hq, d]
-            q[:, b] = float(st.alpha[l]) * mean_q + float(wl.sigma) * eps[:, b]
+            a_t = torch.from_numpy(st.alpha_at(l, steps)).to(self.device)[:, None, None]
+            q[:, b] = a_t * mean_q + float(wl.sigma) * eps[:, b]
         return q.to(self.io_dtype)
