@@ -1054,9 +1054,9 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
     // and takes the weights of its partial outputs by lane permutes: no
     // workgroup barrier.
     const float M = wave_max(q.x);
-    if (M == -INFINITY) {  // no rows at all
+    if (M == -INFINITY) {  // no rows at all: zero output and no image mass
       for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
-      if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
+      if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 1.f;  // image mass = 1 - this
       return;
     }
     const float w = q.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(q.x - M);
@@ -1102,9 +1102,9 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
   float M = s_red[0][0];
 #pragma unroll
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
-  if (M == -INFINITY) {  // no rows at all
+  if (M == -INFINITY) {  // no rows at all: zero output and no image mass
     for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
-    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 0.f;
+    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 1.f;  // image mass = 1 - this
     return;
   }
   float z = 0.f, l = 0.f, t = 0.f;

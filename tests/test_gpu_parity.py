@@ -477,3 +477,77 @@ def test_reprofile_follows_drift(name, over, R):
     assert fo.fastocr_get_status(h) == 0
     fo.fastocr_destroy(h)
     log(f"[reprofile] {name}: picks {picks}, worst out {worst:.2e}, mean Jaccard {np.mean(jac):.3f}")
+
+
+# ---------------------------------------------------------------------------
+# degenerate sequences and the largest head layouts the ABI accepts
+# ---------------------------------------------------------------------------
+
+
+def _small_ragged(**over):
+    base = dict(batch=4, num_layers=4, focal_band=(1, 2), num_focal=2, warmup_steps=2,
+                n_img_range=(30, 60), n_prompt=(30, 40))
+    base.update(over)
+    return get_workload("7b-b16-ragged").with_overrides(**base)
+
+
+@pytest.mark.parametrize("mode", ["pruned", "full"])
+def test_degenerate_sequences(mode):
+    # one batch holding a normal sequence, a text-only one (no image
+    # tokens), an empty one (len = 0: zero output, no image mass) and one
+    # whose only text rows are the generated tokens
+    steps = 6
+    up = upload(_small_ragged(), steps=steps)
+    st = up.st
+    n = st.n_img.copy()
+    p = st.n_prompt.copy()
+    n[1], p[1] = 0, 30
+    n[2] = 0
+    p[3] = 0
+    empty = np.array([False, False, True, False])
+
+    def lens(t, n=n, p=p):
+        out = np.stack([n, n + p + t + 1], axis=1).astype(np.int32)
+        out[empty] = 0
+        return out
+
+    st.n_img = n
+    st.lens = lens
+    up.lens = torch.from_numpy(np.stack([lens(t) for t in range(steps)])).to(DEV)
+    h = fo.fastocr_create(make_config(up, mode=mode))
+    rec = run(up, h, steps)
+    assert rec.status == 0
+    assert np.all(rec.outs[:, :, 2] == 0.0)  # the empty sequence
+    if mode == "full":
+        scale = 1 / math.sqrt(up.wl.head_dim)
+        for t in range(steps):
+            for l in range(up.wl.num_layers):
+                K, V = up.kv64(l)
+                for b in range(up.wl.batch):
+                    want, _ = full_attention(up.q[l][t][b].astype(np.float64), K[b], V[b],
+                                             int(lens(t)[b, 1]), scale)
+                    check_out(rec.outs[t, l, b], want, up.wl.dtype, f"t={t} l={l} b={b}")
+        return
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(up.wl.warmup_steps, steps):
+        chk.pruned_step(t)
+    assert np.all(rec.cnts[up.wl.warmup_steps:, :, 1:3] == 0)  # no image tokens, nothing kept
+    log(f"[degenerate] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [
+    (128, 8, 128, "bf16"),  # the most query heads, a group of 16
+    (16, 1, 64, "f32"),     # one KV head serving a group of 16
+])
+def test_largest_head_layouts(hq, hkv, d, dtype):
+    wl = _small_ragged(batch=2, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                       n_img_range=(200, 700))
+    up = upload(wl, steps=6)
+    rec = run(up, fo.fastocr_create(make_config(up)), 6)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 6):
+        chk.pruned_step(t)
+    log(f"[heads {hq}/{hkv} d={d} {dtype}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
