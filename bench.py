@@ -608,6 +608,7 @@ def main():
         extra["reselection"] = {"profile_call_us": round(profile_ms * 1e3, 1), "every_R": R,
                                 "amortized_us_per_step": round(over * 1e3, 2)}
     if not args.profile_only:
+        extra["pack_image_first"] = pack_probe(torch, fo, Kd, Vd, st.n_img, stream)
         extra["platform"] = platform_probe(torch, stream)
 
     cpu = None
@@ -638,6 +639,36 @@ def main():
         **extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def pack_probe(torch, fo, Kd, Vd, n_img, stream):
+    """One-time cost of bringing a two-page layout (the image split into two
+    pages behind 20 text tokens, 12 text tokens between them) into the
+    image-first layout: every layer's K and V cache gathered once."""
+    B, Hkv, S, d = Kd[0].shape
+    maps = []
+    for b in range(B):
+        n = int(n_img[b])
+        spans = [(20, n // 2), (32 + n // 2, n - n // 2)]
+        maps.append(fo.fastocr_image_first_map(spans, S)[1])
+    row_map = torch.tensor(maps, dtype=torch.int32, device=Kd[0].device)
+    rows = torch.full((B,), S, dtype=torch.int32, device=Kd[0].device)
+    dst = torch.empty_like(Kd[0])
+    with torch.cuda.stream(stream):
+        fo.fastocr_pack_rows(Kd[0], dst, row_map, rows, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for k, v in zip(Kd, Vd):
+            fo.fastocr_pack_rows(k, dst, row_map, rows, stream=stream)
+            fo.fastocr_pack_rows(v, dst, row_map, rows, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    moved = 2 * 2 * len(Kd) * Kd[0].numel() * Kd[0].element_size()  # read + write, K and V
+    del dst
+    return {"us_all_layers": round(ms * 1e3, 1), "launches": 2 * len(Kd),
+            "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
 
 
 def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):

@@ -261,6 +261,31 @@ def fastocr_select_topk(scores, lens, tau: float, idx_out, cnt_out, stream=None)
         _dev_ptr(cnt_out, t.int32, (B,), "cnt_out", 4), ctypes.c_void_p(_stream_ptr(stream))))
 
 
+def fastocr_image_first_map(spans: Sequence[Sequence[int]], rows: int):
+    """(n_img, map): the image-first row permutation of one sequence (host)."""
+    flat = [int(x) for sp in spans for x in sp]
+    arr = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+    out = (ctypes.c_int32 * max(int(rows), 1))()
+    n = int(lib().fastocr_image_first_map(arr, len(spans), int(rows), out))
+    _check("fastocr_image_first_map", min(n, 0))
+    return n, list(out)[:int(rows)]
+
+
+def fastocr_pack_rows(src, dst, row_map, rows, status=None, stream=None) -> None:
+    """dst[b, h, i] = src[b, h, row_map[b, i]] for i < rows[b] (device tensors)."""
+    t = _torch()
+    B, Hkv, S, d = src.shape
+    dtype = {t.bfloat16: DTYPE_BF16, t.float32: DTYPE_F32}.get(src.dtype)
+    if dtype is None:
+        raise ValueError(f"src must be bfloat16 or float32, got {src.dtype}")
+    _check("fastocr_pack_rows", lib().fastocr_pack_rows(
+        _dev_ptr(src, src.dtype, (B, Hkv, S, d), "src"), _dev_ptr(dst, src.dtype, (B, Hkv, S, d), "dst"),
+        _dev_ptr(row_map, t.int32, (B, S), "row_map", 4), _dev_ptr(rows, t.int32, (B,), "rows", 4),
+        int(B), int(Hkv), int(S), int(d), dtype,
+        ctypes.c_void_p(0 if status is None else _dev_ptr(status, t.int32, (1,), "status", 4)),
+        ctypes.c_void_p(_stream_ptr(stream))))
+
+
 def fastocr_kept_count(tau: float, n_img: int) -> int:
     return int(lib().fastocr_kept_count(float(tau), int(n_img)))
 

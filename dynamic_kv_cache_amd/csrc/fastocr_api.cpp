@@ -737,6 +737,53 @@ int fastocr_reset_timing(fastocr_handle* h) {
   return FASTOCR_OK;
 }
 
+int32_t fastocr_image_first_map(const int32_t* spans, int32_t num_spans, int32_t rows, int32_t* map_out) {
+  if ((!spans && num_spans > 0) || !map_out || num_spans < 0 || rows < 0) return FASTOCR_ERR_INVALID_ARG;
+  std::vector<char> img((size_t)rows, 0);
+  int64_t n = 0, prev_end = 0;
+  for (int32_t i = 0; i < num_spans; ++i) {
+    const int64_t a = spans[2 * i], c = spans[2 * i + 1];
+    // ascending, disjoint, inside [0, rows)
+    if (a < prev_end || c < 0 || a + c > rows) return FASTOCR_ERR_INVALID_ARG;
+    for (int64_t r = a; r < a + c; ++r) img[(size_t)r] = 1;
+    n += c;
+    prev_end = a + c;
+  }
+  int32_t at = 0;
+  for (int32_t r = 0; r < rows; ++r)
+    if (img[(size_t)r]) map_out[at++] = r;
+  for (int32_t r = 0; r < rows; ++r)
+    if (!img[(size_t)r]) map_out[at++] = r;
+  return (int32_t)n;
+}
+
+int fastocr_pack_rows(const void* src, void* dst, const int32_t* row_map, const int32_t* rows,
+                      int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t head_dim,
+                      int32_t dtype, int32_t* status, void* hip_stream) {
+  if (!src || !dst || !row_map || !rows) return FASTOCR_ERR_INVALID_ARG;
+  if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1) return FASTOCR_ERR_INVALID_ARG;
+  if ((int64_t)batch * num_kv_heads > 65535) return FASTOCR_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return FASTOCR_ERR_INVALID_ARG;
+  if (dtype != FASTOCR_DTYPE_F32 && dtype != FASTOCR_DTYPE_BF16) return FASTOCR_ERR_INVALID_ARG;
+  const int row_bytes = head_dim * (dtype == FASTOCR_DTYPE_BF16 ? 2 : 4);
+  const uintptr_t bytes = (uintptr_t)batch * num_kv_heads * max_seq_len * row_bytes;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return FASTOCR_ERR_INVALID_ARG;  // overlap
+  if ((s0 | d0) % 16) return FASTOCR_ERR_INVALID_ARG;
+  PackParams p{};
+  p.src = src;
+  p.dst = dst;
+  p.map = row_map;
+  p.rows = rows;
+  p.status = status;
+  p.B = batch;
+  p.Hkv = num_kv_heads;
+  p.S = max_seq_len;
+  p.row_bytes = row_bytes;
+  const hipError_t e = launch_pack(p, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FASTOCR_OK : FASTOCR_ERR_HIP;
+}
+
 int fastocr_select_topk(const float* scores, int32_t score_stride, const int32_t* lens,
                         int32_t batch, double tau, int32_t* idx_out, int32_t idx_stride,
                         int32_t* cnt_out, void* hip_stream) {

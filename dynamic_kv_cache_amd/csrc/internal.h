@@ -100,6 +100,18 @@ struct TopkParams {
                           // read and cleared to zero
 };
 
+// Row gather of a cache: dst[b, h, i] = src[b, h, map[b, i]] for i < rows_b.
+struct PackParams {
+  const void* src;        // [B, Hkv, S, row_bytes]
+  void* dst;              // same shape; must not overlap src
+  const int32_t* map;     // [B, S] source row of each destination row
+  const int32_t* rows;    // [B] destination rows to fill (clamped to [0, S])
+  int32_t* status;        // may be null: FASTOCR_FLAG_INDEX_CLAMPED on a map entry outside [0, S)
+  int32_t B, Hkv, S, row_bytes;  // row_bytes a multiple of 16
+};
+constexpr int kPackThreads = 256;
+constexpr int kPackRowsPerBlock = 64;
+
 // Optional timing: events recorded by the dispatch itself (start: when the
 // dispatch is processed; stop: when the kernel completes).
 struct LaunchTiming {
@@ -113,5 +125,6 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream
                         const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream,
                        const LaunchTiming& timing = LaunchTiming{});
+hipError_t launch_pack(const PackParams& p, hipStream_t stream);
 
 }  // namespace fastocr

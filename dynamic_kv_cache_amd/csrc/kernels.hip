@@ -1296,6 +1296,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// row gather (image-first packing of a multi-span cache)
+// ---------------------------------------------------------------------------
+
+// One workgroup per kPackRowsPerBlock destination rows of one (sequence, KV
+// head): consecutive threads move consecutive 16-byte pieces of a row, so
+// both the source row and the destination rows are read and written
+// contiguously.
+__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(PackParams p) {
+  const int pair = blockIdx.y;
+  const int b = pair / p.Hkv;
+  const int rows = min(max(p.rows[b], 0), p.S);
+  const int i0 = blockIdx.x * kPackRowsPerBlock;
+  if (i0 >= rows) return;
+  const int pieces = p.row_bytes / 16;
+  const int n = min(kPackRowsPerBlock, rows - i0) * pieces;
+  const size_t base = (size_t)pair * p.S;
+  const char* src = reinterpret_cast<const char*>(p.src);
+  char* dst = reinterpret_cast<char*>(p.dst);
+  bool bad = false;
+  for (int t = threadIdx.x; t < n; t += kPackThreads) {
+    const int i = i0 + t / pieces;
+    const int c = t - (t / pieces) * pieces;
+    const int s0 = p.map[(size_t)b * p.S + i];
+    const int s = min(max(s0, 0), p.S - 1);
+    bad |= s != s0;
+    const uint4 v = reinterpret_cast<const uint4*>(src + (base + s) * p.row_bytes)[c];
+    reinterpret_cast<uint4*>(dst + (base + i) * p.row_bytes)[c] = v;
+  }
+  if (bad && p.status) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1361,6 +1393,12 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream, const LaunchTimi
   if (per <= 8) return launch(topk_kernel<8>, grid, block, stream, timing, p);
   if (per <= kTopkRegKeys) return launch(topk_kernel<kTopkRegKeys>, grid, block, stream, timing, p);
   return launch(topk_kernel<0>, grid, block, stream, timing, p);
+}
+
+hipError_t launch_pack(const PackParams& p, hipStream_t stream) {
+  const dim3 grid((p.S + kPackRowsPerBlock - 1) / kPackRowsPerBlock, p.B * p.Hkv), block(kPackThreads);
+  pack_rows_kernel<<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace fastocr

@@ -280,6 +280,41 @@ int fastocr_select_topk(const float* scores, int32_t score_stride, const int32_t
                         int32_t batch, double tau, int32_t* idx_out, int32_t idx_stride,
                         int32_t* cnt_out, void* hip_stream);
 
+/* ---- multi-span image layouts -------------------------------------------- */
+
+/* The library's kernels take every sequence's image tokens as cache rows
+ * [0, n_img_b).  A document whose image sits elsewhere in the cache (behind
+ * a text prefix, or as several pages or images with text between them) is
+ * brought into that layout once, after prefill, by a row permutation of each
+ * layer's cache: softmax attention does not depend on the order of the keys
+ * (positions are already encoded in the keys and values), so every output
+ * of the method is unchanged (Method: only the set of attended tokens
+ * changes).  Image token j of the method is then the j-th image row in
+ * ascending row order, and the kept set is chosen over the tokens of all
+ * spans together.  Rows decoded later are appended at row len_b - 1 as
+ * before (the permutation leaves rows at and after the last prefill row in
+ * place). */
+
+/* fastocr_image_first_map: the permutation for one sequence.  spans: host
+ * int32 [num_spans, 2] of (first row, row count), ascending and disjoint,
+ * inside [0, rows).  map_out: host int32 [rows] receives the source row of
+ * every destination row: the image rows in ascending order, then every other
+ * row in ascending order.  Returns n_img (the summed counts), or
+ * FASTOCR_ERR_INVALID_ARG for unsorted, overlapping or out-of-range spans. */
+int32_t fastocr_image_first_map(const int32_t* spans, int32_t num_spans, int32_t rows, int32_t* map_out);
+
+/* fastocr_pack_rows: dst[b, h, i, :] = src[b, h, row_map[b * S + i], :] for
+ * every KV head h and i < rows_b.  src, dst: device [B, Hkv, S, head_dim] of
+ * dtype, 16-byte aligned, not overlapping (INVALID_ARG otherwise); row_map:
+ * device int32 [B, S]; rows: device int32 [B] (clamped to [0, S]); rows of
+ * dst at or past rows_b are not written.  A map entry outside [0, S) is
+ * clamped and, when status (device int32, may be NULL) is given, latches
+ * FASTOCR_FLAG_INDEX_CLAMPED there.  hip_stream: hipStream_t.  Asynchronous.
+ * Errors: INVALID_ARG, HIP. */
+int fastocr_pack_rows(const void* src, void* dst, const int32_t* row_map, const int32_t* rows,
+                      int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t head_dim,
+                      int32_t dtype, int32_t* status, void* hip_stream);
+
 /* Host helpers (no device use). */
 /* k = clamp(ceil(tau*n - 1e-9), 1, n) for n > 0; 0 for n <= 0; negative
  * FASTOCR_ERR_INVALID_ARG if tau is outside (0, 1]. */

@@ -10,6 +10,7 @@ from .fastocr_oracle import (  # noqa: F401
     attention_probs,
     full_attention,
     sparse_attention,
+    image_rows_of,
     image_scores,
     image_mass,
     kept_count,

@@ -121,35 +121,50 @@ def full_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int,
     return _weighted_values(p, V, rows), p
 
 
+def image_rows_of(spans: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """Cache rows of the image tokens of a sequence whose image occupies the
+    given (start, count) spans (several pages or images), in ascending row
+    order: image token j of the method is row image_rows_of(spans)[j]."""
+    rows = [np.arange(a, a + c, dtype=np.int64) for a, c in spans]
+    return np.sort(np.concatenate(rows)) if rows else np.zeros(0, dtype=np.int64)
+
+
 def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
                      selected: Sequence[int], n_img: int, length: int,
-                     scale: float) -> np.ndarray:
+                     scale: float, image_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Non-focal decode attention: the selected image tokens plus all text rows.
 
     Non-focal layers attend only to the pruned token set (Method / 1.
     Focal-Guided Pruning / Cross-Layer Propagation); pruning applies to image
     tokens [0, n_img), and every prompt/generated row [n_img, length) is kept.
+    With ``image_rows`` the image tokens are those cache rows instead (image
+    token j at row image_rows[j]) and every other row below ``length`` is text.
     Returns out [Hq, d].
     """
-    rows = np.concatenate([np.sort(np.asarray(selected, dtype=np.int64)),
-                           np.arange(n_img, length, dtype=np.int64)])
+    sel = np.sort(np.asarray(selected, dtype=np.int64))
+    if image_rows is None:
+        rows = np.concatenate([sel, np.arange(n_img, length, dtype=np.int64)])
+    else:
+        text = np.setdiff1d(np.arange(length, dtype=np.int64), image_rows)
+        rows = np.concatenate([np.asarray(image_rows, dtype=np.int64)[sel], text])
     p = attention_probs(q, K, rows, scale)
     return _weighted_values(p, V, rows)
 
 
-def image_scores(p: np.ndarray, n_img: int) -> np.ndarray:
+def image_scores(p: np.ndarray, n_img: int, image_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Per-image-token attention score: probability summed over query heads.
 
     Focal layers pick the "top-attended" image tokens (Method / 1.
     Focal-Guided Pruning / Cross-Layer Propagation); the head sum is the
-    statistic.  p is [Hq, length] from a full-cache attention.
+    statistic.  p is [Hq, length] from a full-cache attention; the image
+    tokens are rows [0, n_img), or the rows ``image_rows`` when given.
     """
-    return p[:, :n_img].sum(axis=0)
+    return (p[:, :n_img] if image_rows is None else p[:, image_rows]).sum(axis=0)
 
 
-def image_mass(p: np.ndarray, n_img: int) -> np.ndarray:
+def image_mass(p: np.ndarray, n_img: int, image_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Per-head attention mass on image tokens, [Hq] (Focal Layer Selection)."""
-    return p[:, :n_img].sum(axis=1)
+    return (p[:, :n_img] if image_rows is None else p[:, image_rows]).sum(axis=1)
 
 
 def kept_count(tau: float, n_img: int) -> int:
@@ -222,7 +237,8 @@ class DecodeOracle:
     def __init__(self, *, num_layers: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, tau: float, num_focal: int, warmup_steps: int,
                  scale: Optional[float] = None, full_mode: bool = False,
-                 reprofile_every: int = 0):
+                 reprofile_every: int = 0,
+                 spans: Optional[Sequence[Sequence[Tuple[int, int]]]] = None):
         self.L = num_layers
         self.Hq = num_q_heads
         self.Hkv = num_kv_heads
@@ -233,6 +249,9 @@ class DecodeOracle:
         self.scale = (1.0 / math.sqrt(head_dim)) if not scale else float(scale)
         self.full_mode = full_mode
         self.reprofile_every = reprofile_every
+        # image tokens of sequence b at the rows of its spans (None: rows
+        # [0, n_img)), fixed for the run like the image-token counts
+        self.image_rows = None if spans is None else [image_rows_of(sp) for sp in spans]
         self.mass: Dict[int, List[np.ndarray]] = {l: [] for l in range(num_layers)}
         self.warm_scores: Dict[int, List[np.ndarray]] = {}
         self.ratios: Optional[np.ndarray] = None
@@ -286,7 +305,7 @@ class DecodeOracle:
                 for b in range(B):
                     n, length = int(lens[b, 0]), int(lens[b, 1])
                     out[b], p = full_attention(q[b], K[b], V[b], length, self.scale)
-                    s = image_scores(p, n)
+                    s = image_scores(p, n, self._rows(b, n))
                     current[b] = select_top(s, kept_count(self.tau, n))
                     rec.scores[l].append(s)
                     rec.sets[l].append(current[b].copy())
@@ -294,7 +313,8 @@ class DecodeOracle:
                 rec.used_sets[l] = [c.copy() for c in current]
                 for b in range(B):
                     n, length = int(lens[b, 0]), int(lens[b, 1])
-                    out[b] = sparse_attention(q[b], K[b], V[b], current[b], n, length, self.scale)
+                    out[b] = sparse_attention(q[b], K[b], V[b], current[b], n, length, self.scale,
+                                              self._rows(b, n))
             rec.outs.append(out)
         self.f_last = current
         self.pruned_since += 1
@@ -304,6 +324,12 @@ class DecodeOracle:
             self.mass = {l: [] for l in range(self.L)}
             self.warm_scores = {}
         return rec
+
+    def _rows(self, b: int, n: int) -> Optional[np.ndarray]:
+        if self.image_rows is None:
+            return None
+        assert len(self.image_rows[b]) == n, "lens must count the spans' image tokens"
+        return self.image_rows[b]
 
     def _full_step(self, t, q_of, kv_of, lens, phase, keep_scores=False) -> StepRecord:
         B = lens.shape[0]
@@ -316,8 +342,8 @@ class DecodeOracle:
             for b in range(B):
                 n, length = int(lens[b, 0]), int(lens[b, 1])
                 out[b], p = full_attention(q[b], K[b], V[b], length, self.scale)
-                masses.append(image_mass(p, n))
-                scores.append(image_scores(p, n))
+                masses.append(image_mass(p, n, self._rows(b, n)))
+                scores.append(image_scores(p, n, self._rows(b, n)))
             if phase == "warmup":
                 self.mass[l].append(np.stack(masses))
                 if keep_scores:

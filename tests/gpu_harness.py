@@ -179,14 +179,17 @@ def check_scores(got: np.ndarray, want: np.ndarray, what: str) -> None:
 class Checker:
     """Replays the method on the CPU next to the GPU records."""
 
-    def __init__(self, up: Uploaded, rec: Records, tau: Optional[float] = None):
+    def __init__(self, up: Uploaded, rec: Records, tau: Optional[float] = None, spans=None):
+        """spans: per sequence (start, count) of its image pages in up's
+        (host) cache layout; the GPU ran on the image-first permuted cache."""
         self.up, self.rec = up, rec
         wl = up.wl
         self.tau = wl.tau if tau is None else tau
         self.scale = 1.0 / math.sqrt(wl.head_dim)
         self.oracle = DecodeOracle(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads,
                                    num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, tau=self.tau,
-                                   num_focal=wl.num_focal, warmup_steps=wl.warmup_steps)
+                                   num_focal=wl.num_focal, warmup_steps=wl.warmup_steps, spans=spans)
+        self.rows = (lambda b: None) if spans is None else (lambda b: self.oracle.image_rows[b])
         self.jaccard: List[float] = []
         self.worst_out = 0.0
 
@@ -227,7 +230,7 @@ class Checker:
                 n, length = int(lens[b, 0]), int(lens[b, 1])
                 if l in focal:
                     out, p = full_attention(ql[b], K[b], V[b], length, self.scale)
-                    s = image_scores(p, n)
+                    s = image_scores(p, n, self.rows(b))
                     slot = focal.index(l)
                     check_scores(rec.scores[t, slot, b, :n], s, f"scores t={t} l={l} b={b}")
                     c = int(rec.cnts[t, l + 1, b])
@@ -236,7 +239,7 @@ class Checker:
                 else:
                     c = int(rec.cnts[t, l, b])
                     used = rec.sets[t, l, b, :c]
-                    out = sparse_attention(ql[b], K[b], V[b], used, n, length, self.scale)
+                    out = sparse_attention(ql[b], K[b], V[b], used, n, length, self.scale, self.rows(b))
                 self.worst_out = max(self.worst_out, check_out(
                     rec.outs[t, l, b], out, wl.dtype, f"out t={t} l={l} b={b}"))
         # the warm start of step t+1 is the set after the deepest focal layer

@@ -133,3 +133,37 @@ def test_create_without_device_reports_hip_error():
 def test_error_strings():
     for code in (fo.OK, fo.ERR_INVALID_ARG, fo.ERR_STATE, fo.ERR_HIP, fo.ERR_OOM, 7):
         assert isinstance(fo.fastocr_error_string(code), str)
+
+
+def test_image_first_map_matches_definition():
+    # image rows ascending, then every other row ascending
+    from oracle import image_rows_of
+    rng = np.random.default_rng(3)
+    for trial in range(300):
+        rows = int(rng.integers(1, 200))
+        cuts = np.sort(rng.choice(rows + 1, size=min(2 * int(rng.integers(0, 5)), rows + 1 - rows % 2 - 1),
+                                  replace=False))
+        spans = [(int(a), int(b - a)) for a, b in zip(cuts[0::2], cuts[1::2])]
+        n, m = fo.fastocr_image_first_map(spans, rows)
+        img = image_rows_of(spans)
+        want = np.concatenate([img, np.setdiff1d(np.arange(rows), img)])
+        assert n == len(img) and m == list(want), (spans, rows)
+
+
+def test_image_first_map_rejects_bad_spans():
+    for spans, rows in [([(5, 4), (2, 1)], 20), ([(0, 5), (4, 2)], 20), ([(18, 4)], 20), ([(3, -1)], 20)]:
+        with pytest.raises(fo.FastOCRError):
+            fo.fastocr_image_first_map(spans, rows)
+
+
+def test_pack_rows_rejects_bad_arguments():
+    lib = fo.lib()
+    i32 = ctypes.c_void_p(0x2000)
+    # null pointers, bad head_dim, overlapping buffers (the pointers are
+    # checked on the host and never dereferenced)
+    assert lib.fastocr_pack_rows(None, None, None, None, 1, 1, 8, 64, 1, None, None) == fo.ERR_INVALID_ARG
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100000 + 512)
+    assert lib.fastocr_pack_rows(a, b, i32, i32, 1, 1, 8, 64, 1, None, None) == fo.ERR_INVALID_ARG
+    c = ctypes.c_void_p(0x200000)
+    assert lib.fastocr_pack_rows(a, c, i32, i32, 1, 1, 8, 96, 1, None, None) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_pack_rows(a, c, i32, i32, 1, 1, 8, 64, 7, None, None) == fo.ERR_INVALID_ARG

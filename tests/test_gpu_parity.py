@@ -551,3 +551,73 @@ def test_largest_head_layouts(hq, hkv, d, dtype):
     for t in range(wl.warmup_steps, 6):
         chk.pruned_step(t)
     log(f"[heads {hq}/{hkv} d={d} {dtype}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# image tokens in several pages with text around them
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name,over,steps", [
+    # two 8x8 pages behind 12 text tokens with 6 between them
+    ("tiny-fp32", dict(batch=2, grid=(16, 8), pages=2, page_text=(12, 6), n_prompt=(38, 38)), None),
+    # two 40x80 pages behind 20 text tokens with 12 between them, bf16
+    ("7b-b1", dict(pages=2, page_text=(20, 12), n_prompt=(96, 96), num_layers=8, focal_band=(3, 5),
+                   num_focal=2, warmup_steps=3), 12),
+])
+def test_multi_page_layout_packed(name, over, steps):
+    import dataclasses
+    wl = get_workload(name).with_overrides(**over)
+    up = upload(wl, steps=steps)
+    wl, st = up.wl, up.st
+    B, S = wl.batch, st.max_seq_len
+    maps = []
+    for b in range(B):
+        n, m = fo.fastocr_image_first_map(st.spans[b], S)
+        assert n == int(st.n_img[b])
+        maps.append(m)
+    row_map = torch.tensor(maps, dtype=torch.int32, device=DEV)
+    rows = torch.full((B,), S, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Kp = [torch.empty_like(k) for k in up.Kd]
+    Vp = [torch.empty_like(v) for v in up.Vd]
+    for l in range(wl.num_layers):
+        fo.fastocr_pack_rows(up.Kd[l], Kp[l], row_map, rows, status)
+        fo.fastocr_pack_rows(up.Vd[l], Vp[l], row_map, rows, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    perm = torch.tensor(maps, dtype=torch.long, device=DEV)
+    for l in range(wl.num_layers):  # a pure row gather: bit-exact
+        for b in range(B):
+            assert torch.equal(Kp[l][b], up.Kd[l][b][:, perm[b]]), (l, b)
+            assert torch.equal(Vp[l][b], up.Vd[l][b][:, perm[b]]), (l, b)
+    # the method on the packed cache against the oracle on the page layout
+    packed = dataclasses.replace(up, Kd=Kp, Vd=Vp)
+    T = wl.steps
+    rec = run(packed, fo.fastocr_create(make_config(packed)), T)
+    assert rec.status == 0
+    chk = Checker(up, rec, spans=st.spans)
+    chk.warmup()
+    for t in range(wl.warmup_steps, T):
+        chk.pruned_step(t)
+    log(f"[pages] {name}: focal {rec.focal}, worst out {chk.worst_out:.2e}, "
+        f"mean Jaccard {np.mean(chk.jaccard):.3f}")
+
+
+def test_pack_rows_partial_and_clamped():
+    # rows past rows_b are left alone; a map entry outside [0, S) is clamped
+    # and flagged
+    B, Hkv, S, d = 2, 3, 40, 64
+    src = torch.randn((B, Hkv, S, d), device=DEV).to(torch.bfloat16)
+    dst = torch.zeros_like(src)
+    m = torch.arange(S, dtype=torch.int32, device=DEV).flip(0).repeat(B, 1).contiguous()
+    m[1, 3] = S + 7
+    rows = torch.tensor([S, 10], dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    fo.fastocr_pack_rows(src, dst, m, rows, status)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[0], src[0].flip(1))
+    want = src[1][:, m[1, :10].clamp(0, S - 1).long()]
+    assert torch.equal(dst[1][:, :10], want)
+    assert torch.count_nonzero(dst[1][:, 10:]) == 0
+    assert int(status.item()) & fo.FLAG_INDEX_CLAMPED

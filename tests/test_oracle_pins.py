@@ -408,6 +408,93 @@ def test_reprofile_pin_catches_pooled_windows():
         assert [list(c) for _, c in orc.profiles][2] == [0, 2]
 
 
+
+# ---------------------------------------------------------------------------
+# image tokens in several spans (pages with text around them)
+# ---------------------------------------------------------------------------
+
+
+def _two_page_inputs():
+    wl = get_workload("tiny-fp32").with_overrides(batch=2, grid=(16, 8), pages=2, page_text=(12, 6),
+                                                  n_prompt=(38, 38))
+    st, kv, qs = _tiny_inputs(wl)
+    return wl, st, kv, qs
+
+
+def _image_first(st, b, S):
+    img = st.image_rows[b]
+    return np.concatenate([img, np.setdiff1d(np.arange(S), img)])
+
+
+def test_spans_attention_invariant_under_image_first_permutation():
+    # softmax attention does not depend on key order: permuting the cache rows
+    # image-first leaves outputs, probabilities per token, scores and masses
+    # unchanged (closed form), and rows [0, n) of the permuted cache are the
+    # image tokens in span order
+    wl, st, kv, qs = _two_page_inputs()
+    scale = 1 / math.sqrt(wl.head_dim)
+    t = 3
+    lens = st.lens(t)
+    for b in range(wl.batch):
+        n, length = int(lens[b, 0]), int(lens[b, 1])
+        perm = _image_first(st, b, st.max_seq_len)
+        K, V = kv[0][0][b], kv[0][1][b]
+        o1, p1 = ofo.full_attention(qs[0][t][b], K, V, length, scale)
+        o2, p2 = ofo.full_attention(qs[0][t][b], K[:, perm], V[:, perm], length, scale)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(p1[:, perm[:length]], p2, rtol=0, atol=1e-15)
+        img = st.image_rows[b]
+        np.testing.assert_allclose(ofo.image_scores(p1, n, img), ofo.image_scores(p2, n), rtol=1e-12)
+        np.testing.assert_allclose(ofo.image_mass(p1, n, img), ofo.image_mass(p2, n), rtol=1e-12)
+        sel = np.array([0, 5, 70, 127])
+        s1 = ofo.sparse_attention(qs[0][t][b], K, V, sel, n, length, scale, img)
+        s2 = ofo.sparse_attention(qs[0][t][b], K[:, perm], V[:, perm], sel, n, length, scale)
+        np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-12)
+
+
+def test_spans_sparse_matches_masked_sdpa():
+    import torch
+    wl, st, kv, qs = _two_page_inputs()
+    scale = 1 / math.sqrt(wl.head_dim)
+    t, b = 5, 1
+    n, length = (int(x) for x in st.lens(t)[b])
+    img = st.image_rows[b]
+    sel = np.array([1, 2, 63, 64, 100])
+    allowed = np.zeros(length, dtype=bool)
+    allowed[img[sel]] = True
+    text = np.ones(length, dtype=bool)
+    text[img] = False
+    allowed |= text
+    q = torch.from_numpy(qs[1][t][b])[:, None, :]  # [Hq, 1, d]
+    g = wl.num_q_heads // wl.num_kv_heads
+    K = torch.from_numpy(kv[1][0][b][:, :length]).repeat_interleave(g, dim=0)
+    V = torch.from_numpy(kv[1][1][b][:, :length]).repeat_interleave(g, dim=0)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        q, K, V, attn_mask=torch.from_numpy(allowed)[None, None, :], scale=scale)[:, 0].numpy()
+    got = ofo.sparse_attention(qs[1][t][b], kv[1][0][b], kv[1][1][b], sel, n, length, scale, img)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_spans_trajectory_equals_image_first_trajectory():
+    # the whole procedure on the page layout (image tokens at their span
+    # rows) equals the procedure on the image-first permuted cache
+    wl, st, kv, qs = _two_page_inputs()
+    S = st.max_seq_len
+    perms = [_image_first(st, b, S) for b in range(wl.batch)]
+    kv_p = [(np.stack([k[b][:, perms[b]] for b in range(wl.batch)]),
+             np.stack([v[b][:, perms[b]] for b in range(wl.batch)])) for k, v in kv]
+    a = _oracle_for(wl, spans=st.spans)
+    p = _oracle_for(wl)
+    for t in range(wl.steps):
+        ra = a.step(t, lambda l: qs[l][t], lambda l: kv[l], st.lens(t))
+        rp = p.step(t, lambda l: qs[l][t], lambda l: kv_p[l], st.lens(t))
+        for x, y in zip(ra.outs, rp.outs):
+            np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+        for l in ra.sets:
+            assert all(np.array_equal(u, v) for u, v in zip(ra.sets[l], rp.sets[l]))
+    assert list(a.focal) == list(p.focal) == [1, 3]
+
+
 def _mut_gqa_modulo(h, Hq, Hkv):
     return h % Hkv
 

@@ -92,6 +92,13 @@ class Workload:
     # and the layers that had it before take the low alpha (a focal set that
     # drifts during decoding); None = no drift
     drift: Optional[Tuple[int, Tuple[int, ...]]] = None
+    # multi-page layout: the image (grid rows split evenly into `pages`
+    # pages) sits in the cache behind page_text[0] text tokens, with
+    # page_text[1] text tokens between pages; n_prompt counts every text
+    # token before decoding (these included).  pages = 1 and (0, 0): the
+    # image first, then the prompt.
+    pages: int = 1
+    page_text: Tuple[int, int] = (0, 0)
 
     @property
     def group(self) -> int:
@@ -194,6 +201,12 @@ class Structure:
     windows: List[List[np.ndarray]] = field(default_factory=list)  # [B][T] token ids
     alpha_late: Optional[np.ndarray] = None  # [L] alpha from drift_step on (drifting workloads)
     drift_step: int = 0
+    spans: Optional[List[List[Tuple[int, int]]]] = None  # [B] (start, count) of each page
+    image_rows: Optional[List[np.ndarray]] = None  # [B] cache row of image token j
+
+    def image_row(self, b: int, j: np.ndarray) -> np.ndarray:
+        """Cache rows of image tokens j of sequence b."""
+        return np.asarray(j) if self.image_rows is None else self.image_rows[b][np.asarray(j)]
 
     def alpha_at(self, l: int, steps) -> np.ndarray:
         """[len(steps)] float32: query alignment of layer l at each step."""
@@ -295,6 +308,16 @@ def make_structure(wl: Workload) -> Structure:
                    alpha_late=alpha_late, drift_step=0 if wl.drift is None else int(wl.drift[0]))
     st.windows = [[_window_tokens(centre[t, b], int(n_img[b]), int(grid_w[b]), wl.window)
                    for t in range(T)] for b in range(B)]
+    if wl.pages > 1 or wl.page_text != (0, 0):
+        pre, gap = wl.page_text
+        st.spans, st.image_rows = [], []
+        for b in range(B):
+            m = int(n_img[b]) // wl.pages
+            assert m * wl.pages == int(n_img[b]), "pages must split the image evenly"
+            assert int(n_prompt[b]) >= pre + gap * (wl.pages - 1), "n_prompt counts the text around pages"
+            sp = [(pre + i * (m + gap), m) for i in range(wl.pages)]
+            st.spans.append(sp)
+            st.image_rows.append(np.concatenate([np.arange(a, a + c) for a, c in sp]).astype(np.int64))
     return st
 
 
@@ -362,7 +385,7 @@ class Generator:
             for i, w in enumerate(wins):
                 idx[i, :len(w)] = w
                 wgt[i, :len(w)] = 1.0 / len(w)
-            gathered = K[b][:, idx, :]  # [Hkv, S, wmax, d]
+            gathered = K[b][:, st.image_row(b, idx), :]  # [Hkv, S, wmax, d]
             mean = np.einsum("hswd,sw->shd", gathered, wgt, optimize=True)  # [S, Hkv, d]
             mean_q = np.repeat(mean, g, axis=1)  # [S, Hq, d], head h -> kv head h // g
             q[:, b] = st.alpha_at(l, steps)[:, None, None] * mean_q + np.float32(wl.sigma) * eps[:, b]
@@ -429,7 +452,7 @@ class DeviceGenerator:
             for i, w in enumerate(wins):
                 idx[i, :len(w)] = w
                 wgt[i, :len(w)] = 1.0 / len(w)
-            idx_t = torch.from_numpy(idx).to(self.device)
+            idx_t = torch.from_numpy(st.image_row(b, idx)).to(self.device)
             wgt_t = torch.from_numpy(wgt).to(self.device)
             Kb = K[b].float()  # [Hkv, S, d]
             gathered = Kb[:, idx_t.reshape(-1)].reshape(Hkv, len(steps), wmax, d)
