@@ -61,7 +61,8 @@ def parse():
                     help="end with a 256 MiB device-to-device copy, the reference kernel that "
                          "scales hardware byte counters")
     ap.add_argument("--pmc-summary", default=None, nargs="+", metavar="DIR",
-                    help="summarise rocprofv3 counter CSVs under the DIRs and exit (no GPU use)")
+                    help="summarise rocprofv3 counter CSVs under the DIRs (and the algorithmic bytes in a "
+                         "profiled run's output file, if given) and exit (no GPU use)")
     ap.add_argument("--trace-summary", default=None, nargs="+", metavar="ARG",
                     help="DIR COMMAND [BENCH_JSON]: summarise a rocprofv3 kernel trace under DIR made by "
                          "COMMAND, beside the event averages of BENCH_JSON, and exit")
@@ -101,13 +102,22 @@ def kernel_class(name):
     return None
 
 
-def pmc_summary(directories):
+def pmc_summary(args):
     """HBM bytes per dispatch of each library kernel from rocprofv3 counter
     CSVs (one directory per counter pass).  Each counter is scaled by what
     it reads for the calibration kernel (an int64 add that reads and writes
-    CAL_BYTES once each)."""
+    CAL_BYTES once each).  A file argument is the output of one of the
+    profiled runs: its JSON line gives the algorithmic bytes per launch of
+    that run's dispatches."""
     import csv
     import glob
+    directories = [a for a in args if os.path.isdir(a)]
+    run_alg = {}
+    for a in args:
+        if os.path.isfile(a):
+            for line in open(a):
+                if line.startswith("{") and "alg_bytes_per_launch_run" in line:
+                    run_alg = json.loads(line)["alg_bytes_per_launch_run"]
     acc = {}
     for directory in directories:
         for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
@@ -134,6 +144,8 @@ def pmc_summary(directories):
         if all(c in ctrs and c in scale for c in ("FETCH_SIZE", "WRITE_SIZE")):
             hbm = sum(ctrs[c][0] * scale[c] * 1024 for c in ("FETCH_SIZE", "WRITE_SIZE"))
             print(f"{cls}.hbm_bytes_per_launch: {hbm:.0f}")
+        if cls in run_alg:
+            print(f"{cls}.run_alg_bytes_per_launch: {run_alg[cls]}  # K/V rows the same run's dispatches read")
 
 
 def trace_summary(directory, command, bench_json=None):
@@ -170,12 +182,13 @@ def trace_summary(directory, command, bench_json=None):
 
 
 def read_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/pmc_<workload>.txt), or None when there is none or the kernels
+    """(HBM bytes per launch of `kernel`, algorithmic bytes per launch of the
+    same counter run's dispatches) from the committed counter summary
+    (profiles/pmc_<workload>.txt); None when there is none or the kernels
     changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     vals = {}
     for line in open(path):
         line = line.split("#", 1)[0]
@@ -183,11 +196,14 @@ def read_traffic(kernel, workload):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("library_source_sha256_16") != library_source_digest():
-        return None
-    try:
-        return float(vals[f"{kernel}.hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return None, None
+
+    def num(key):
+        try:
+            return float(vals[key])
+        except (KeyError, ValueError):
+            return None
+    return num(f"{kernel}.hbm_bytes_per_launch"), num(f"{kernel}.run_alg_bytes_per_launch")
 
 
 def main():
@@ -227,13 +243,18 @@ def main():
     # interleaved, so every phase sees short and long text alike.
     do_scrub = args.scrub_mb > 0 and not args.profile_only and not args.no_graph
     do_append = not args.no_append and not args.profile_only and not args.no_graph
-    phases = ["graph", "events"] + (["scrub"] if do_scrub else []) + (
-        ["append_separate", "append_fused"] if do_append else [])
+    # the schedule does not depend on which phases run, so a profiler run of
+    # a subset times the same decode steps as the full run
+    phases = ["graph", "events", "scrub", "append_separate", "append_fused"]
     t_timed = w + W
     assert t_timed < wl.steps, f"--warmup too large for {wl.steps} decode steps"
     span, n_log = wl.steps - t_timed, len(phases) * K
     phase_steps = {ph: [t_timed + ((k * len(phases) + i) * span) // n_log for k in range(K)]
                    for i, ph in enumerate(phases)}
+    if not do_scrub:
+        del phase_steps["scrub"]
+    if not do_append:
+        del phase_steps["append_separate"], phase_steps["append_fused"]
     used = sorted(set(range(t_timed)).union(*phase_steps.values()))
     slot = {t: i for i, t in enumerate(used)}
     io = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -510,6 +531,26 @@ def main():
     bytes_pruned = R * (C * rows_focal + (L - C) * rows_sparse)
     bytes_full = R * L * rows_focal
 
+    def run_alg_bytes():
+        """Average algorithmic K/V bytes per launch of each split class over
+        every dispatch of a profile-only run (warm-up, untimed, graph-phase
+        and event-phase steps of the pruned handle), for comparison with
+        hardware counters taken over the same run."""
+        pruned_steps = list(range(w, t_timed)) + phase_steps["graph"] + phase_steps["events"]
+        n = {"full_split": [0, 0.0], "focal_split": [0, 0.0], "sparse_split": [0, 0.0]}
+        for t in range(w):
+            n["full_split"][0] += L
+            n["full_split"][1] += L * R * float(st.lens(t)[:, 1].sum())
+        for t in pruned_steps:
+            ln = st.lens(t)[:, 1].astype(np.int64)
+            n["focal_split"][0] += C
+            n["focal_split"][1] += C * R * float(ln.sum())
+            other = "full_split" if wl.tau >= 1.0 else "sparse_split"
+            rows = ln.sum() if wl.tau >= 1.0 else (kb + ln - n_img).sum()
+            n[other][0] += L - C
+            n[other][1] += (L - C) * R * float(rows)
+        return {k: int(v[1] / v[0]) for k, v in n.items() if v[0]}
+
     def per_step(r):
         """Per kernel class: average launch time and launches per step."""
         out = {}
@@ -533,10 +574,13 @@ def main():
     roofline = None
     if per_launch_bytes is not None:
         achieved = per_launch_bytes / (dom_avg_ms * 1e-3) / 1e9
+        traffic, traffic_alg = read_traffic(dom, wl.name)
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic(dom, wl.name), "avg_launch_us": round(dom_avg_ms * 1e3, 3),
-                    "bytes_per_launch": int(per_launch_bytes)}
+                    "traffic": traffic, "avg_launch_us": round(dom_avg_ms * 1e3, 3),
+                    "bytes_per_launch": int(per_launch_bytes),
+                    # the algorithmic bytes per launch of the counter run's own dispatches
+                    "traffic_run_alg_bytes": traffic_alg}
     def kernel_table(kr):
         """Per kernel class: launch time, launches and time per step; for the
         split kernels also the algorithmic K/V bytes per launch and the rate."""
@@ -615,6 +659,8 @@ def main():
     if args.cpu_seconds > 0 and not args.profile_only:
         cpu = cpu_baseline(wl, st, Kd, Vd, Qall, used, focal, args.cpu_seconds)
 
+    if args.profile_only:
+        extra["alg_bytes_per_launch_run"] = run_alg_bytes()
     line = {
         "metric": "decode-step attention us (all layers) + HBM GB/s, tau=0.05 vs full attention",
         "value": round(value_us, 2),

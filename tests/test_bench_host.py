@@ -54,7 +54,9 @@ def test_pmc_summary_scales_by_calibration(tmp_path, capsys):
         {"Kernel_Name": add, "Counter_Name": "WRITE_SIZE", "Counter_Value": cal},
         {"Kernel_Name": split, "Counter_Name": "WRITE_SIZE", "Counter_Value": 10.0},
     ])
-    bench.pmc_summary([str(fetch), str(write)])
+    log = tmp_path / "run.log"
+    log.write_text('[bench] noise\n{"value": 1.0, "alg_bytes_per_launch_run": {"sparse_split": 4321}}\n')
+    bench.pmc_summary([str(fetch), str(write), str(log)])
     out = capsys.readouterr().out
     vals = dict(line.split("#")[0].split(":", 1) for line in out.splitlines() if ":" in line)
     vals = {k.strip(): v.strip() for k, v in vals.items()}
@@ -63,19 +65,21 @@ def test_pmc_summary_scales_by_calibration(tmp_path, capsys):
     # (mean 200 KiB fetched x 2 + 10 KiB written) per launch
     assert float(vals["sparse_split.hbm_bytes_per_launch"]) == pytest.approx((200 * 2 + 10) * 1024, rel=1e-6)
     assert vals["library_source_sha256_16"] == bench.library_source_digest()
+    assert int(vals["sparse_split.run_alg_bytes_per_launch"]) == 4321
 
 
 def test_read_traffic_requires_matching_sources(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    text = "# header: with a colon\nlibrary_source_sha256_16: {}\nsparse_split.hbm_bytes_per_launch: 1234  # note\n"
+    text = ("# header: with a colon\nlibrary_source_sha256_16: {}\nsparse_split.hbm_bytes_per_launch: 1234  # note\n"
+            "sparse_split.run_alg_bytes_per_launch: 1200  # rows\n")
     (prof / "pmc_w.txt").write_text(text.format(bench.library_source_digest()))
-    assert bench.read_traffic("sparse_split", "w") == 1234.0
-    assert bench.read_traffic("merge", "w") is None
-    assert bench.read_traffic("sparse_split", "other") is None
+    assert bench.read_traffic("sparse_split", "w") == (1234.0, 1200.0)
+    assert bench.read_traffic("merge", "w") == (None, None)
+    assert bench.read_traffic("sparse_split", "other") == (None, None)
     (prof / "pmc_w.txt").write_text(text.format("0" * 16))
-    assert bench.read_traffic("sparse_split", "w") is None
+    assert bench.read_traffic("sparse_split", "w") == (None, None)
 
 
 def test_more_than_one_gpu_is_refused():
