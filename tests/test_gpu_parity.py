@@ -621,3 +621,43 @@ def test_pack_rows_partial_and_clamped():
     assert torch.equal(dst[1][:, :10], want)
     assert torch.count_nonzero(dst[1][:, 10:]) == 0
     assert int(status.item()) & fo.FLAG_INDEX_CLAMPED
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes within the ABI's limits
+# ---------------------------------------------------------------------------
+
+
+def _random_workload(seed):
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 5, 7, 8, 16]))
+    L = int(rng.integers(2, 7))
+    lo = int(rng.integers(1, 400))
+    hi = lo + int(rng.integers(0, 900))
+    plo = int(rng.integers(1, 60))
+    nf = int(rng.integers(1, L))
+    band_lo = int(rng.integers(0, L - nf + 1))
+    return get_workload("7b-b16-ragged").with_overrides(
+        batch=int(rng.integers(1, 7)), num_layers=L, num_q_heads=hkv * g, num_kv_heads=hkv,
+        head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+        tau=float(rng.choice([0.02, 0.05, 0.1, 0.3, 0.7])), num_focal=nf,
+        warmup_steps=int(rng.integers(1, 4)), focal_band=(band_lo, band_lo + nf - 1),
+        n_img_range=(lo, hi), n_prompt=(plo, plo + int(rng.integers(0, 120))), seed=5000 + seed)
+
+
+@SPARSE_VARIANTS
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(monkeypatch, seed, rows):
+    _sparse_variant(monkeypatch, rows)
+    wl = _random_workload(seed)
+    steps = wl.warmup_steps + 4
+    up = upload(wl, steps=steps)
+    log(f"[random {seed}] B={wl.batch} L={wl.num_layers} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"d={wl.head_dim} {wl.dtype} tau={wl.tau} n={up.st.n_img.tolist()}")
+    rec = run(up, fo.fastocr_create(make_config(up)), steps)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, steps):
+        chk.pruned_step(t)
