@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--pmc-summary", default=None, nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter CSVs under the DIRs (and the algorithmic bytes in a "
                          "profiled run's output file, if given) and exit (no GPU use)")
+    ap.add_argument("--counter-summary", default=None, nargs="+", metavar="DIR",
+                    help="average every counter per library kernel over rocprofv3 counter CSVs under the DIRs "
+                         "and exit (no GPU use)")
     ap.add_argument("--trace-summary", default=None, nargs="+", metavar="ARG",
                     help="DIR COMMAND [BENCH_JSON]: summarise a rocprofv3 kernel trace under DIR made by "
                          "COMMAND, beside the event averages of BENCH_JSON, and exit")
@@ -95,6 +98,8 @@ def kernel_class(name):
     m = re.search(r"split_attn_kernel<[^,]+, \d+, (\d)", head)
     if m:
         return KERNEL_CLASSES[int(m.group(1))]
+    if "fastocr::split_valu_kernel<" in head:
+        return "full_split"  # the VALU variant of the full pass
     if "fastocr::merge_kernel<" in head:
         return "merge"
     if "fastocr::topk_kernel" in head:
@@ -146,6 +151,26 @@ def pmc_summary(args):
             print(f"{cls}.hbm_bytes_per_launch: {hbm:.0f}")
         if cls in run_alg:
             print(f"{cls}.run_alg_bytes_per_launch: {run_alg[cls]}  # K/V rows the same run's dispatches read")
+
+
+def counter_summary(directories):
+    """Per kernel (demangled name up to its argument list) and counter: the
+    average value per dispatch over rocprofv3 counter CSVs under the
+    directories (raw counts, no calibration)."""
+    import csv
+    import glob
+    acc = {}
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = r["Kernel_Name"].split("(")[0]
+                    if kernel_class(name) is None:
+                        continue
+                    acc.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    print(f"library_source_sha256_16: {library_source_digest()}")
+    for (name, ctr), vals in sorted(acc.items()):
+        print(f"{kernel_class(name):12s} {ctr:26s} {np.mean(vals):16.1f}  # {len(vals)} dispatches, {name}")
 
 
 def trace_summary(directory, command, bench_json=None):
@@ -210,6 +235,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary[:3])

@@ -68,6 +68,7 @@ struct fastocr_handle {
   bool wave_states = false;            // kept-token splits write one state per wave
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
+  bool valu_full = false;              // full passes run the VALU variant (measurement override)
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
   int states_per_sparse_split = 1;
@@ -213,6 +214,7 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
   const bool focal = scores_dst != nullptr;
   SplitParams sp = split_params(h, q, k, v, lens, out, false);
   sp.direct = 0;
+  sp.valu = (h->valu_full && !focal && !h->app_k) ? 1 : 0;
   int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream, lt);
   });
@@ -403,6 +405,10 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1 &&
                    !h->sparse_pipe;
   h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
+  // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
+  // of at most kValuMaxGroup heads), to measure what the matrix cores buy
+  h->valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 &&
+                 c.head_dim == 128 && h->G <= kValuMaxGroup;
   // k_b = n_b for every n_b exactly when tau = 1
   h->keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
   // state slots per head (a direct kept-token pass writes none)

@@ -63,7 +63,11 @@ struct SplitParams {
   int32_t pipe;           // kept-token pass of multi-round splits (rows_per_split <=
                           // kMaxPipeRows): row map in LDS, rounds double-buffered
   float scale_log2;       // logit scale * log2(e)
+  int32_t valu;           // full kind, bf16, D = 128, Hq/Hkv <= kValuMaxGroup: the VALU
+                          // variant (fp32 FMAs and 16-lane shuffle reductions instead of
+                          // MFMA; a measurement override, same states)
 };
+constexpr int kValuMaxGroup = 8;
 
 // Merge of a split pass (one workgroup per head) and, for focal layers, the
 // head-summed image-token scores (score_blocks workgroups per sequence).

@@ -985,6 +985,184 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
 }
 
 // ---------------------------------------------------------------------------
+// VALU variant of the full split pass (measurement override)
+// ---------------------------------------------------------------------------
+
+// The same work and merge-state format as split_attn_kernel<.., KIND_FULL>,
+// with the query-group x K-tile product and the probability x V product done
+// as fp32 FMAs on the vector ALUs.  Lane (s, c) = (lane / 16, lane % 16) holds
+// elements [8c, 8c + 8) of its rows and of the group's queries; a row's logit
+// is the sum over the 16 lanes of a slot (four shuffle steps), and each slot
+// keeps its own softmax state over the rows it visits, combined across slots
+// and waves at the end.  bf16, D = 128, groups of at most GM heads.
+template <int GM>
+__global__ __launch_bounds__(256, 2) void split_valu_kernel(SplitParams p) {
+  constexpr int D = 128, NW = 4, U = 4;  // U rows per lane per round
+  constexpr int RND = NW * U * 4;        // rows per workgroup round
+  __shared__ float s_acc[NW][GM][D];
+  __shared__ float s_st[NW][GM][3];
+  const int pair = blockIdx.y;
+  const int split = blockIdx.x;
+  const int kvh = pair % p.Hkv;
+  const int b = pair / p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, slot = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+  const int begin = split * p.rows_per_split;
+  const size_t row_base = ((size_t)b * p.Hkv + kvh) * (size_t)p.S;
+  const uint16_t* __restrict__ Kb = reinterpret_cast<const uint16_t*>(p.k) + row_base * D + 8 * c;
+  const uint16_t* __restrict__ Vb = reinterpret_cast<const uint16_t*>(p.v) + row_base * D + 8 * c;
+
+  float qf[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (h < G)
+      w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                          ((size_t)b * p.Hq + kvh * G + h) * D + 8 * c);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[h][2 * e] = __uint_as_float(ws[e] << 16) * p.scale_log2;
+      qf[h][2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u) * p.scale_log2;
+    }
+  }
+  int n, len;
+  const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
+  if (clamped && split == 0 && kvh == 0 && tid == 0) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
+  (void)split_count(len, p.rows_per_split, p.grid_splits, p.status, split == 0 && kvh == 0 && tid == 0);
+  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
+  if (begin >= len) {
+    if (tid < G) p.pstat[slot0 + (size_t)tid * p.max_splits] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int end = min(begin + p.rows_per_split, len);
+
+  float m[GM], z[GM], zt[GM], acc[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    m[h] = -INFINITY;
+    z[h] = zt[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  for (int r0 = begin; r0 < end; r0 += RND) {
+    int rr[U];
+    uint4 kw[U], vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      rr[u] = r0 + (u * NW + wave) * 4 + slot;
+      const size_t rc = (size_t)min(rr[u], p.S - 1);
+      kw[u] = *reinterpret_cast<const uint4*>(Kb + rc * D);
+      vw[u] = *reinterpret_cast<const uint4*>(Vb + rc * D);
+    }
+    float kf[U][8], vf[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = rr[u] < end;
+      const uint32_t ks[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
+      const uint32_t vs[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[u][2 * e] = __uint_as_float(ks[e] << 16);
+        kf[u][2 * e + 1] = __uint_as_float(ks[e] & 0xffff0000u);
+        // rows past the end carry zero weight: zero their values so that
+        // whatever the cache holds there cannot turn 0 * v into NaN
+        vf[u][2 * e] = ok ? __uint_as_float(vs[e] << 16) : 0.f;
+        vf[u][2 * e + 1] = ok ? __uint_as_float(vs[e] & 0xffff0000u) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h >= G) break;  // uniform
+      float x[U];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sacc = fmaf(kf[u][e], qf[h][e], sacc);
+        sacc += __shfl_xor(sacc, 1);
+        sacc += __shfl_xor(sacc, 2);
+        sacc += __shfl_xor(sacc, 4);
+        sacc += __shfl_xor(sacc, 8);
+        x[u] = rr[u] < end ? sacc : -INFINITY;
+        mt = fmaxf(mt, x[u]);
+      }
+      const float m_new = fmaxf(m[h], mt);
+      if (m_new == -INFINITY) continue;  // no rows for this slot yet
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
+      z[h] *= alpha;
+      zt[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pr = __builtin_amdgcn_exp2f(x[u] - m_new);
+        z[h] += pr;
+        zt[h] += rr[u] >= n ? pr : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[u][e], acc[h][e]);
+      }
+      m[h] = m_new;
+    }
+  }
+
+  // combine the four slots of a wave (lanes c, c + 16, c + 32, c + 48)
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h >= G) break;
+    float M = fmaxf(m[h], __shfl_xor(m[h], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float w = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
+    float zz = z[h] * w, tt = zt[h] * w;
+    zz += __shfl_xor(zz, 16);
+    zz += __shfl_xor(zz, 32);
+    tt += __shfl_xor(tt, 16);
+    tt += __shfl_xor(tt, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = acc[h][e] * w;
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      if (slot == 0) s_acc[wave][h][8 * c + e] = a;
+    }
+    if (lane == 0) {
+      s_st[wave][h][0] = M;
+      s_st[wave][h][1] = zz;
+      s_st[wave][h][2] = tt;
+    }
+  }
+  __syncthreads();
+  // combine the waves: one state per head (the normaliser is the fp32 sum)
+  for (int i = tid; i < G * D; i += NW * 64) {
+    const int h = i / D, d = i - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_st[w][h][0]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (s_st[w][h][0] != -INFINITY) o += s_acc[w][h][d] * __builtin_amdgcn_exp2f(s_st[w][h][0] - M);
+    p.po[(slot0 + (size_t)h * p.max_splits) * D + d] = o;
+  }
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_st[w][tid][0]);
+    float zz = 0.f, tt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (s_st[w][tid][0] != -INFINITY) {
+        const float e = __builtin_amdgcn_exp2f(s_st[w][tid][0] - M);
+        zz += s_st[w][tid][1] * e;
+        tt += s_st[w][tid][2] * e;
+      }
+    p.pstat[slot0 + (size_t)tid * p.max_splits] = make_float4(M, zz, zz, tt);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge of split states, and image-token scores
 // ---------------------------------------------------------------------------
 
@@ -1350,6 +1528,8 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
   const dim3 grid = kind == KIND_SPARSE ? dim3(p.Hkv * p.B, p.grid_splits) : dim3(p.grid_splits, p.Hkv * p.B);
   switch (kind) {
     case KIND_FULL:
+      if constexpr (sizeof(T) == 2 && D == 128)
+        if (p.valu) return launch(split_valu_kernel<kValuMaxGroup>, grid, block, stream, timing, p);
       return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, kTilesPerWave>, grid, block, stream,
                     timing, p);
     case KIND_FOCAL:

@@ -50,6 +50,10 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
+ *   FASTOCR_VALU_FULL=0|1   full passes (warm-up, FULL mode, tau = 1 non-focal
+ *                           layers) without MFMA: fp32 FMAs with 16-lane
+ *                           shuffle reductions (bf16, head_dim 128, at most 8
+ *                           query heads per KV head; default 0)
  */
 #ifndef FASTOCR_H
 #define FASTOCR_H

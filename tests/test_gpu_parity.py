@@ -28,8 +28,11 @@ def _need_gpu():
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("name,steps", [("tiny-fp32", 6), ("7b-b1", 3)])
-def test_full_mode_matches_oracle(name, steps):
+@pytest.mark.parametrize("name,steps,valu", [("tiny-fp32", 6, False), ("7b-b1", 3, False),
+                                             ("7b-b1", 3, True)])
+def test_full_mode_matches_oracle(monkeypatch, name, steps, valu):
+    # valu: the full split without MFMA (a measurement override)
+    monkeypatch.setenv("FASTOCR_VALU_FULL", "1" if valu else "0")
     up = upload(get_workload(name), steps=steps)
     h = fo.fastocr_create(make_config(up, mode="full"))
     rec = run(up, h, steps)
@@ -661,3 +664,20 @@ def test_random_shapes(monkeypatch, seed, rows):
     chk.warmup()
     for t in range(wl.warmup_steps, steps):
         chk.pruned_step(t)
+
+
+@pytest.mark.parametrize("hq,hkv", [(28, 4), (40, 8), (64, 8), (8, 8)])
+def test_valu_full_split_trajectory(monkeypatch, hq, hkv):
+    # the VALU full split in warm-up steps (text mass -> focal set) and at
+    # tau = 1 on non-focal layers, over a ragged batch
+    monkeypatch.setenv("FASTOCR_VALU_FULL", "1")
+    wl = _small_ragged(batch=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, dtype="bf16",
+                       n_img_range=(300, 1500), tau=1.0)
+    up = upload(wl, steps=5)
+    rec = run(up, fo.fastocr_create(make_config(up)), 5)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 5):
+        chk.pruned_step(t)
+    log(f"[valu {hq}/{hkv}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
