@@ -681,3 +681,66 @@ def test_valu_full_split_trajectory(monkeypatch, hq, hkv):
     for t in range(wl.warmup_steps, 5):
         chk.pruned_step(t)
     log(f"[valu {hq}/{hkv}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# a captured step replayed as a HIP graph
+# ---------------------------------------------------------------------------
+
+
+def test_graph_replayed_steps_match_eager():
+    # one pruned step captured as a graph (q and lens staged by copies, as
+    # the benchmark does) and replayed step after step, with another
+    # handle's eager steps and synchronisations in between: every replay's
+    # outputs and kept set equal the eager step's bit for bit
+    wl = get_workload("7b-b1").with_overrides(num_layers=6, focal_band=(2, 3), num_focal=2, warmup_steps=2)
+    T = 10
+    up = upload(wl, steps=T)
+    L, B, Hq, d = wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim
+    stream = torch.cuda.Stream()
+    ha = fo.fastocr_create(make_config(up), stream)
+    hb = fo.fastocr_create(make_config(up), stream)
+    io = up.io_dtype
+
+    def eager(h, t, outs):
+        for l in range(L):
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], outs[l])
+
+    scratch = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
+    with torch.cuda.stream(stream):
+        for t in range(wl.warmup_steps):
+            eager(ha, t, scratch)
+            eager(hb, t, scratch)
+    assert fo.fastocr_profile_warmup(ha) == fo.fastocr_profile_warmup(hb)
+    q_stage = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
+    lens_stage = torch.empty((B, 2), dtype=torch.int32, device=DEV)
+    out_stage = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
+    k_max = fo.fastocr_get_info(ha)["k_max"]
+    sa, sb = (torch.zeros((B, k_max), dtype=torch.int32, device=DEV) for _ in range(2))
+    ca, cb = (torch.zeros((B,), dtype=torch.int32, device=DEV) for _ in range(2))
+    with torch.cuda.stream(stream):
+        q_stage.copy_(torch.stack([up.Qd[l][wl.warmup_steps] for l in range(L)]))
+        lens_stage.copy_(up.lens[wl.warmup_steps])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for l in range(L):
+            fo.fastocr_attend(ha, l, q_stage[l], up.Kd[l], up.Vd[l], lens_stage, out_stage[l])
+    torch.cuda.synchronize()
+    out_b = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
+    for t in range(wl.warmup_steps, T):
+        with torch.cuda.stream(stream):
+            q_stage.copy_(torch.stack([up.Qd[l][t] for l in range(L)]))
+            lens_stage.copy_(up.lens[t])
+            g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            eager(hb, t, out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_stage, out_b), f"step {t}"
+        fo.fastocr_get_selection(ha, sa, ca)
+        fo.fastocr_get_selection(hb, sb, cb)
+        torch.cuda.synchronize()
+        assert torch.equal(ca, cb) and torch.equal(sa, sb), f"kept set after step {t}"
+    assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
+    del g
