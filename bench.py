@@ -52,11 +52,15 @@ def parse():
                     help="budget of the CPU oracle baseline sample (0 disables it)")
     ap.add_argument("--profile-only", action="store_true",
                     help="skip the CPU baseline and the FULL comparison (for profiler runs)")
-    ap.add_argument("--scrub-mb", type=int, default=512,
+    # The two extra phases are off by default, so that a kernel trace of the
+    # default command averages the same launches as its event timing (the
+    # scrubbed replays run MALL-cold, the append variants do more work).
+    ap.add_argument("--scrub-mb", type=int, default=0,
                     help="also time steps after a read pass over this many MiB that evicts the 256 MB "
-                         "MALL (0 disables it)")
-    ap.add_argument("--no-append", action="store_true",
-                    help="skip the comparison of a separate K/V append kernel with fastocr_attend_append")
+                         "MALL (512 evicts it; 0, the default, disables it)")
+    ap.add_argument("--append", action="store_true",
+                    help="also compare a separate K/V append kernel with fastocr_attend_append")
+    ap.add_argument("--no-append", action="store_true", help="(the default) no append comparison")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 256 MiB device-to-device copy, the reference kernel that "
                          "scales hardware byte counters")
@@ -270,7 +274,7 @@ def main():
     # spread over the rest of the trajectory [w + W, T), the phases
     # interleaved, so every phase sees short and long text alike.
     do_scrub = args.scrub_mb > 0 and not args.profile_only and not args.no_graph
-    do_append = not args.no_append and not args.profile_only and not args.no_graph
+    do_append = args.append and not args.no_append and not args.profile_only and not args.no_graph
     # the schedule does not depend on which phases run, so a profiler run of
     # a subset times the same decode steps as the full run
     phases = ["graph", "events", "scrub", "append_separate", "append_fused"]
