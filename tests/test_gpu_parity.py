@@ -744,3 +744,18 @@ def test_graph_replayed_steps_match_eager():
         assert torch.equal(ca, cb) and torch.equal(sa, sb), f"kept set after step {t}"
     assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
     del g
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_unknown_bounds(seed):
+    # min_img_tokens = max_text_tokens = 0: launches sized for the whole row
+    # capacity (most kept-token splits and full-pass splits find no rows)
+    wl = _random_workload(100 + seed)
+    steps = wl.warmup_steps + 3
+    up = upload(wl, steps=steps)
+    rec = run(up, fo.fastocr_create(make_config(up, min_img_tokens=0, max_text_tokens=0)), steps)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, steps):
+        chk.pruned_step(t)
