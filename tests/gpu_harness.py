@@ -179,16 +179,18 @@ def check_scores(got: np.ndarray, want: np.ndarray, what: str) -> None:
 class Checker:
     """Replays the method on the CPU next to the GPU records."""
 
-    def __init__(self, up: Uploaded, rec: Records, tau: Optional[float] = None, spans=None):
+    def __init__(self, up: Uploaded, rec: Records, tau: Optional[float] = None, spans=None,
+                 scale: Optional[float] = None):
         """spans: per sequence (start, count) of its image pages in up's
         (host) cache layout; the GPU ran on the image-first permuted cache."""
         self.up, self.rec = up, rec
         wl = up.wl
         self.tau = wl.tau if tau is None else tau
-        self.scale = 1.0 / math.sqrt(wl.head_dim)
+        self.scale = 1.0 / math.sqrt(wl.head_dim) if scale is None else scale
         self.oracle = DecodeOracle(num_layers=wl.num_layers, num_q_heads=wl.num_q_heads,
                                    num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, tau=self.tau,
-                                   num_focal=wl.num_focal, warmup_steps=wl.warmup_steps, spans=spans)
+                                   num_focal=wl.num_focal, warmup_steps=wl.warmup_steps, spans=spans,
+                                   scale=scale)
         self.rows = (lambda b: None) if spans is None else (lambda b: self.oracle.image_rows[b])
         self.jaccard: List[float] = []
         self.worst_out = 0.0

@@ -759,3 +759,18 @@ def test_random_shapes_unknown_bounds(seed):
     chk.warmup()
     for t in range(wl.warmup_steps, steps):
         chk.pruned_step(t)
+
+
+@pytest.mark.parametrize("name,scale", [("tiny-fp32", 0.05), ("7b-b1", 0.2)])
+def test_custom_logit_scale(name, scale):
+    # sm_scale given instead of 1/sqrt(d)
+    wl = get_workload(name)
+    if name == "7b-b1":
+        wl = wl.with_overrides(num_layers=4, focal_band=(1, 2), num_focal=2, warmup_steps=2)
+    up = upload(wl, steps=8)
+    rec = run(up, fo.fastocr_create(make_config(up, sm_scale=scale)), 8)
+    assert rec.status == 0
+    chk = Checker(up, rec, scale=scale)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 8):
+        chk.pruned_step(t)
