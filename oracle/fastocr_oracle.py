@@ -124,7 +124,12 @@ def full_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int,
 def image_rows_of(spans: Sequence[Tuple[int, int]]) -> np.ndarray:
     """Cache rows of the image tokens of a sequence whose image occupies the
     given (start, count) spans (several pages or images), in ascending row
-    order: image token j of the method is row image_rows_of(spans)[j]."""
+    order: image token j of the method is row image_rows_of(spans)[j].
+
+    The method prunes visual tokens and keeps every text token (Method / 1.
+    Focal-Guided Pruning); where in the cache the visual tokens sit is not
+    fixed by the summary, so they are whichever rows the spans name.
+    """
     rows = [np.arange(a, a + c, dtype=np.int64) for a, c in spans]
     return np.sort(np.concatenate(rows)) if rows else np.zeros(0, dtype=np.int64)
 
