@@ -774,3 +774,24 @@ def test_custom_logit_scale(name, scale):
     chk.warmup()
     for t in range(wl.warmup_steps, 8):
         chk.pruned_step(t)
+
+
+@pytest.mark.parametrize("case", ["long-page", "wide-batch"])
+def test_large_extents(case):
+    # long-page: 40000 image tokens (the in-pipeline top-k beyond 16 keys per
+    # thread re-reads its keys per pass); wide-batch: 64 sequences x 8 KV
+    # heads (512 pairs per launch row)
+    if case == "long-page":
+        wl = get_workload("7b-b1").with_overrides(grid=(200, 200), num_layers=3, focal_band=(1, 1),
+                                                  num_focal=1, warmup_steps=2, num_q_heads=8, num_kv_heads=1)
+    else:
+        wl = _small_ragged(batch=64, num_q_heads=32, num_kv_heads=8, n_img_range=(100, 300),
+                           n_prompt=(10, 50), num_layers=3, focal_band=(1, 1), num_focal=1)
+    up = upload(wl, steps=5)
+    rec = run(up, fo.fastocr_create(make_config(up)), 5)
+    assert rec.status == 0
+    chk = Checker(up, rec)
+    chk.warmup()
+    for t in range(wl.warmup_steps, 5):
+        chk.pruned_step(t)
+    log(f"[{case}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
