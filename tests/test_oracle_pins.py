@@ -94,6 +94,30 @@ def pin_golden_decode(name):
     np.testing.assert_allclose(sp, ex["sparse_out"], rtol=0, atol=1e-12)
 
 
+def pin_golden_spans():
+    fx = _load("decode_spans.yaml")
+    q = np.array(fx["q"], dtype=np.float64)
+    K = np.array(fx["keys"], dtype=np.float64)
+    V = np.array(fx["values"], dtype=np.float64)
+    length, scale = fx["length"], fx["scale"]
+    ex = fx["expect"]
+    rows = ofo.image_rows_of([tuple(sp) for sp in fx["spans"]])
+    assert list(rows) == ex["image_rows"]
+    n = len(rows)
+    out, p = ofo.full_attention(q, K, V, length, scale)
+    np.testing.assert_allclose(p, ex["probs"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, ex["out"], rtol=0, atol=1e-12)
+    s = ofo.image_scores(p, n, rows)
+    np.testing.assert_allclose(s, ex["scores"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ofo.image_mass(p, n, rows), ex["image_mass"], rtol=0, atol=1e-12)
+    k = ofo.kept_count(fx["tau"], n)
+    assert k == ex["kept"]
+    sel = ofo.select_top(s, k)
+    assert list(sel) == ex["selected"]
+    sp = ofo.sparse_attention(q, K, V, sel, n, length, scale, rows)
+    np.testing.assert_allclose(sp, ex["sparse_out"], rtol=0, atol=1e-12)
+
+
 def pin_kept_counts():
     fx = _load("selection_and_counts.yaml")
     for row in fx["kept"]:
@@ -213,7 +237,7 @@ def pin_focal_brute_force():
 PINS = [
     pin_kept_counts, pin_golden_topk, pin_golden_focal, pin_full_vs_sdpa,
     pin_sparse_vs_masked_sdpa, pin_tau_one_is_full, pin_uniform_keys,
-    pin_mass_identities, pin_topk_brute_force, pin_focal_brute_force,
+    pin_mass_identities, pin_topk_brute_force, pin_focal_brute_force, pin_golden_spans,
 ] + [lambda name=n: pin_golden_decode(name) for n in
      ("decode_one_head.yaml", "decode_gqa_two_heads.yaml", "decode_gqa_map.yaml")]
 
@@ -509,13 +533,17 @@ def _mut_floor(tau, n):
     return 0 if n <= 0 else int(min(max(math.floor(tau * n), 1), n))
 
 
-def _mut_mean_scores(p, n):
-    return p[:, :n].mean(axis=0)
+def _mut_mean_scores(p, n, image_rows=None):
+    return (p[:, :n] if image_rows is None else p[:, image_rows]).mean(axis=0)
 
 
-def _mut_drop_current(q, K, V, selected, n, length, scale):
-    rows = np.concatenate([np.sort(np.asarray(selected, dtype=np.int64)),
-                           np.arange(n, length - 1, dtype=np.int64)])
+def _mut_drop_current(q, K, V, selected, n, length, scale, image_rows=None):
+    sel = np.sort(np.asarray(selected, dtype=np.int64))
+    if image_rows is None:
+        rows = np.concatenate([sel, np.arange(n, length - 1, dtype=np.int64)])
+    else:
+        text = np.setdiff1d(np.arange(length - 1, dtype=np.int64), image_rows)
+        rows = np.concatenate([np.asarray(image_rows)[sel], text])
     p = ofo.attention_probs(q, K, rows, scale)
     return ofo._weighted_values(p, V, rows)
 
