@@ -261,6 +261,25 @@ def fastocr_select_topk(scores, lens, tau: float, idx_out, cnt_out, stream=None)
         _dev_ptr(cnt_out, t.int32, (B,), "cnt_out", 4), ctypes.c_void_p(_stream_ptr(stream))))
 
 
+def fastocr_state_bytes(h: Handle) -> int:
+    n = ctypes.c_int64(0)
+    _check("fastocr_state_bytes", lib().fastocr_state_bytes(h.ptr, ctypes.byref(n)))
+    return n.value
+
+
+def fastocr_save_state(h: Handle) -> bytes:
+    """The handle's decode state at a step boundary, as bytes."""
+    n = fastocr_state_bytes(h)
+    buf = ctypes.create_string_buffer(n)
+    _check("fastocr_save_state", lib().fastocr_save_state(h.ptr, buf, n))
+    return buf.raw
+
+
+def fastocr_load_state(h: Handle, blob: bytes) -> None:
+    buf = ctypes.create_string_buffer(bytes(blob), len(blob))
+    _check("fastocr_load_state", lib().fastocr_load_state(h.ptr, buf, len(blob)))
+
+
 def fastocr_image_first_map(spans: Sequence[Sequence[int]], rows: int):
     """(n_img, map): the image-first row permutation of one sequence (host)."""
     flat = [int(x) for sp in spans for x in sp]

@@ -99,6 +99,9 @@ SIGNATURES = [
     ("fastocr_reset_timing", c_int32, [c_void_p]),
     ("fastocr_select_topk", c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_double, c_void_p,
                                       c_int32, c_void_p, c_void_p]),
+    ("fastocr_state_bytes", c_int32, [c_void_p, ctypes.POINTER(c_int64)]),
+    ("fastocr_save_state", c_int32, [c_void_p, c_void_p, c_int64]),
+    ("fastocr_load_state", c_int32, [c_void_p, c_void_p, c_int64]),
     ("fastocr_image_first_map", c_int32, [ctypes.POINTER(c_int32), c_int32, c_int32, ctypes.POINTER(c_int32)]),
     ("fastocr_pack_rows", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_void_p, c_void_p]),

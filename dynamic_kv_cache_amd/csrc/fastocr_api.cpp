@@ -288,6 +288,82 @@ bool config_ok(const fastocr_config& c) {
 
 }  // namespace
 
+// ---- decode state save / load --------------------------------------------
+
+namespace {
+
+constexpr uint32_t kStateMagic = 0x52434f46u;  // "FOCR"
+constexpr uint32_t kStateVersion = 1;
+
+// Everything a later step depends on, at a step boundary: the host state
+// machine and the device arrays that persist across steps (kept set and
+// counts, the warm-up window's statistics, the lens copy of its last step,
+// the status word).  The configuration fields identify the handles a blob
+// fits.
+struct StateHeader {
+  uint32_t magic, version;
+  int32_t L, Hq, Hkv, D, B, S, n_cap, n_stride, k_max, w, num_focal, mode, dtype, reprofile_every;
+  double tau;
+  int32_t step, phase, warm_pos, pruned_since, profiles, n_focal, n_ratios, pad;
+};
+
+struct StateArray {
+  void* dev;
+  size_t bytes;
+};
+
+std::vector<StateArray> state_arrays(fastocr_handle* h) {
+  const fastocr_config& c = h->cfg;
+  const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers;
+  const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
+  return {
+      {h->sel, B * h->k_max * sizeof(int32_t)},
+      {h->sel_cnt, B * sizeof(int32_t)},
+      {h->text_mass, pruned ? L * (size_t)c.warmup_steps * B * Hq * sizeof(float) : 0},
+      {h->warm_scores, pruned ? L * B * h->n_stride * sizeof(float) : 0},
+      {h->lens_shadow, B * 2 * sizeof(int32_t)},
+      {h->status, sizeof(int32_t)},
+  };
+}
+
+size_t state_bytes(fastocr_handle* h) {
+  size_t n = sizeof(StateHeader) + (size_t)h->cfg.num_layers * (sizeof(int32_t) + sizeof(double));
+  for (const StateArray& a : state_arrays(h)) n += a.bytes;
+  return n;
+}
+
+StateHeader state_header(fastocr_handle* h) {
+  const fastocr_config& c = h->cfg;
+  StateHeader s{};
+  s.magic = kStateMagic;
+  s.version = kStateVersion;
+  s.L = c.num_layers;
+  s.Hq = c.num_q_heads;
+  s.Hkv = c.num_kv_heads;
+  s.D = c.head_dim;
+  s.B = c.batch;
+  s.S = c.max_seq_len;
+  s.n_cap = h->n_cap;
+  s.n_stride = h->n_stride;
+  s.k_max = h->k_max;
+  s.w = c.warmup_steps;
+  s.num_focal = c.num_focal;
+  s.mode = c.mode;
+  s.dtype = c.dtype;
+  s.reprofile_every = c.reprofile_every;
+  s.tau = c.tau;
+  s.step = h->step;
+  s.phase = h->phase;
+  s.warm_pos = h->warm_pos;
+  s.pruned_since = h->pruned_since;
+  s.profiles = h->profiles;
+  s.n_focal = (int32_t)h->focal.size();
+  s.n_ratios = (int32_t)h->ratios.size();
+  return s;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t fastocr_kept_count(double tau, int32_t n_img) {
@@ -740,6 +816,93 @@ int fastocr_reset_timing(fastocr_handle* h) {
   if (hipStreamSynchronize(h->stream) != hipSuccess) return fail_hip(h, hipErrorUnknown);
   h->ev_used = 0;
   h->timing_acc = fastocr_timing{};
+  return FASTOCR_OK;
+}
+
+
+int fastocr_state_bytes(fastocr_handle* h, int64_t* bytes) {
+  if (!h || !bytes) return FASTOCR_ERR_INVALID_ARG;
+  *bytes = (int64_t)state_bytes(h);
+  return FASTOCR_OK;
+}
+
+int fastocr_save_state(fastocr_handle* h, void* host_buf, int64_t bytes) {
+  if (!h || !host_buf) return FASTOCR_ERR_INVALID_ARG;
+  if (bytes < (int64_t)state_bytes(h)) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned || h->next_layer != 0) return FASTOCR_ERR_STATE;
+  const int L = h->cfg.num_layers;
+  char* p = static_cast<char*>(host_buf);
+  const StateHeader s = state_header(h);
+  std::memcpy(p, &s, sizeof(s));
+  p += sizeof(s);
+  std::vector<int32_t> focal(L, -1);
+  std::copy(h->focal.begin(), h->focal.end(), focal.begin());
+  std::vector<double> ratios(L, 0.0);
+  std::copy(h->ratios.begin(), h->ratios.end(), ratios.begin());
+  std::memcpy(p, focal.data(), L * sizeof(int32_t));
+  p += L * sizeof(int32_t);
+  std::memcpy(p, ratios.data(), L * sizeof(double));
+  p += L * sizeof(double);
+  hipError_t e = hipStreamSynchronize(h->stream);
+  for (const StateArray& a : state_arrays(h)) {
+    if (e == hipSuccess && a.bytes) e = hipMemcpy(p, a.dev, a.bytes, hipMemcpyDeviceToHost);
+    p += a.bytes;
+  }
+  return e == hipSuccess ? FASTOCR_OK : fail_hip(h, e);
+}
+
+int fastocr_load_state(fastocr_handle* h, const void* host_buf, int64_t bytes) {
+  if (!h || !host_buf) return FASTOCR_ERR_INVALID_ARG;
+  if (bytes < (int64_t)sizeof(StateHeader) || bytes < (int64_t)state_bytes(h)) return FASTOCR_ERR_INVALID_ARG;
+  if (h->poisoned || h->next_layer != 0) return FASTOCR_ERR_STATE;
+  const int L = h->cfg.num_layers;
+  const char* p = static_cast<const char*>(host_buf);
+  StateHeader s;
+  std::memcpy(&s, p, sizeof(s));
+  p += sizeof(s);
+  StateHeader mine = state_header(h);
+  // the configuration must be the handle's own (the per-run fields may differ)
+  mine.step = s.step;
+  mine.phase = s.phase;
+  mine.warm_pos = s.warm_pos;
+  mine.pruned_since = s.pruned_since;
+  mine.profiles = s.profiles;
+  mine.n_focal = s.n_focal;
+  mine.n_ratios = s.n_ratios;
+  if (std::memcmp(&s, &mine, sizeof(s)) != 0) return FASTOCR_ERR_INVALID_ARG;
+  const bool pruned = h->cfg.mode == FASTOCR_MODE_PRUNED;
+  const int ph = s.phase;
+  const bool phase_ok = pruned ? (ph == PHASE_WARMUP || ph == PHASE_WARMUP_DONE || ph == PHASE_PRUNED)
+                               : ph == PHASE_FULL;
+  if (!phase_ok || s.step < 0 || s.warm_pos < 0 || s.warm_pos > s.w || s.pruned_since < 0 ||
+      s.profiles < 0 || s.n_focal < 0 || s.n_focal > L || s.n_ratios < 0 || s.n_ratios > L ||
+      (ph == PHASE_PRUNED && s.n_focal == 0))
+    return FASTOCR_ERR_INVALID_ARG;
+  std::vector<int32_t> focal(L);
+  std::memcpy(focal.data(), p, L * sizeof(int32_t));
+  p += L * sizeof(int32_t);
+  std::vector<char> is_focal(L, 0);
+  for (int i = 0; i < s.n_focal; ++i) {
+    if (focal[i] < 0 || focal[i] >= L || is_focal[focal[i]]) return FASTOCR_ERR_INVALID_ARG;
+    is_focal[focal[i]] = 1;
+  }
+  std::vector<double> ratios(L);
+  std::memcpy(ratios.data(), p, L * sizeof(double));
+  p += L * sizeof(double);
+  hipError_t e = hipStreamSynchronize(h->stream);
+  for (const StateArray& a : state_arrays(h)) {
+    if (e == hipSuccess && a.bytes) e = hipMemcpy(a.dev, p, a.bytes, hipMemcpyHostToDevice);
+    p += a.bytes;
+  }
+  if (e != hipSuccess) return fail_hip(h, e);
+  h->step = s.step;
+  h->phase = s.phase;
+  h->warm_pos = s.warm_pos;
+  h->pruned_since = s.pruned_since;
+  h->profiles = s.profiles;
+  h->focal.assign(focal.begin(), focal.begin() + s.n_focal);
+  h->is_focal = is_focal;
+  h->ratios.assign(ratios.begin(), ratios.begin() + s.n_ratios);
   return FASTOCR_OK;
 }
 

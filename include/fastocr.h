@@ -284,6 +284,32 @@ int fastocr_select_topk(const float* scores, int32_t score_stride, const int32_t
                         int32_t batch, double tau, int32_t* idx_out, int32_t idx_stride,
                         int32_t* cnt_out, void* hip_stream);
 
+/* ---- decode state save / load ------------------------------------------- */
+
+/* A decode can move to another handle (another process, another device)
+ * between steps: the blob holds the step count and phase, the focal set and
+ * ratios, the kept set carried to the next step (Cross-Step Fixation Reuse),
+ * the current warm-up window's statistics, and the status flags.  It does
+ * not hold the KV cache, which stays the caller's. */
+
+/* fastocr_state_bytes: size in bytes of this handle's state blob. */
+int fastocr_state_bytes(fastocr_handle* h, int64_t* bytes);
+
+/* fastocr_save_state: at a step boundary (no layer of the current step
+ * called yet), write the handle's decode state to host_buf (host memory of
+ * at least fastocr_state_bytes bytes).  Synchronises the stream.  Errors:
+ * INVALID_ARG (null, buffer too small), STATE (mid-step, poisoned handle),
+ * HIP. */
+int fastocr_save_state(fastocr_handle* h, void* host_buf, int64_t bytes);
+
+/* fastocr_load_state: replace the decode state of a handle at a step
+ * boundary with a blob from fastocr_save_state of a handle created with the
+ * same configuration; the next fastocr_attend continues that decode exactly.
+ * Synchronises the stream.  Errors: INVALID_ARG (null, short buffer, not a
+ * blob of this configuration, inconsistent contents), STATE (mid-step,
+ * poisoned handle), HIP. */
+int fastocr_load_state(fastocr_handle* h, const void* host_buf, int64_t bytes);
+
 /* ---- multi-span image layouts -------------------------------------------- */
 
 /* The library's kernels take every sequence's image tokens as cache rows

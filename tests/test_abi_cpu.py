@@ -116,6 +116,9 @@ def test_null_arguments():
     assert lib.fastocr_attend(None, 0, None, None, None, None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_profile_warmup(None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_get_focal_layers(None, None) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_state_bytes(None, None) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_save_state(None, None, 0) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_load_state(None, None, 0) == fo.ERR_INVALID_ARG
     assert lib.fastocr_destroy(None) == fo.OK
     assert lib.fastocr_select_topk(None, 4, None, 1, 0.5, None, 4, None, None) == fo.ERR_INVALID_ARG
 

@@ -795,3 +795,77 @@ def test_large_extents(case):
     for t in range(wl.warmup_steps, 5):
         chk.pruned_step(t)
     log(f"[{case}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# decode state moved to another handle between steps
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("cut", [2, 4, 6, 10, 13])
+def test_save_load_state_resumes_exactly(cut):
+    # tiny page, 20 steps, re-selection every 4 pruned steps (windows at
+    # steps 0-3, 8-11, 16-19): cuts mid-window, at the end of the first
+    # window (before its profile), in pruned steps and mid re-selection
+    wl = get_workload("tiny-fp32").with_overrides(steps=20, drift=(10, (0, 2)))
+    up = upload(wl)
+    L, B, Hq, d, T = wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim, wl.steps
+    cfg = make_config(up, reprofile_every=4)
+
+    def step(h, t, out):
+        info = fo.fastocr_get_info(h)
+        if info["phase"] == 1 and info["profiles"] == 0:
+            fo.fastocr_profile_warmup(h)
+        for l in range(L):
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out[l])
+
+    ha = fo.fastocr_create(cfg)
+    scratch = torch.empty((L, B, Hq, d), dtype=up.io_dtype, device=DEV)
+    for t in range(cut):
+        step(ha, t, scratch)
+    blob = fo.fastocr_save_state(ha)
+    hb = fo.fastocr_create(cfg)
+    fo.fastocr_load_state(hb, blob)
+    assert fo.fastocr_get_info(hb)["step"] == cut
+    oa = torch.empty((T - cut, L, B, Hq, d), dtype=up.io_dtype, device=DEV)
+    ob = torch.empty_like(oa)
+    for t in range(cut, T):
+        step(ha, t, oa[t - cut])
+        step(hb, t, ob[t - cut])
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert fo.fastocr_get_focal_layers(ha) == fo.fastocr_get_focal_layers(hb)
+    k_max = fo.fastocr_get_info(ha)["k_max"]
+    sa, sb = (torch.zeros((B, k_max), dtype=torch.int32, device=DEV) for _ in range(2))
+    ca, cb = (torch.zeros((B,), dtype=torch.int32, device=DEV) for _ in range(2))
+    fo.fastocr_get_selection(ha, sa, ca)
+    fo.fastocr_get_selection(hb, sb, cb)
+    torch.cuda.synchronize()
+    assert torch.equal(sa, sb) and torch.equal(ca, cb)
+    assert fo.fastocr_get_info(ha)["profiles"] == fo.fastocr_get_info(hb)["profiles"]
+
+
+def test_save_load_state_errors():
+    wl = get_workload("tiny-fp32")
+    up = upload(wl, steps=2)
+    h = fo.fastocr_create(make_config(up))
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
+    fo.fastocr_attend(h, 0, up.Qd[0][0], up.Kd[0], up.Vd[0], up.lens[0], out)
+    with pytest.raises(fo.FastOCRError) as e:  # mid-step
+        fo.fastocr_save_state(h)
+    assert e.value.code == fo.ERR_STATE
+    for l in range(1, wl.num_layers):
+        fo.fastocr_attend(h, l, up.Qd[l][0], up.Kd[l], up.Vd[l], up.lens[0], out)
+    blob = fo.fastocr_save_state(h)
+    other = fo.fastocr_create(make_config(up, tau=0.2))  # another configuration
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_load_state(other, blob)
+    assert e.value.code == fo.ERR_INVALID_ARG
+    with pytest.raises(fo.FastOCRError) as e:  # truncated
+        fo.fastocr_load_state(fo.fastocr_create(make_config(up)), blob[:100])
+    assert e.value.code == fo.ERR_INVALID_ARG
+    bad = bytearray(blob)
+    bad[0] ^= 0xFF  # not a state blob
+    with pytest.raises(fo.FastOCRError) as e:
+        fo.fastocr_load_state(fo.fastocr_create(make_config(up)), bytes(bad))
+    assert e.value.code == fo.ERR_INVALID_ARG
