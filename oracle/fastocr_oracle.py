@@ -44,7 +44,13 @@ supports):
   scores at the deepest focal layer;
 * grouped-query attention maps query head h to KV head h // (Hq / Hkv); the
   logit scale is 1 / sqrt(d);
-* an empty attention set yields a zero output.
+* an empty attention set yields a zero output;
+* optional periodic re-selection (the conclusion names adaptive layer
+  selection as future work): after every R pruned steps a new w-step
+  warm-up window picks C and F_last again from that window alone;
+* image tokens may sit in several spans of the cache (pages with text
+  between them): image token j is the j-th image row in ascending order,
+  and every other row is text.
 
 Parity pins: every function here is checked in tests/test_oracle_pins.py
 against closed forms, hand-worked fixtures, an independent library routine
