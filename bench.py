@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--pmc-summary", default=None, nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter CSVs under the DIRs (and the algorithmic bytes in a "
                          "profiled run's output file, if given) and exit (no GPU use)")
+    ap.add_argument("--marker-summary", default=None, nargs="+", metavar="DIR",
+                    help="host time per library call kind from a FASTOCR_TRACE=1 rocprofv3 --marker-trace run "
+                         "under the DIRs, and exit (no GPU use)")
     ap.add_argument("--counter-summary", default=None, nargs="+", metavar="DIR",
                     help="average every counter per library kernel over rocprofv3 counter CSVs under the DIRs "
                          "and exit (no GPU use)")
@@ -177,6 +180,30 @@ def counter_summary(directories):
         print(f"{kernel_class(name):12s} {ctr:26s} {np.mean(vals):16.1f}  # {len(vals)} dispatches, {name}")
 
 
+def marker_summary(directories):
+    """Host time of the library's calls from the named ranges a FASTOCR_TRACE=1
+    run leaves in a rocprofv3 --marker-trace CSV: per kind of call, the count
+    and the median and mean time from entering to leaving the call (the
+    host's enqueue cost, not kernel time)."""
+    import csv
+    import glob
+    per = {}
+    for directory in directories:
+        for path in glob.glob(os.path.join(directory, "**", "*marker_api_trace.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = r["Function"]
+                    if not name.startswith("fastocr"):
+                        continue
+                    kind = "profile" if name == "fastocr profile" else name.split()[-1]
+                    dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    per.setdefault(kind, []).append(dt)
+    print(f"library_source_sha256_16: {library_source_digest()}")
+    print(f"# {'call kind':12s} {'calls':>7s} {'median_us':>10s} {'mean_us':>10s}")
+    for kind, v in sorted(per.items()):
+        print(f"{kind:14s} {len(v):7d} {float(np.median(v)):10.2f} {float(np.mean(v)):10.2f}")
+
+
 def trace_summary(directory, command, bench_json=None):
     """Per-kernel durations from a rocprofv3 --kernel-trace --stats run of
     this script, beside the averages that a run of the same command measured
@@ -239,6 +266,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.marker_summary:
+        marker_summary(args.marker_summary)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary)

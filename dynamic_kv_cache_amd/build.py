@@ -41,6 +41,7 @@ def command(out_path: str = LIB_PATH, extra=()) -> list:
         "-I", os.path.join(ROOT, "include"),
         "-o", out_path,
         *[os.path.join(CSRC, s) for s in SOURCES],
+        "-ldl",
         *extra,
     ]
 

@@ -7,10 +7,12 @@
 // Pruning (Focal Layer Selection, Cross-Layer Propagation) and 2. Cross-Step
 // Fixation Reuse (Implementation).
 
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -25,6 +27,37 @@ using namespace fastocr;
 namespace {
 
 enum Phase : int { PHASE_WARMUP = 0, PHASE_WARMUP_DONE = 1, PHASE_PRUNED = 2, PHASE_FULL = 3 };
+
+// Optional named ranges for profiler traces (FASTOCR_TRACE=1): the roctx
+// library is opened at run time, so the library itself does not depend on it.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+Roctx open_roctx() {
+  Roctx r;
+  for (const char* name : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so", "libroctx64.so.4"}) {
+    void* lib = dlopen(name, RTLD_NOW | RTLD_LOCAL);
+    if (!lib) continue;
+    r.push = reinterpret_cast<int (*)(const char*)>(dlsym(lib, "roctxRangePushA"));
+    r.pop = reinterpret_cast<int (*)()>(dlsym(lib, "roctxRangePop"));
+    if (r.push && r.pop) return r;
+    r = Roctx{};
+  }
+  return r;
+}
+
+// One named range for the lifetime of the object (no-op without roctx).
+struct TraceRange {
+  const Roctx* r;
+  TraceRange(const Roctx* roctx, const char* msg) : r(roctx && roctx->push ? roctx : nullptr) {
+    if (r) r->push(msg);
+  }
+  ~TraceRange() {
+    if (r) r->pop();
+  }
+};
 
 struct TimedLaunch {
   int cls;
@@ -69,6 +102,7 @@ struct fastocr_handle {
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
+  Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
   int states_per_sparse_split = 1;
@@ -481,6 +515,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1 &&
                    !h->sparse_pipe;
   h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
+  if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
   // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
   // of at most kValuMaxGroup heads), to measure what the matrix cores buy
   h->valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 &&
@@ -553,6 +588,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
 // Focal Layer Selection at the end of a warm-up window (the first one, or a
 // periodic re-selection window): synchronises the stream.
 static int profile_impl(fastocr_handle* h) {
+  TraceRange range(&h->roctx, "fastocr profile");
   const fastocr_config& c = h->cfg;
   const size_t BH = (size_t)c.batch * c.num_q_heads;
   const size_t per_layer = (size_t)c.warmup_steps * BH;
@@ -607,6 +643,16 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
   }
 
   const size_t BH = (size_t)c.batch * c.num_q_heads;
+  char label[96] = "";
+  if (h->roctx.push) {
+    const char* kind = h->phase == PHASE_FULL      ? "full"
+                       : h->phase == PHASE_WARMUP  ? "warm-up"
+                       : h->is_focal[layer]        ? "focal"
+                       : h->keeps_all              ? "kept-all"
+                                                   : "kept-token";
+    std::snprintf(label, sizeof(label), "fastocr step %d layer %d %s", h->step, layer, kind);
+  }
+  TraceRange range(&h->roctx, label);
   switch (h->phase) {
     case PHASE_FULL:
       rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);

@@ -35,7 +35,7 @@
  *   - After FASTOCR_ERR_HIP the handle is poisoned: every later call except
  *     fastocr_destroy returns FASTOCR_ERR_STATE.
  *
- * Launch-plan overrides, read once by fastocr_create (for measurement and
+ * Environment settings, read once by fastocr_create (for measurement and
  * tests; results do not depend on them beyond rounding order):
  *   FASTOCR_FULL_ROWS=R     rows per split of full passes (multiple of 16)
  *   FASTOCR_SPARSE_ROWS=R   rows per split of kept-token passes; R at least the
@@ -50,6 +50,10 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
+ *   FASTOCR_TRACE=0|1       a named roctx range around every fastocr_attend
+ *                           call ("fastocr step S layer L <kind>") and the
+ *                           focal-layer profile, for rocprofv3 --marker-trace
+ *                           (the roctx library is opened at run time; default 0)
  *   FASTOCR_VALU_FULL=0|1   full passes (warm-up, FULL mode, tau = 1 non-focal
  *                           layers) without MFMA: fp32 FMAs with 16-lane
  *                           shuffle reductions (bf16, head_dim 128, at most 8

@@ -869,3 +869,17 @@ def test_save_load_state_errors():
     with pytest.raises(fo.FastOCRError) as e:
         fo.fastocr_load_state(fo.fastocr_create(make_config(up)), bytes(bad))
     assert e.value.code == fo.ERR_INVALID_ARG
+
+
+def test_trace_ranges_leave_results_unchanged(monkeypatch):
+    # FASTOCR_TRACE=1 wraps every call in a named roctx range; outputs and
+    # kept sets are bitwise those of an untraced run
+    wl = get_workload("tiny-fp32")
+    up = upload(wl)
+    monkeypatch.setenv("FASTOCR_TRACE", "1")
+    traced = run(up, fo.fastocr_create(make_config(up)), wl.steps)
+    monkeypatch.setenv("FASTOCR_TRACE", "0")
+    plain = run(up, fo.fastocr_create(make_config(up)), wl.steps)
+    assert np.array_equal(traced.outs, plain.outs)
+    assert np.array_equal(traced.sets, plain.sets) and np.array_equal(traced.cnts, plain.cnts)
+    assert traced.focal == plain.focal
