@@ -210,9 +210,13 @@ def test_32b_b4_longpage_full_size():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("tau", [0.05, 0.2])
-def test_72b_b8_full_size(tau):
-    wl = get_workload("72b-b8-sweep", tau=tau)
+@pytest.mark.parametrize("tau,sigma", [(0.05, None), (0.2, None), (0.02, None), (0.1, None), (1.0, None),
+                                       (0.05, 0.25), (0.05, 1.0)])
+def test_72b_b8_full_size(tau, sigma):
+    # the sweep's tau values (tau = 1: non-focal layers take the full pass)
+    # and query-noise levels (sigma None: the default 0.5 and its seed)
+    wl = get_workload("72b-b8-sweep", tau=tau) if sigma is None else \
+        get_workload("72b-b8-sweep", tau=tau, sigma=sigma)
     run = run_sampled(wl, _samples(wl), False)
     check_sampled(run, _samples(wl), _ranked_sample(run, [0, 30, 79]),
                   nonfocal_sample=[0, 39, 79])
