@@ -55,8 +55,11 @@ supports):
 Parity pins: every function here is checked in tests/test_oracle_pins.py
 against closed forms, hand-worked fixtures, an independent library routine
 (torch's scaled_dot_product_attention on the CPU) or brute-force enumeration.
-The end-to-end decode trajectory has no printed worked example on the pages;
-beyond those invariants it is "parity unpinned".
+The pages print no worked example of a decode trajectory; DecodeOracle is
+pinned by a hand-worked three-step, four-layer trajectory with exact
+rational outputs (warm-up pick, warm start, replacement by each focal layer,
+carry from the deepest one, ties) and by invariants (fixed point under
+stationary inputs, layer-0 focal, no eviction, drift recovery).
 """
 
 from __future__ import annotations

@@ -118,6 +118,44 @@ def pin_golden_spans():
     np.testing.assert_allclose(sp, ex["sparse_out"], rtol=0, atol=1e-12)
 
 
+def pin_golden_trajectory():
+    """A hand-worked three-step trajectory (tests/golden/trajectory_two_focal.yaml)."""
+    from fractions import Fraction
+    fx = _load("trajectory_two_focal.yaml")
+    L, S, n, P = fx["layers"], fx["rows"], fx["n_img"], fx["prompt"]
+    ex = fx["expect"]
+    frac = lambda x: float(Fraction(str(x)))  # noqa: E731
+    K = np.eye(S)[None, None]  # key row j = e_j, d = S
+    V = np.zeros((1, 1, S, S))
+    for j in range(S):
+        V[0, 0, j, :3] = (j + 1, (j + 1) ** 2, 1)
+    orc = ofo.DecodeOracle(num_layers=L, num_q_heads=1, num_kv_heads=1, head_dim=S, tau=fx["tau"],
+                           num_focal=fx["num_focal"], warmup_steps=fx["warmup_steps"], scale=1.0)
+    for t, per_layer in enumerate(fx["weights"]):
+        length = n + P + t + 1
+        lens = np.array([[n, length]])
+
+        def q_of(l, t=t, per_layer=per_layer):
+            q = np.zeros((1, 1, S))
+            a = per_layer[l]
+            assert len(a) == length
+            q[0, 0, :length] = np.log(np.asarray(a, dtype=np.float64))
+            return q
+        rec = orc.step(t, q_of, lambda l: (K, V), lens)
+        for l in range(L):
+            want = np.array([[frac(x) for x in ex["outs"][t][l]] + [0.0] * (S - 3)])
+            np.testing.assert_allclose(rec.outs[l][0], want, rtol=0, atol=1e-12)
+        if t == 0:
+            assert list(orc.focal) == ex["focal"], orc.focal
+            np.testing.assert_allclose(orc.ratios, [frac(r) for r in ex["ratios"]], rtol=0, atol=1e-12)
+            continue
+        assert [list(x) for x in rec.warm_start] == [ex["warm_start"][t - 1]]
+        for l, sel in ex["sets"][t - 1].items():
+            assert list(rec.sets[int(l)][0]) == sel, (t, l, rec.sets[int(l)][0])
+        for l, sel in ex["used_sets"][t - 1].items():
+            assert list(rec.used_sets[int(l)][0]) == sel, (t, l, rec.used_sets[int(l)][0])
+
+
 def pin_kept_counts():
     fx = _load("selection_and_counts.yaml")
     for row in fx["kept"]:
@@ -238,6 +276,7 @@ PINS = [
     pin_kept_counts, pin_golden_topk, pin_golden_focal, pin_full_vs_sdpa,
     pin_sparse_vs_masked_sdpa, pin_tau_one_is_full, pin_uniform_keys,
     pin_mass_identities, pin_topk_brute_force, pin_focal_brute_force, pin_golden_spans,
+    pin_golden_trajectory,
 ] + [lambda name=n: pin_golden_decode(name) for n in
      ("decode_one_head.yaml", "decode_gqa_two_heads.yaml", "decode_gqa_map.yaml")]
 
@@ -591,3 +630,61 @@ def test_planted_mistake_is_caught(mutation, monkeypatch):
         except AssertionError:
             caught.append(getattr(pin, "__name__", "golden"))
     assert caught, f"no pin caught the planted mistake {mutation}"
+
+
+class _ProcedureMistake(ofo.DecodeOracle):
+    """The pruned step with one planted mistake in the procedure:
+    'stale'  non-focal layers keep the step's warm start instead of the
+             latest focal pick;
+    'first'  the next step starts from the first focal layer's pick, not the
+             deepest one's;
+    'fixed'  every step starts from the set picked at profile time."""
+
+    bug = None
+
+    def step(self, t, q_of, kv_of, lens):
+        if self.window_pos is not None or self.full_mode:
+            rec = super().step(t, q_of, kv_of, lens)
+            self._profiled = [s.copy() for s in self.f_last] if self.window_pos is None else None
+            return rec
+        lens = np.asarray(lens)
+        rec = ofo.StepRecord(t=t, phase="pruned")
+        start = self._profiled if self.bug == "fixed" else self.f_last
+        current = [s.copy() for s in start]
+        rec.warm_start = [s.copy() for s in current]
+        first = None
+        for l in range(self.L):
+            q, (K, V) = q_of(l), kv_of(l)
+            out = np.zeros((lens.shape[0], self.Hq, self.d))
+            if l in set(int(c) for c in self.focal):
+                rec.sets[l] = []
+                for b in range(lens.shape[0]):
+                    n, length = int(lens[b, 0]), int(lens[b, 1])
+                    out[b], p = ofo.full_attention(q[b], K[b], V[b], length, self.scale)
+                    current[b] = ofo.select_top(ofo.image_scores(p, n), ofo.kept_count(self.tau, n))
+                    rec.sets[l].append(current[b].copy())
+                if first is None:
+                    first = [c.copy() for c in current]
+            else:
+                use = rec.warm_start if self.bug == "stale" else current
+                rec.used_sets[l] = [c.copy() for c in use]
+                for b in range(lens.shape[0]):
+                    n, length = int(lens[b, 0]), int(lens[b, 1])
+                    out[b] = ofo.sparse_attention(q[b], K[b], V[b], use[b], n, length, self.scale)
+            rec.outs.append(out)
+        self.f_last = first if self.bug == "first" else current
+        return rec
+
+
+@pytest.mark.parametrize("bug", ["stale", "first", "fixed"])
+def test_trajectory_pin_catches_procedure_mistakes(bug, monkeypatch):
+    cls = type(f"Mistake_{bug}", (_ProcedureMistake,), {"bug": bug})
+    monkeypatch.setattr(ofo, "DecodeOracle", cls)
+    with pytest.raises(AssertionError):
+        pin_golden_trajectory()
+
+
+def test_procedure_mistake_harness_without_mistake_passes(monkeypatch):
+    # the mutated step with no mistake planted reproduces the oracle
+    monkeypatch.setattr(ofo, "DecodeOracle", type("NoMistake", (_ProcedureMistake,), {"bug": None}))
+    pin_golden_trajectory()
