@@ -883,3 +883,55 @@ def test_trace_ranges_leave_results_unchanged(monkeypatch):
     assert np.array_equal(traced.outs, plain.outs)
     assert np.array_equal(traced.sets, plain.sets) and np.array_equal(traced.cnts, plain.cnts)
     assert traced.focal == plain.focal
+
+
+def test_hand_worked_trajectory_on_gpu():
+    # the hand-worked trajectory of tests/golden/trajectory_two_focal.yaml
+    # (exact rational outputs, sets and focal layers) run by the library in
+    # fp32 with head_dim 64 (the fixture's 8-dimensional rows zero-padded)
+    import os
+    from fractions import Fraction
+
+    import yaml
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "trajectory_two_focal.yaml")
+    fx = yaml.safe_load(open(path))
+    L, S, n, P, D = fx["layers"], fx["rows"], fx["n_img"], fx["prompt"], 64
+    ex = fx["expect"]
+    K = torch.zeros((1, 1, S, D), device=DEV)
+    V = torch.zeros((1, 1, S, D), device=DEV)
+    for j in range(S):
+        K[0, 0, j, j] = 1.0
+        V[0, 0, j, :3] = torch.tensor([j + 1, (j + 1) ** 2, 1.0])
+    h = fo.fastocr_create(fo.Config(num_layers=L, num_q_heads=1, num_kv_heads=1, head_dim=D, batch=1,
+                                    max_seq_len=S, max_img_tokens=n, tau=fx["tau"], num_focal=fx["num_focal"],
+                                    warmup_steps=fx["warmup_steps"], dtype="f32", sm_scale=1.0))
+    sel = torch.zeros((1, fo.fastocr_get_info(h)["k_max"]), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    out = torch.empty((1, 1, D), device=DEV)
+    for t, per_layer in enumerate(fx["weights"]):
+        length = n + P + t + 1
+        if t == fx["warmup_steps"]:
+            assert fo.fastocr_profile_warmup(h) == ex["focal"]
+            ratios = fo.fastocr_get_layer_ratios(h)
+            np.testing.assert_allclose(ratios, [float(Fraction(r)) for r in ex["ratios"]], rtol=0, atol=1e-6)
+            fo.fastocr_get_selection(h, sel, cnt)
+            assert sel[0, :int(cnt.item())].tolist() == ex["warm_start"][0]
+        lens = torch.tensor([[n, length]], dtype=torch.int32, device=DEV)
+        for l in range(L):
+            q = torch.zeros((1, 1, D), device=DEV)
+            q[0, 0, :length] = torch.log(torch.tensor(per_layer[l], dtype=torch.float64)).float()
+            fo.fastocr_attend(h, l, q, K, V, lens, out)
+            want = [float(Fraction(x)) for x in ex["outs"][t][l]]
+            got = out[0, 0, :3].cpu().numpy()
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * max(1.0, max(abs(w) for w in want)))
+            assert float(out[0, 0, 3:].abs().max()) == 0.0
+            if t > 0:
+                fo.fastocr_get_selection(h, sel, cnt)
+                got_set = sel[0, :int(cnt.item())].tolist()
+                focal_sets = ex["sets"][t - 1]
+                used = ex["used_sets"][t - 1]
+                if l in focal_sets:
+                    assert got_set == focal_sets[l], (t, l, got_set)
+                else:
+                    assert got_set == used[l], (t, l, got_set)
+    assert fo.fastocr_get_status(h) == 0
