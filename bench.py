@@ -603,10 +603,15 @@ def main():
         for t in range(w):
             n["full_split"][0] += L
             n["full_split"][1] += L * R * float(st.lens(t)[:, 1].sum())
+        # a focal layer followed by a focal layer runs the full pass alone
+        unused = (sum(1 for l in focal if l + 1 < L and l + 1 in focal)
+                  if os.environ.get("FASTOCR_SKIP_DEAD_PICKS", "1") != "0" else 0)
         for t in pruned_steps:
             ln = st.lens(t)[:, 1].astype(np.int64)
-            n["focal_split"][0] += C
-            n["focal_split"][1] += C * R * float(ln.sum())
+            n["focal_split"][0] += C - unused
+            n["focal_split"][1] += (C - unused) * R * float(ln.sum())
+            n["full_split"][0] += unused
+            n["full_split"][1] += unused * R * float(ln.sum())
             other = "full_split" if wl.tau >= 1.0 else "sparse_split"
             rows = ln.sum() if wl.tau >= 1.0 else (kb + ln - n_img).sum()
             n[other][0] += L - C

@@ -102,6 +102,7 @@ struct fastocr_handle {
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
+  bool skip_dead_picks = true;         // a focal layer followed by a focal layer picks nothing
   Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
@@ -516,6 +517,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
                    !h->sparse_pipe;
   h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
   if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
+  h->skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
   // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
   // of at most kValuMaxGroup heads), to measure what the matrix cores buy
   h->valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 &&
@@ -645,9 +647,11 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
   const size_t BH = (size_t)c.batch * c.num_q_heads;
   char label[96] = "";
   if (h->roctx.push) {
-    const char* kind = h->phase == PHASE_FULL      ? "full"
-                       : h->phase == PHASE_WARMUP  ? "warm-up"
-                       : h->is_focal[layer]        ? "focal"
+    const bool dead = h->skip_dead_picks && layer + 1 < c.num_layers && h->is_focal[layer + 1];
+    const char* kind = h->phase == PHASE_FULL              ? "full"
+                       : h->phase == PHASE_WARMUP          ? "warm-up"
+                       : h->is_focal[layer] && dead        ? "focal-unused-pick"
+                       : h->is_focal[layer]                ? "focal"
                        : h->keeps_all              ? "kept-all"
                                                    : "kept-token";
     std::snprintf(label, sizeof(label), "fastocr step %d layer %d %s", h->step, layer, kind);
@@ -671,7 +675,11 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
       break;
     }
     case PHASE_PRUNED:
-      if (h->is_focal[layer]) {
+      if (h->is_focal[layer] && h->skip_dead_picks && layer + 1 < c.num_layers && h->is_focal[layer + 1]) {
+        // the next layer is focal too and replaces this layer's pick before
+        // any layer attends with it: the full pass alone gives every output
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
+      } else if (h->is_focal[layer]) {
         rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores, true);
       } else if (h->keeps_all) {
         // tau = 1 keeps every image token: the kept set plus the text is the

@@ -50,6 +50,10 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
+ *   FASTOCR_SKIP_DEAD_PICKS=0|1  a focal layer directly followed by another
+ *                           focal layer skips its scores and top-k (default 1;
+ *                           the outputs and the kept sets any layer uses are
+ *                           the same either way)
  *   FASTOCR_TRACE=0|1       a named roctx range around every fastocr_attend
  *                           call ("fastocr step S layer L <kind>") and the
  *                           focal-layer profile, for rocprofv3 --marker-trace
@@ -179,7 +183,10 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
  *   PRUNED mode, pruned step, layer in C: full attention, then per sequence
  *            the head-summed attention probability of every image token, then
  *            the k_b = clamp(ceil(tau*n_img_b - 1e-9), 1, n_img_b) highest
- *            (ties to the lower index) replace the kept set.
+ *            (ties to the lower index) replace the kept set.  When layer + 1
+ *            is in C too, that pick would be replaced before any layer
+ *            attends with it, so only the full attention runs (set
+ *            FASTOCR_SKIP_DEAD_PICKS=0 to compute it anyway).
  *   PRUNED mode, pruned step, layer not in C: attention over the kept set
  *            plus rows [n_img_b, len_b).
  * The first window ends with fastocr_profile_warmup.  A re-selection window
@@ -243,8 +250,9 @@ int fastocr_get_status(fastocr_handle* h, int32_t* flags);
  * [B, k_max] (ascending, first cnt entries valid) and cnt_dev int32 [B]. */
 int fastocr_get_selection(fastocr_handle* h, int32_t* idx_dev, int32_t* cnt_dev);
 
-/* Enqueues a device-to-device copy of the last focal layer's image-token
- * scores, float [B, max_img_tokens] (entries >= n_img_b are unspecified). */
+/* Enqueues a device-to-device copy of the image-token scores of the last
+ * focal layer that picked a kept set, float [B, max_img_tokens] (entries >=
+ * n_img_b are unspecified). */
 int fastocr_get_scores(fastocr_handle* h, float* scores_dev);
 
 /* After fastocr_profile_warmup: the L per-layer mean image-attention ratios

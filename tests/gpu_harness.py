@@ -27,6 +27,17 @@ TOL = {"f32": (1e-5, None), "bf16": (2e-2, 1e-2)}
 SET_BAND = 1e-3
 
 
+def unused_picks(focal, num_layers) -> set:
+    """Focal layers whose pick the next (focal) layer replaces before any
+    layer uses it: the library runs only their full attention (unless
+    FASTOCR_SKIP_DEAD_PICKS=0), so they have outputs but no scores or set."""
+    import os
+    if os.environ.get("FASTOCR_SKIP_DEAD_PICKS", "1") == "0" or focal is None or len(focal) == 0:
+        return set()
+    f = set(int(x) for x in focal)
+    return {l for l in f if l + 1 < num_layers and l + 1 in f}
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -225,12 +236,15 @@ class Checker:
         wl, up, rec = self.up.wl, self.up, self.rec
         lens = up.st.lens(t)
         focal = rec.focal
+        unused = unused_picks(focal, wl.num_layers)
         for l in range(wl.num_layers):
             K, V = up.kv64(l)
             ql = self.q(l, t)
             for b in range(wl.batch):
                 n, length = int(lens[b, 0]), int(lens[b, 1])
-                if l in focal:
+                if l in unused:
+                    out, _ = full_attention(ql[b], K[b], V[b], length, self.scale)
+                elif l in focal:
                     out, p = full_attention(ql[b], K[b], V[b], length, self.scale)
                     s = image_scores(p, n, self.rows(b))
                     slot = focal.index(l)

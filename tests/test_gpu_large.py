@@ -27,7 +27,7 @@ from oracle import (choose_focal_layers, full_attention, image_mass, image_score
                     select_top, sparse_attention)
 from workload import DeviceGenerator, get_workload, make_structure
 
-from gpu_harness import check_out, check_scores, check_set, log
+from gpu_harness import check_out, check_scores, check_set, log, unused_picks
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,7 @@ def check_sampled(run, sample_steps, ratio_layers, nonfocal_sample):
     L, B, w = wl.num_layers, wl.batch, wl.warmup_steps
     scale = 1.0 / math.sqrt(wl.head_dim)
     deepest = max(focal)
+    unused = unused_picks(focal, L)
     layers = sorted(set(ratio_layers) | set(focal) | set(nonfocal_sample) | {0})
     oracle_ratio = {}
     warm_scores_deepest = []
@@ -137,7 +138,9 @@ def check_sampled(run, sample_steps, ratio_layers, nonfocal_sample):
             r = rec[t]
             for b in range(B):
                 n, length = int(lens[b, 0]), int(lens[b, 1])
-                if l in focal:
+                if l in unused:
+                    out, _ = full_attention(q[b], K[b], V[b], length, scale)
+                elif l in focal:
                     out, p = full_attention(q[b], K[b], V[b], length, scale)
                     s = image_scores(p, n)
                     check_scores(r["scores"][focal.index(l), b, :n], s, f"scores t={t} l={l} b={b}")
