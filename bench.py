@@ -1,10 +1,12 @@
 """Decode-step attention benchmark of the FastOCR library on one MI355X.
 
-Workload (default): Qwen2.5-VL-7B-like decode attention, batch 1, 28 layers,
-28 query / 4 KV heads, head_dim 128, bf16 KV cache, 6400 image tokens (80x80
-page) + 64 prompt tokens, tau = 0.05, w = 8 warm-up steps, |C| = 4 focal
-layers; synthetic seeded inputs (K, V ~ N(0,1); queries follow a 3x5 fixation
-window that moves one cell per step).
+Workload (default): the 72B-like configuration at tau = 0.05 -- 80 layers,
+64 query / 8 KV heads, head_dim 128, batch 8, bf16 KV cache, 12800 image
+tokens (80x160 page) + 128 prompt tokens + 2048 decode steps, w = 8 warm-up
+steps, |C| = 8 focal layers; synthetic seeded inputs (K, V ~ N(0,1); queries
+follow a 3x5 fixation window that moves one cell per step).  The other
+workloads (7b-b1, 7b-b16-ragged, 32b-b4-longpage, other tau / sigma of the
+72B-like sweep) run with --workload / --tau / --sigma.
 
 A timed step is one decode step of the method through all layers: focal
 layers (full attention + image-logit export + combine + head-summed scores +
@@ -44,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="7b-b1")
+    ap.add_argument("--workload", default="72b-b8-sweep")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
@@ -84,6 +86,10 @@ CAL_BYTES = 256 << 20
 # summaries taken with other sources no longer describe the launches
 LIBRARY_SRC = [os.path.join(ROOT, "dynamic_kv_cache_amd", "csrc", f)
                for f in ("kernels.hip", "fastocr_api.cpp", "internal.h")]
+# rates of the read probe: the buffer it cycles through (far above the 256 MB
+# MALL, so every read comes from HBM) and the read sizes of the curve
+PROBE_BUFFER = 2 << 30
+PROBE_SIZES_MB = (1, 2, 4, 8, 16, 32, 64)
 
 
 def library_source_digest():
@@ -529,8 +535,25 @@ def main():
             log("warning: the spin may have ended before a chunk was enqueued; kernel times include idle gaps")
         return kt, len(steps) - 1
 
+    def record_step(h, t, focal):
+        k_max = fo.fastocr_get_info(h)["k_max"]
+        rec = {"t": t, "outs": torch.empty((L, B, Hq, d), dtype=io, device=dev),
+               "sel": torch.zeros((L, B, k_max), dtype=torch.int32, device=dev),
+               "cnt": torch.zeros((L, B), dtype=torch.int32, device=dev)}
+        with torch.cuda.stream(stream):
+            for l in range(L):
+                if l not in focal:
+                    fo.fastocr_get_selection(h, rec["sel"][l], rec["cnt"][l])
+                fo.fastocr_attend(h, l, q_at(t)[l], Kd[l], Vd[l], lens_at(t), rec["outs"][l])
+                if l in focal:
+                    fo.fastocr_get_selection(h, rec["sel"][l], rec["cnt"][l])
+        torch.cuda.synchronize()
+        return {"t": t, "outs": rec["outs"].float().cpu().numpy().astype(np.float64),
+                "sel": rec["sel"].cpu().numpy(), "cnt": rec["cnt"].cpu().numpy()}
+
     results = {}
     outs = {}
+    recorded = None
     for mode in (["pruned"] if args.profile_only else ["pruned", "full"]):
         h = make(mode)
         with torch.cuda.stream(stream):
@@ -542,6 +565,7 @@ def main():
                 p0 = time.perf_counter()
                 focal = fo.fastocr_profile_warmup(h)
                 profile_ms = (time.perf_counter() - p0) * 1e3
+                gpu_ratios = fo.fastocr_get_layer_ratios(h)
             for t in range(w, t_timed):  # untimed steps
                 eager_step(h, t, out_stage)
         torch.cuda.synchronize()
@@ -563,6 +587,11 @@ def main():
             r["append_separate_ms"] = time_append(h, phase_steps["append_separate"], 0, False)
             r["append_fused_ms"] = time_append(h, phase_steps["append_fused"], K, True)
         outs[mode] = out_hist.float()
+        if mode == "pruned" and not args.profile_only:
+            # one more step, eager and recorded, for the oracle check beside
+            # the CPU baseline: every layer's output, the set each non-focal
+            # layer attends with and the set each focal layer picks
+            recorded = record_step(h, phase_steps["events"][-1], focal)
         fo.fastocr_destroy(h)
         results[mode] = r
         log(f"{mode}: {r['step_ms']:.4f} ms/step ({'eager' if args.no_graph else 'graph'})")
@@ -718,13 +747,21 @@ def main():
         over = (w * (results["full"]["step_ms"] - pr_ms) + profile_ms) / (R + w)
         extra["reselection"] = {"profile_call_us": round(profile_ms * 1e3, 1), "every_R": R,
                                 "amortized_us_per_step": round(over * 1e3, 2)}
+    if focal is not None and len(focal) < L:
+        # how clearly the warm-up separates the focal layers: the gap between
+        # the |C|-th and the (|C|+1)-th layer's image-attention ratio
+        ranked = sorted(gpu_ratios, reverse=True)
+        C = len(focal)
+        extra["focal_margin"] = {"ratio_C": round(ranked[C - 1], 7), "ratio_next": round(ranked[C], 7),
+                                 "abs": float(f"{ranked[C - 1] - ranked[C]:.3e}"),
+                                 "rel": float(f"{(ranked[C - 1] - ranked[C]) / ranked[C - 1]:.3e}")}
     if not args.profile_only:
         extra["pack_image_first"] = pack_probe(torch, fo, Kd, Vd, st.n_img, stream)
-        extra["platform"] = platform_probe(torch, stream)
+        extra["platform"] = platform_probe(torch, fo, stream)
 
     cpu = None
     if args.cpu_seconds > 0 and not args.profile_only:
-        cpu = cpu_baseline(wl, st, Kd, Vd, Qall, used, focal, args.cpu_seconds)
+        cpu, extra["oracle_check"] = cpu_baseline(wl, st, Kd, Vd, Qall, slot, focal, args.cpu_seconds, recorded)
 
     if args.profile_only:
         extra["alg_bytes_per_launch_run"] = run_alg_bytes()
@@ -784,11 +821,29 @@ def pack_probe(torch, fo, Kd, Vd, n_img, stream):
             "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
 
 
-def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):
+def platform_probe(torch, fo, stream, launches=200, copy_bytes=1 << 30):
     """Context for the kernel times: the per-launch floor of back-to-back
-    graph-replayed null kernels, and a device-to-device copy rate."""
+    graph-replayed null kernels, a device-to-device copy rate, the HBM read
+    rate of the library's stream-read probe over 1 GiB, and the probe's time
+    per launch for reads of 1-64 MB (graph-replayed back to back, each launch
+    reading a region no earlier launch of the series read, so it comes from
+    HBM and not from the MALL)."""
     out = {}
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def best_replay(g, reps=4):
+        best = None
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                a, b = ev(), ev()
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                t = a.elapsed_time(b)
+                best = t if best is None else min(best, t)
+        return best
+
     try:
         with torch.cuda.stream(stream):
             torch.cuda._sleep(0)
@@ -797,17 +852,7 @@ def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):
         with torch.cuda.graph(g, stream=stream):
             for _ in range(launches):
                 torch.cuda._sleep(0)
-        best = None
-        with torch.cuda.stream(stream):
-            for _ in range(4):
-                a, b = ev(), ev()
-                a.record(stream)
-                g.replay()
-                b.record(stream)
-                torch.cuda.synchronize()
-                t = a.elapsed_time(b)
-                best = t if best is None else min(best, t)
-        out["null_kernel_graph_us"] = round(best * 1e3 / launches, 3)
+        out["null_kernel_graph_us"] = round(best_replay(g) * 1e3 / launches, 3)
         del g
     except RuntimeError as exc:  # the spin kernel could not be captured
         out["null_kernel_graph_us"] = None
@@ -827,81 +872,175 @@ def platform_probe(torch, stream, launches=200, copy_bytes=1 << 30):
     out["copy_GBps"] = round(2 * copy_bytes / (best * 1e-3) / 1e9, 1)  # read + write
     out["copy_MiB"] = copy_bytes >> 20
     del src, dst
+
+    # stream-read probe
+    buf = torch.ones(PROBE_BUFFER // 8, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    torch.cuda.synchronize()
+
+    def series(nbytes, wgs, count):
+        """Per-launch ms of `count` graph-replayed probe launches of `nbytes`
+        each, at successive offsets of the buffer."""
+        g = torch.cuda.CUDAGraph()
+        step = nbytes // 8
+        with torch.cuda.stream(stream):
+            fo.fastocr_probe_read(buf, nbytes, wgs, sink, stream=stream)  # first launch outside the graph
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(count):
+                off = (i * step) % (buf.numel() - step + 1)
+                fo.fastocr_probe_read(buf[off:], nbytes, wgs, sink, stream=stream)
+        torch.cuda.synchronize()
+        ms = best_replay(g, reps=3) / count
+        del g
+        return ms
+
+    peak = {}
+    for per_cu in (2, 4, 8):
+        ms = series(1 << 30, per_cu * num_cu, 2)
+        peak[per_cu] = (1 << 30) / (ms * 1e-3) / 1e9
+    best_cu = max(peak, key=peak.get)
+    out["read_probe_GBps"] = round(peak[best_cu], 1)
+    out["read_probe_workgroups_per_cu"] = best_cu
+    curve = {}
+    for mb in PROBE_SIZES_MB:
+        nbytes = mb << 20
+        count = max(8, min(64, (PROBE_BUFFER // nbytes)))
+        best = None
+        for wgs in sorted({max(1, min(8 * num_cu, nbytes // (256 * 16))),
+                           max(1, min(8 * num_cu, nbytes // (256 * 64))), 2 * num_cu}):
+            ms = series(nbytes, wgs, count)
+            if best is None or ms < best[0]:
+                best = (ms, wgs)
+        curve[f"{mb}MB"] = {"us_per_launch": round(best[0] * 1e3, 2),
+                            "GBps": round(nbytes / (best[0] * 1e-3) / 1e9, 1), "workgroups": best[1]}
+    out["read_curve"] = curve
+    del buf, sink
     return out
 
 
-def cpu_baseline(wl, st, Kd, Vd, Qall, used, focal_gpu, budget_s):
-    """The CPU oracle, as written, timed on a bounded sample of the same run.
-
-    Whole decode steps when every layer's cache fits comfortably in host
-    memory as float64 (the 7B-like workloads); otherwise one focal and one
-    non-focal layer of one pruned step are timed and the step time is
-    extrapolated to all layers.  Qall[i] holds the queries of decode step
-    used[i] (the warm-up steps first, in order).
-    """
+def host_cpu():
+    """(nproc, CPU model name, BLAS threads) of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    from oracle import DecodeOracle, full_attention, sparse_attention, image_scores, kept_count, select_top
+    return os.cpu_count(), model, threads
 
-    L = wl.num_layers
-    host = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    layer_bytes = Kd[0].numel() * 8 * 2
-    if L * layer_bytes < 4e9:
-        kv64 = [(host(k), host(v)) for k, v in zip(Kd, Vd)]
-        q_of = lambda i: (lambda l: host(Qall[i, l]))  # noqa: E731
-        orc = DecodeOracle(num_layers=L, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
-                           head_dim=wl.head_dim, tau=wl.tau, num_focal=wl.num_focal,
-                           warmup_steps=wl.warmup_steps)
-        t0 = time.time()
-        for t in range(wl.warmup_steps):
-            orc.step(t, q_of(t), lambda l: kv64[l], st.lens(t))
-        warm_s = time.time() - t0
-        times = []
-        i = wl.warmup_steps  # pruned steps in the order the GPU ran them
-        begin = time.time()
-        while time.time() - begin < budget_s and i < len(used):
-            s0 = time.time()
-            orc.step(used[i], q_of(i), lambda l: kv64[l], st.lens(used[i]))
-            times.append(time.time() - s0)
-            i += 1
-        us = float(np.median(times)) * 1e6 if times else None
-        log(f"cpu oracle: warm-up {warm_s:.1f}s, {len(times)} pruned steps, median {us:.0f} us/step, "
-            f"focal {[int(c) for c in orc.focal]} (gpu {focal_gpu})")
-        sample = (f"float64 numpy oracle: {wl.warmup_steps} warm-up steps then {len(times)} pruned "
-                  f"decode steps (all {L} layers; the GPU run's steps in its order) of the same "
-                  f"workload; median per pruned step")
-    else:
-        t = wl.warmup_steps
-        lens = st.lens(t)
-        scale = 1.0 / math.sqrt(wl.head_dim)
-        lf = int(focal_gpu[0])
-        ln = next(l for l in range(L) if l not in focal_gpu)
-        Kf, Vf, qf = host(Kd[lf]), host(Vd[lf]), host(Qall[t, lf])
-        s0 = time.time()
-        sets = []
-        for b in range(wl.batch):
+
+def cpu_baseline(wl, st, Kd, Vd, Qall, slot, focal_gpu, budget_s, recorded):
+    """The CPU oracle, as written, timed on a bounded sample of the same run,
+    and the oracle's check of one recorded GPU step.
+
+    The sample is the recorded decode step's layers, focal layers that pick a
+    kept set and non-focal layers alternately (spread over the depth), until
+    `budget_s` seconds of float64 oracle work: a focal layer is full
+    attention + head-summed scores + top-k, a non-focal layer is attention
+    over the kept set the GPU attended with.  The step time is the sum over
+    all layers of the median time of their kind.  The same layers then run in float32 for the float32 figure.
+    Reading a layer's cache back and converting it is not timed.
+
+    The check: every sampled layer's GPU output against the float64 oracle
+    (non-focal layers conditioned on the GPU's set), and for focal layers the
+    Jaccard overlap of the GPU's kept set with the oracle's own set (the
+    oracle's unconditioned pick: a focal layer picks from the full cache).
+    """
+    from oracle import full_attention, image_scores, kept_count, select_top, sparse_attention
+
+    nproc, model, threads = host_cpu()
+    L, B = wl.num_layers, wl.batch
+    t = recorded["t"]
+    lens = st.lens(t)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    focal = [int(x) for x in focal_gpu]
+    unused = {l for l in focal if l + 1 < L and l + 1 in focal}
+    picking = [l for l in focal if l not in unused]
+    nonfocal = [l for l in range(L) if l not in focal]
+    # non-focal layers in an order that spreads a short sample over the depth
+    spread, stride = [], max(1, len(nonfocal) // 8)
+    for start in range(stride):
+        spread += nonfocal[start::stride]
+    order = []
+    for i in range(max(len(picking), len(spread))):
+        order += ([("focal", picking[i])] if i < len(picking) else []) + \
+                 ([("sparse", spread[i])] if i < len(spread) else [])
+
+    def run_layer(kind, l, K, V, q, dtype):
+        outs, sets = [], []
+        for b in range(B):
             n, length = int(lens[b, 0]), int(lens[b, 1])
-            _, p = full_attention(qf[b], Kf[b], Vf[b], length, scale)
-            sets.append(select_top(image_scores(p, n), kept_count(wl.tau, n)))
-        t_focal = time.time() - s0
-        del Kf, Vf
-        Kn, Vn, qn = host(Kd[ln]), host(Vd[ln]), host(Qall[t, ln])
-        s0 = time.time()
-        for b in range(wl.batch):
-            n, length = int(lens[b, 0]), int(lens[b, 1])
-            sparse_attention(qn[b], Kn[b], Vn[b], sets[b], n, length, scale)
-        t_sparse = time.time() - s0
-        C = len(focal_gpu)
-        us = (C * t_focal + (L - C) * t_sparse) * 1e6
-        log(f"cpu oracle (sampled layers): focal layer {t_focal:.2f}s, non-focal layer {t_sparse:.2f}s, "
-            f"step estimate {us / 1e6:.1f}s")
-        sample = (f"float64 numpy oracle on one focal and one non-focal layer of pruned step "
-                  f"{t}, extrapolated to {C} focal + {L - C} non-focal layers")
-    return {"value": round(us, 1) if us else None, "unit": "us/step", "cores": threads,
-            "kind": "oracle", "sample": sample}
+            if kind == "focal":
+                out, p = full_attention(q[b], K[b], V[b], length, scale, dtype)
+                sets.append(select_top(image_scores(p, n), kept_count(wl.tau, n)))
+            else:
+                c = int(recorded["cnt"][l, b])
+                out = sparse_attention(q[b], K[b], V[b], recorded["sel"][l, b, :c], n, length, scale,
+                                       dtype=dtype)
+            outs.append(out)
+        return np.stack(outs), sets
+
+    times = {np.float64: {"focal": [], "sparse": []}, np.float32: {"focal": [], "sparse": []}}
+    worst_abs, worst_rel, jac, checked = 0.0, 0.0, [], []
+    spent = 0.0
+    for kind, l in order:
+        if spent > budget_s and times[np.float64]["focal"] and times[np.float64]["sparse"]:
+            break
+        K = Kd[l].float().cpu().numpy()
+        V = Vd[l].float().cpu().numpy()
+        q = Qall[slot[t], l].float().cpu().numpy()
+        for dtype in (np.float64, np.float32):
+            Kc, Vc, qc = K.astype(dtype), V.astype(dtype), q.astype(dtype)
+            s0 = time.perf_counter()
+            out, sets = run_layer(kind, l, Kc, Vc, qc, dtype)
+            dt = time.perf_counter() - s0
+            times[dtype][kind].append(dt)
+            if dtype is np.float64:
+                spent += dt
+                got = recorded["outs"][l]
+                worst_abs = max(worst_abs, float(np.abs(got - out).max()))
+                worst_rel = max(worst_rel, float(np.linalg.norm(got - out) / max(np.linalg.norm(out), 1e-30)))
+                checked.append(l)
+                for b, want in enumerate(sets):
+                    gpu = set(int(j) for j in recorded["sel"][l, b, :int(recorded["cnt"][l, b])])
+                    ours = set(int(j) for j in want)
+                    jac.append(len(gpu & ours) / max(len(gpu | ours), 1))
+            del Kc, Vc, qc
+        del K, V
+
+    def step_us(tt):
+        med = {k: float(np.median(v)) for k, v in tt.items() if v}
+        f = med.get("focal", med.get("sparse"))
+        n_ = med.get("sparse", f)
+        return (len(focal) * f + (L - len(focal)) * n_) * 1e6
+
+    us64, us32 = step_us(times[np.float64]), step_us(times[np.float32])
+    n_f, n_s = len(times[np.float64]["focal"]), len(times[np.float64]["sparse"])
+    log(f"cpu oracle: {n_f} focal + {n_s} non-focal layers of step {t}; step estimate float64 "
+        f"{us64 / 1e3:.1f} ms, float32 {us32 / 1e3:.1f} ms; {nproc} CPUs ({model}), BLAS threads {threads}")
+    sample = (f"float64 numpy oracle on {n_f} focal and {n_s} non-focal layers of decode step {t} "
+              f"(focal: full attention + scores + top-k; non-focal: attention over the GPU's kept set), "
+              f"step = {len(focal)} focal + {L - len(focal)} non-focal layers at the median time of their kind")
+    cpu = {"value": round(us64, 1), "unit": "us/step", "cores": threads, "kind": "oracle", "sample": sample,
+           "nproc": nproc, "cpu_model": model, "blas_threads": threads,
+           "float32_value": round(us32, 1), "layers_timed": n_f + n_s}
+    tol_abs, tol_rel = (2e-2, 1e-2) if wl.dtype == "bf16" else (1e-5, None)
+    check = {"step": t, "layers": checked, "max_abs_err": float(f"{worst_abs:.3e}"),
+             "max_rel_l2": float(f"{worst_rel:.3e}"), "tolerance_abs": tol_abs, "tolerance_rel_l2": tol_rel,
+             "within_tolerance": bool(worst_abs <= tol_abs and (tol_rel is None or worst_rel <= tol_rel)),
+             "jaccard_vs_oracle_sets": round(float(np.mean(jac)), 4) if jac else None,
+             "focal_sets_compared": len(jac)}
+    return cpu, check
 
 
 if __name__ == "__main__":

@@ -202,6 +202,14 @@ def fastocr_get_info(h: Handle) -> Dict[str, int]:
     return {f: getattr(info, f) for f, _ in _abi.Info._fields_}
 
 
+def fastocr_plan_launch(cfg: Config, num_cu: int = 256) -> Dict[str, int]:
+    """The launch plan fastocr_create would choose for cfg (host only)."""
+    c = cfg.to_c()
+    info = _abi.Info()
+    _check("fastocr_plan_launch", lib().fastocr_plan_launch(ctypes.byref(c), int(num_cu), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in _abi.Info._fields_}
+
+
 def fastocr_get_selection(h: Handle, idx, cnt) -> None:
     t = _torch()
     info = fastocr_get_info(h)
@@ -303,6 +311,19 @@ def fastocr_pack_rows(src, dst, row_map, rows, status=None, stream=None) -> None
         int(B), int(Hkv), int(S), int(d), dtype,
         ctypes.c_void_p(0 if status is None else _dev_ptr(status, t.int32, (1,), "status", 4)),
         ctypes.c_void_p(_stream_ptr(stream))))
+
+
+def fastocr_probe_read(buf, nbytes: int, workgroups: int, sink, stream=None) -> None:
+    """Read `nbytes` of the device tensor `buf` (from its start) with a
+    stream-read kernel; sink: device int32 tensor of 64 entries."""
+    t = _torch()
+    if not isinstance(buf, t.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if nbytes > buf.numel() * buf.element_size() or buf.data_ptr() % 16:
+        raise ValueError("nbytes exceeds buf, or buf is not 16-byte aligned")
+    _check("fastocr_probe_read", lib().fastocr_probe_read(
+        ctypes.c_void_p(buf.data_ptr()), int(nbytes), int(workgroups),
+        ctypes.c_void_p(_dev_ptr(sink, t.int32, (64,), "sink", 4)), ctypes.c_void_p(_stream_ptr(stream))))
 
 
 def fastocr_kept_count(tau: float, n_img: int) -> int:

@@ -94,6 +94,7 @@ SIGNATURES = [
     ("fastocr_set_focal_layers", c_int32, [c_void_p, ctypes.POINTER(c_int32), c_int32]),
     ("fastocr_set_selection", c_int32, [c_void_p, c_void_p, c_void_p]),
     ("fastocr_get_info", c_int32, [c_void_p, ctypes.POINTER(Info)]),
+    ("fastocr_plan_launch", c_int32, [ctypes.POINTER(Config), c_int32, ctypes.POINTER(Info)]),
     ("fastocr_set_timing", c_int32, [c_void_p, c_int32]),
     ("fastocr_get_timing", c_int32, [c_void_p, ctypes.POINTER(Timing)]),
     ("fastocr_reset_timing", c_int32, [c_void_p]),
@@ -105,6 +106,7 @@ SIGNATURES = [
     ("fastocr_image_first_map", c_int32, [ctypes.POINTER(c_int32), c_int32, c_int32, ctypes.POINTER(c_int32)]),
     ("fastocr_pack_rows", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_void_p, c_void_p]),
+    ("fastocr_probe_read", c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
     ("fastocr_kept_count", c_int32, [c_double, c_int32]),
     ("fastocr_choose_focal_layers", c_int32, [ctypes.POINTER(c_double), c_int32, c_int32,
                                               ctypes.POINTER(c_int32)]),

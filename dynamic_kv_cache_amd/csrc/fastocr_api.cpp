@@ -89,6 +89,140 @@ int plan_rows_per_split(int64_t pairs, int rows, int target, int max_splits, con
   return R;
 }
 
+// Launch geometry and scratch layout of a handle: a function of its
+// configuration, the device's compute-unit count and the FASTOCR_*
+// environment overrides alone (no device use).
+struct Plan {
+  int n_cap = 0, n_stride = 0, k_max = 0;
+  int full_R = 0, full_splits = 0, full_sure = 0;  // sure: splits that hold rows for any accepted sequence
+  int sparse_R = 0, sparse_splits = 0, sparse_sure = 0;
+  bool wave_states = false;      // kept-token splits write one state per wave
+  bool sparse_pipe = false;      // kept-token passes run pipelined multi-round splits
+  bool keeps_all = false;        // tau = 1: non-focal layers run the full pass
+  bool valu_full = false;        // full passes run the VALU variant (measurement override)
+  bool skip_dead_picks = true;   // a focal layer followed by a focal layer picks nothing
+  int states_per_sparse_split = 1;
+  int max_splits = 0;            // merge states per head the scratch holds
+  // scratch arena: byte offsets of each array, and the total
+  size_t o_pstat = 0, o_po = 0, o_logits = 0, o_mz = 0, o_scores = 0, o_warm = 0, o_tm = 0, o_sel = 0,
+         o_cnt = 0, o_status = 0, o_lens = 0, o_hist0 = 0, arena_bytes = 0;
+};
+
+bool config_ok(const fastocr_config& c);
+int32_t kept_count_host(double tau, int32_t n_img);
+
+// FASTOCR_OK, or FASTOCR_ERR_INVALID_ARG for a configuration whose launches
+// cannot be planned.
+int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
+  if (!config_ok(c) || num_cu < 1) return FASTOCR_ERR_INVALID_ARG;
+  const int G = c.num_q_heads / c.num_kv_heads;
+  p = Plan{};
+  p.n_cap = c.max_img_tokens;
+  p.n_stride = (int)align_up((size_t)std::max(c.max_img_tokens, 1), 4);
+  p.k_max = std::max(kept_count_host(c.tau, c.max_img_tokens), 1);
+  const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
+  // about one wave of resident split workgroups per launch
+  // A ragged batch (image counts between min_img_tokens and max_img_tokens)
+  // is planned for the middle of that range, not for the longest sequence,
+  // whose plan would leave most splits of the shorter sequences empty and
+  // fill few CUs; each pair's last split is partly empty, so the plan keeps
+  // half a workgroup per pair of the resident slots free (a launch just
+  // over the slots runs a second wave).  7B-like B=16, 2169-6682 image
+  // tokens, full step: 768-row splits (440 workgroups with rows) 1067 us,
+  // 640 (516) 1247, 1024 (336) 1178, 1152 (304) 1224.
+  int full_rows_est = c.max_seq_len;
+  int full_target = split_blocks_per_cu(KIND_FULL) * num_cu;
+  if (c.min_img_tokens > 0 && c.min_img_tokens < c.max_img_tokens) {
+    full_rows_est = (c.min_img_tokens + c.max_img_tokens) / 2 + (c.max_seq_len - c.max_img_tokens);
+    full_target = (int)std::max<int64_t>(full_target - pairs / 2, full_target / 2);
+  }
+  p.full_R = plan_rows_per_split(pairs, full_rows_est, full_target, kMaxMergeSplits, "FASTOCR_FULL_ROWS");
+  while ((c.max_seq_len + p.full_R - 1) / p.full_R > kMaxMergeSplits) p.full_R += kRowsPerRound;
+  p.full_splits = (c.max_seq_len + p.full_R - 1) / p.full_R;
+  // rows of a kept-token pass: kept image rows + text rows
+  int sparse_rows = c.max_seq_len;
+  if (c.min_img_tokens > 0)
+    sparse_rows = std::min(sparse_rows, p.k_max + c.max_seq_len - c.min_img_tokens);
+  if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, p.k_max + c.max_text_tokens);
+  // Kept-token passes: one round per split, the most workgroups, dispatched
+  // split-major (measured faster than fewer, longer splits at every batch),
+  // or, pipelined, splits sized like a full pass's (whole rounds, about one
+  // wave of resident workgroups, at most kMaxPipeRows rows).
+  // Pipelined when the kept rows of all (sequence, KV head) pairs reach
+  // 64 x 2048: measured 2837 against 3104 us per step at 72B-like B=8,
+  // tau = 0.2 (2560 kept rows), but slower at tau <= 0.1 and at every
+  // smaller configuration.
+  const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
+  const bool pipe_default = pairs * (int64_t)p.k_max >= 64 * 2048;
+  p.sparse_pipe = pruned && env_int("FASTOCR_SPARSE_PIPE", pipe_default ? 1 : 0) != 0;
+  if (p.sparse_pipe) {
+    int R = plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE, true) * num_cu,
+                                kMaxMergeSplits, "FASTOCR_SPARSE_ROWS");
+    R = std::min((int)align_up((size_t)R, kRowsPerRound), kMaxPipeRows);
+    // a pipelined split holds at most kMaxPipeRows rows (its row map lives
+    // in LDS); a pass that would need more than kMaxMergeSplits of them runs
+    // one-round splits instead
+    if ((sparse_rows + R - 1) / R > kMaxMergeSplits) p.sparse_pipe = false;
+    else p.sparse_R = R;
+  }
+  if (!p.sparse_pipe)
+    p.sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
+                                     "FASTOCR_SPARSE_ROWS");
+  p.sparse_splits = pruned ? (sparse_rows + p.sparse_R - 1) / p.sparse_R : 0;
+  // A kept-token pass of at most one workgroup per CU is latency-bound: its
+  // waves then write their states themselves (no cross-wave combine and
+  // barrier; measured 5.75 against 6.4 us per launch at 7B-like B=1), as
+  // long as the merge keeps one state per lane.  A larger pass streams, and
+  // there the 4x partial-output traffic costs more than the combine.
+  const bool ws_default = p.sparse_splits > 1 && pairs * p.sparse_splits <= num_cu &&
+                          p.sparse_splits * kSplitWaves <= 64;
+  p.wave_states = env_int("FASTOCR_WAVE_STATES", ws_default ? 1 : 0) != 0 && p.sparse_splits > 1 &&
+                  !p.sparse_pipe;
+  p.states_per_sparse_split = p.wave_states ? kSplitWaves : 1;
+  p.skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
+  // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
+  // of at most kValuMaxGroup heads), to measure what the matrix cores buy
+  p.valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 && c.head_dim == 128 &&
+                G <= kValuMaxGroup;
+  // k_b = n_b for every n_b exactly when tau = 1
+  p.keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
+  // state slots per head (a direct kept-token pass writes none); the merge
+  // keeps one weight per state in LDS
+  p.max_splits = std::max(p.full_splits, p.sparse_splits * p.states_per_sparse_split);
+  if (p.max_splits > kMaxMergeSplits) return FASTOCR_ERR_INVALID_ARG;
+  // Full passes: every sequence has at least min_img_tokens image rows and
+  // the current token, so splits below that hold rows and load their K/V
+  // ahead; the others (possibly empty for a short sequence of a ragged
+  // batch) wait for the extent.  Kept-token splits only load indices ahead,
+  // which costs an empty split nothing worth saving.
+  const int min_full_rows = c.min_img_tokens + 1;
+  p.full_sure = std::min((min_full_rows + p.full_R - 1) / p.full_R, p.full_splits);
+  p.sparse_sure = p.sparse_splits;
+
+  // scratch arena
+  const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers, D = c.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  p.o_pstat = take(B * Hq * p.max_splits * sizeof(float4));
+  p.o_po = take(B * Hq * p.max_splits * D * sizeof(float));
+  p.o_logits = take(pruned ? B * Hq * p.n_stride * sizeof(float) : 0);
+  p.o_mz = take(B * Hq * sizeof(float2));
+  p.o_scores = take(pruned ? B * p.n_stride * sizeof(float) : 0);
+  p.o_warm = take(pruned ? L * B * p.n_stride * sizeof(float) : 0);
+  p.o_tm = take(pruned ? L * (size_t)c.warmup_steps * B * Hq * sizeof(float) : 0);
+  p.o_sel = take(B * p.k_max * sizeof(int32_t));
+  p.o_cnt = take(B * sizeof(int32_t));
+  p.o_status = take(sizeof(int32_t));
+  p.o_lens = take(B * 2 * sizeof(int32_t));
+  p.o_hist0 = take(pruned ? B * 256 * sizeof(unsigned int) : 0);
+  p.arena_bytes = off;
+  return FASTOCR_OK;
+}
+
 }  // namespace
 
 struct fastocr_handle {
@@ -296,6 +430,17 @@ void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {
   for (int i = 0; i < num_focal; ++i) out[i] = pick[i];
 }
 
+// k = clamp(ceil(tau*n - 1e-9), 1, n) for n > 0 (tau in (0, 1]); each
+// operation rounded on its own, as the device computes it.
+int32_t kept_count_host(double tau, int32_t n_img) {
+#pragma clang fp contract(off)
+  if (n_img <= 0) return 0;
+  const double prod = tau * (double)n_img;
+  const double k = std::ceil(prod - 1e-9);
+  int32_t ki = (int32_t)k;
+  return std::min(std::max(ki, 1), n_img);
+}
+
 bool config_ok(const fastocr_config& c) {
   if (c.num_layers < 1 || c.num_kv_heads < 1 || c.num_q_heads < 1 || c.batch < 1) return false;
   if (c.num_q_heads % c.num_kv_heads != 0) return false;
@@ -402,13 +547,8 @@ StateHeader state_header(fastocr_handle* h) {
 extern "C" {
 
 int32_t fastocr_kept_count(double tau, int32_t n_img) {
-#pragma clang fp contract(off)
   if (!(tau > 0.0 && tau <= 1.0)) return FASTOCR_ERR_INVALID_ARG;
-  if (n_img <= 0) return 0;
-  const double prod = tau * (double)n_img;
-  const double k = std::ceil(prod - 1e-9);
-  int32_t ki = (int32_t)k;
-  return std::min(std::max(ki, 1), n_img);
+  return kept_count_host(tau, n_img);
 }
 
 int fastocr_choose_focal_layers(const double* ratios, int32_t num_layers, int32_t num_focal,
@@ -446,6 +586,8 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
       num_cu = prop.multiProcessorCount;
   }
 
+  Plan plan;
+  if (make_plan(*cfg, num_cu, plan) != FASTOCR_OK) return FASTOCR_ERR_INVALID_ARG;
   fastocr_handle* h = new (std::nothrow) fastocr_handle();
   if (!h) return FASTOCR_ERR_OOM;
   h->cfg = *cfg;
@@ -454,109 +596,31 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   const fastocr_config& c = h->cfg;
   h->G = c.num_q_heads / c.num_kv_heads;
   h->D = c.head_dim;
-  h->n_cap = c.max_img_tokens;
-  h->n_stride = (int)align_up((size_t)std::max(c.max_img_tokens, 1), 4);
-  h->k_max = std::max(fastocr_kept_count(c.tau, c.max_img_tokens), 1);
+  h->n_cap = plan.n_cap;
+  h->n_stride = plan.n_stride;
+  h->k_max = plan.k_max;
   const float scale = c.sm_scale > 0.f ? c.sm_scale : 1.0f / std::sqrt((float)c.head_dim);
   h->scale_log2 = scale * 1.4426950408889634f;
   h->phase = c.mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
-
-  const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
-  // about one wave of resident split workgroups per launch
-  // A ragged batch (image counts between min_img_tokens and max_img_tokens)
-  // is planned for the middle of that range, not for the longest sequence,
-  // whose plan would leave most splits of the shorter sequences empty and
-  // fill few CUs; each pair's last split is partly empty, so the plan keeps
-  // half a workgroup per pair of the resident slots free (a launch just
-  // over the slots runs a second wave).  7B-like B=16, 2169-6682 image
-  // tokens, full step: 768-row splits (440 workgroups with rows) 1067 us,
-  // 640 (516) 1247, 1024 (336) 1178, 1152 (304) 1224.
-  int full_rows_est = c.max_seq_len;
-  int full_target = split_blocks_per_cu(KIND_FULL) * num_cu;
-  if (c.min_img_tokens > 0 && c.min_img_tokens < c.max_img_tokens) {
-    full_rows_est = (c.min_img_tokens + c.max_img_tokens) / 2 + (c.max_seq_len - c.max_img_tokens);
-    full_target = (int)std::max<int64_t>(full_target - pairs / 2, full_target / 2);
-  }
-  h->full_R = plan_rows_per_split(pairs, full_rows_est, full_target, kMaxMergeSplits, "FASTOCR_FULL_ROWS");
-  while ((c.max_seq_len + h->full_R - 1) / h->full_R > kMaxMergeSplits) h->full_R += kRowsPerRound;
-  h->full_splits = (c.max_seq_len + h->full_R - 1) / h->full_R;
-  // rows of a kept-token pass: kept image rows + text rows
-  int sparse_rows = c.max_seq_len;
-  if (c.min_img_tokens > 0)
-    sparse_rows = std::min(sparse_rows, h->k_max + c.max_seq_len - c.min_img_tokens);
-  if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, h->k_max + c.max_text_tokens);
-  // Kept-token passes: one round per split, the most workgroups, dispatched
-  // split-major (measured faster than fewer, longer splits at every batch),
-  // or, pipelined, splits sized like a full pass's (whole rounds, about one
-  // wave of resident workgroups, at most kMaxPipeRows rows).
-  // Pipelined when the kept rows of all (sequence, KV head) pairs reach
-  // 64 x 2048: measured 2837 against 3104 us per step at 72B-like B=8,
-  // tau = 0.2 (2560 kept rows), but slower at tau <= 0.1 and at every
-  // smaller configuration.
-  const bool pipe_default = pairs * (int64_t)h->k_max >= 64 * 2048;
-  h->sparse_pipe = c.mode == FASTOCR_MODE_PRUNED && env_int("FASTOCR_SPARSE_PIPE", pipe_default ? 1 : 0) != 0;
-  if (h->sparse_pipe) {
-    h->sparse_R = std::min(plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE, true) * num_cu,
-                                               kMaxMergeSplits, "FASTOCR_SPARSE_ROWS"),
-                           kMaxPipeRows);
-    h->sparse_R = (int)align_up((size_t)h->sparse_R, kRowsPerRound);
-    if (h->sparse_R > kMaxPipeRows) h->sparse_R = kMaxPipeRows;
-  } else {
-    h->sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
-                                      "FASTOCR_SPARSE_ROWS");
-  }
-  h->sparse_splits = (c.mode == FASTOCR_MODE_PRUNED) ? (sparse_rows + h->sparse_R - 1) / h->sparse_R : 0;
-  // A kept-token pass of at most one workgroup per CU is latency-bound: its
-  // waves then write their states themselves (no cross-wave combine and
-  // barrier; measured 5.75 against 6.4 us per launch at 7B-like B=1), as
-  // long as the merge keeps one state per lane.  A larger pass streams, and
-  // there the 4x partial-output traffic costs more than the combine.
-  h->wave_states = h->sparse_splits > 1 && pairs * h->sparse_splits <= num_cu &&
-                   h->sparse_splits * kSplitWaves <= 64;
-  h->wave_states = env_int("FASTOCR_WAVE_STATES", h->wave_states ? 1 : 0) != 0 && h->sparse_splits > 1 &&
-                   !h->sparse_pipe;
-  h->states_per_sparse_split = h->wave_states ? kSplitWaves : 1;
+  h->full_R = plan.full_R;
+  h->full_splits = plan.full_splits;
+  h->full_sure = plan.full_sure;
+  h->sparse_R = plan.sparse_R;
+  h->sparse_splits = plan.sparse_splits;
+  h->sparse_sure = plan.sparse_sure;
+  h->wave_states = plan.wave_states;
+  h->sparse_pipe = plan.sparse_pipe;
+  h->keeps_all = plan.keeps_all;
+  h->valu_full = plan.valu_full;
+  h->skip_dead_picks = plan.skip_dead_picks;
+  h->states_per_sparse_split = plan.states_per_sparse_split;
+  h->max_splits = plan.max_splits;
   if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
-  h->skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
-  // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
-  // of at most kValuMaxGroup heads), to measure what the matrix cores buy
-  h->valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 &&
-                 c.head_dim == 128 && h->G <= kValuMaxGroup;
-  // k_b = n_b for every n_b exactly when tau = 1
-  h->keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
-  // state slots per head (a direct kept-token pass writes none)
-  h->max_splits = std::max(h->full_splits, h->sparse_splits * h->states_per_sparse_split);
-  // Full passes: every sequence has at least min_img_tokens image rows and
-  // the current token, so splits below that hold rows and load their K/V
-  // ahead; the others (possibly empty for a short sequence of a ragged
-  // batch) wait for the extent.  Kept-token splits only load indices ahead,
-  // which costs an empty split nothing worth saving.
-  const int min_full_rows = c.min_img_tokens + 1;
-  h->full_sure = std::min((min_full_rows + h->full_R - 1) / h->full_R, h->full_splits);
-  h->sparse_sure = h->sparse_splits;
-
-  // scratch arena
-  const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers, D = c.head_dim;
   const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = align_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_pstat = take(B * Hq * h->max_splits * sizeof(float4));
-  const size_t o_po = take(B * Hq * h->max_splits * D * sizeof(float));
-  const size_t o_logits = take(pruned ? B * Hq * h->n_stride * sizeof(float) : 0);
-  const size_t o_mz = take(B * Hq * sizeof(float2));
-  const size_t o_scores = take(pruned ? B * h->n_stride * sizeof(float) : 0);
-  const size_t o_warm = take(pruned ? L * B * h->n_stride * sizeof(float) : 0);
-  const size_t o_tm = take(pruned ? L * (size_t)c.warmup_steps * B * Hq * sizeof(float) : 0);
-  const size_t o_sel = take(B * h->k_max * sizeof(int32_t));
-  const size_t o_cnt = take(B * sizeof(int32_t));
-  const size_t o_status = take(sizeof(int32_t));
-  const size_t o_lens = take(B * 2 * sizeof(int32_t));
-  const size_t o_hist0 = take(pruned ? B * 256 * sizeof(unsigned int) : 0);
-  h->arena_bytes = off;
+  const size_t o_pstat = plan.o_pstat, o_po = plan.o_po, o_logits = plan.o_logits, o_mz = plan.o_mz,
+               o_scores = plan.o_scores, o_warm = plan.o_warm, o_tm = plan.o_tm, o_sel = plan.o_sel,
+               o_cnt = plan.o_cnt, o_status = plan.o_status, o_lens = plan.o_lens, o_hist0 = plan.o_hist0;
+  h->arena_bytes = plan.arena_bytes;
   hipError_t e = hipMalloc(&h->arena, h->arena_bytes);
   if (e != hipSuccess) {
     delete h;
@@ -802,7 +866,9 @@ int fastocr_get_layer_ratios(fastocr_handle* h, double* ratios_host) {
 int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int32_t count) {
   if (!h || !layers_host) return FASTOCR_ERR_INVALID_ARG;
   const int L = h->cfg.num_layers;
-  if (count < 1 || count > L) return FASTOCR_ERR_INVALID_ARG;
+  // exactly |C| layers: fastocr_get_focal_layers and fastocr_profile_warmup
+  // write num_focal entries
+  if (count != h->cfg.num_focal) return FASTOCR_ERR_INVALID_ARG;
   std::vector<char> seen(L, 0);
   for (int i = 0; i < count; ++i) {
     const int l = layers_host[i];
@@ -815,7 +881,19 @@ int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int3
   for (int l = 0; l < L; ++l)
     if (seen[l]) h->focal.push_back(l);
   h->is_focal = seen;
-  if (h->phase == PHASE_WARMUP_DONE) h->pruned_since = 0;
+  if (h->phase == PHASE_WARMUP_DONE) {
+    // ends the warm-up window as a profile does, with the given set: the
+    // first pruned step inherits top-k of the window's last-step scores at
+    // the deepest of these layers (Cross-Step Fixation Reuse /
+    // Implementation); the layer ratios are not computed
+    const int deepest = h->focal.back();
+    int rc = run_topk(h, h->warm_scores + (size_t)deepest * h->cfg.batch * h->n_stride, h->lens_shadow, nullptr);
+    if (rc) return rc;
+    const hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return fail_hip(h, e);
+    h->pruned_since = 0;
+    ++h->profiles;
+  }
   h->phase = PHASE_PRUNED;
   return FASTOCR_OK;
 }
@@ -835,6 +913,25 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->profiles = h->profiles;
   info->scratch_bytes = (int64_t)h->arena_bytes;
+  return FASTOCR_OK;
+}
+
+int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info* info) {
+  if (!cfg || !info) return FASTOCR_ERR_INVALID_ARG;
+  Plan p;
+  const int rc = make_plan(*cfg, num_cu, p);
+  if (rc != FASTOCR_OK) return rc;
+  *info = fastocr_info{};
+  info->phase = cfg->mode == FASTOCR_MODE_FULL ? PHASE_FULL : PHASE_WARMUP;
+  info->k_max = p.k_max;
+  info->full_rows_per_split = p.full_R;
+  info->full_max_splits = p.full_splits;
+  info->sparse_rows_per_split = p.sparse_R;
+  info->sparse_max_splits = p.sparse_splits;
+  info->sparse_direct = p.sparse_splits <= 1 ? 1 : 0;
+  info->sparse_wave_states = p.wave_states ? 1 : 0;
+  info->sparse_pipe = p.sparse_pipe ? 1 : 0;
+  info->scratch_bytes = (int64_t)p.arena_bytes;
   return FASTOCR_OK;
 }
 

@@ -259,8 +259,17 @@ int fastocr_get_scores(fastocr_handle* h, float* scores_dev);
  * (host double [L]). */
 int fastocr_get_layer_ratios(fastocr_handle* h, double* ratios_host);
 
-/* Replace the focal set C (host int32 [count], distinct, in [0, L)); switches
- * a handle whose warm-up is complete to pruned steps without profiling. */
+/* Replace the focal set C with count = num_focal distinct layers (host int32
+ * [count], in [0, L)), at a step boundary.  On a handle whose warm-up window
+ * is complete (the first one or a re-selection window) it ends the window
+ * the way fastocr_profile_warmup does, with this set instead of the profiled
+ * one: the kept set is initialised by top-k of the window's last-step
+ * scores at the deepest given layer, and the handle switches to pruned
+ * steps (the layer ratios are not computed).  During pruned steps it only
+ * replaces C; the kept set carried to the next step is unchanged.
+ * Synchronises the stream when it ends a window.  Errors: INVALID_ARG (null,
+ * count != num_focal, a layer repeated or out of range), STATE (not at a step
+ * boundary, warm-up window not complete, poisoned handle), HIP. */
 int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int32_t count);
 
 /* Enqueues device-to-device copies into the kept set (same layout as
@@ -269,6 +278,15 @@ int fastocr_set_focal_layers(fastocr_handle* h, const int32_t* layers_host, int3
 int fastocr_set_selection(fastocr_handle* h, const int32_t* idx_dev, const int32_t* cnt_dev);
 
 int fastocr_get_info(fastocr_handle* h, fastocr_info* info);
+
+/* fastocr_plan_launch: the launch geometry and scratch size fastocr_create
+ * would choose for cfg on a device with num_cu compute units (the FASTOCR_*
+ * environment overrides included), written to the plan fields of *info
+ * (k_max, rows per split and splits of the full and kept-token passes,
+ * sparse_direct / wave_states / pipe, scratch_bytes; the state fields are
+ * those of a new handle).  Host only: no device is used.  Errors:
+ * INVALID_ARG (null, a configuration fastocr_create rejects, num_cu < 1). */
+int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info* info);
 
 /* Kernel timing with HIP events on the handle's stream.  enable != 0 makes
  * every launch record an event when its kernel completes (bound to the
@@ -356,6 +374,17 @@ int32_t fastocr_image_first_map(const int32_t* spans, int32_t num_spans, int32_t
 int fastocr_pack_rows(const void* src, void* dst, const int32_t* row_map, const int32_t* rows,
                       int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t head_dim,
                       int32_t dtype, int32_t* status, void* hip_stream);
+
+/* ---- measurement --------------------------------------------------------- */
+
+/* fastocr_probe_read: stream `bytes` (a positive multiple of 16) of device
+ * memory at buf (16-byte aligned) through the vector memory path with
+ * `workgroups` workgroups of 256 threads, each thread folding what it reads
+ * into one word; sink: device uint32 [64], written only if a fold hits a
+ * sentinel value (not in practice).  Reads only; used to measure the HBM read
+ * rate and the per-launch cost of reads the size of a kept-token pass.
+ * hip_stream: hipStream_t.  Asynchronous.  Errors: INVALID_ARG, HIP. */
+int fastocr_probe_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* hip_stream);
 
 /* Host helpers (no device use). */
 /* k = clamp(ceil(tau*n - 1e-9), 1, n) for n > 0; 0 for n <= 0; negative

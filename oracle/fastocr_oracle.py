@@ -80,7 +80,12 @@ def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
     return h // (num_q_heads // num_kv_heads)
 
 
-def attention_probs(q: np.ndarray, K: np.ndarray, rows, scale: float) -> np.ndarray:
+# Every function computes in float64 unless a caller asks for another
+# working precision (``dtype``): the benchmark's CPU baseline also times a
+# float32 run of the same definitions; parity always uses float64.
+
+
+def attention_probs(q: np.ndarray, K: np.ndarray, rows, scale: float, dtype=np.float64) -> np.ndarray:
     """Softmax attention probabilities of one sequence over the given rows.
 
     q: [Hq, d]; K: [Hkv, S, d]; rows: a 1-D index array or a slice of cache
@@ -91,33 +96,33 @@ def attention_probs(q: np.ndarray, K: np.ndarray, rows, scale: float) -> np.ndar
     """
     Hq, Hkv = q.shape[0], K.shape[0]
     n_rows = len(range(K.shape[1])[rows]) if isinstance(rows, slice) else len(rows)
-    p = np.zeros((Hq, n_rows), dtype=np.float64)
+    p = np.zeros((Hq, n_rows), dtype=dtype)
     if n_rows == 0:
         return p
     for kvh in range(Hkv):
         heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == kvh]
-        keys = np.asarray(K[kvh][rows], dtype=np.float64)  # [n_rows, d]
-        x = scale * (np.asarray(q[heads], dtype=np.float64) @ keys.T)  # [g, n_rows]
+        keys = np.asarray(K[kvh][rows], dtype=dtype)  # [n_rows, d]
+        x = dtype(scale) * (np.asarray(q[heads], dtype=dtype) @ keys.T)  # [g, n_rows]
         e = np.exp(x - x.max(axis=1, keepdims=True))
         p[heads] = e / e.sum(axis=1, keepdims=True)
     return p
 
 
 def _weighted_values(p: np.ndarray, V: np.ndarray, rows) -> np.ndarray:
-    """out[h] = sum_i p[h, i] * V[kv(h), rows[i]]."""
+    """out[h] = sum_i p[h, i] * V[kv(h), rows[i]] (in p's precision)."""
     Hq = p.shape[0]
     Hkv, _, d = V.shape
-    out = np.zeros((Hq, d), dtype=np.float64)
+    out = np.zeros((Hq, d), dtype=p.dtype)
     if p.shape[1] == 0:
         return out
     for kvh in range(Hkv):
         heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == kvh]
-        out[heads] = p[heads] @ np.asarray(V[kvh][rows], dtype=np.float64)
+        out[heads] = p[heads] @ np.asarray(V[kvh][rows], dtype=p.dtype)
     return out
 
 
 def full_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int,
-                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: float, dtype=np.float64) -> Tuple[np.ndarray, np.ndarray]:
     """Full decode attention over cache rows [0, length) of one sequence.
 
     Used on every layer during the warm-up and on focal layers afterwards,
@@ -126,7 +131,7 @@ def full_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int,
     Returns (out [Hq, d], p [Hq, length]).
     """
     rows = slice(0, int(length))
-    p = attention_probs(q, K, rows, scale)
+    p = attention_probs(q, K, rows, scale, dtype)
     return _weighted_values(p, V, rows), p
 
 
@@ -145,7 +150,7 @@ def image_rows_of(spans: Sequence[Tuple[int, int]]) -> np.ndarray:
 
 def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
                      selected: Sequence[int], n_img: int, length: int,
-                     scale: float, image_rows: Optional[np.ndarray] = None) -> np.ndarray:
+                     scale: float, image_rows: Optional[np.ndarray] = None, dtype=np.float64) -> np.ndarray:
     """Non-focal decode attention: the selected image tokens plus all text rows.
 
     Non-focal layers attend only to the pruned token set (Method / 1.
@@ -161,7 +166,7 @@ def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
     else:
         text = np.setdiff1d(np.arange(length, dtype=np.int64), image_rows)
         rows = np.concatenate([np.asarray(image_rows, dtype=np.int64)[sel], text])
-    p = attention_probs(q, K, rows, scale)
+    p = attention_probs(q, K, rows, scale, dtype)
     return _weighted_values(p, V, rows)
 
 

@@ -263,3 +263,35 @@ class Checker:
             deepest = max(focal)
             np.testing.assert_array_equal(rec.sets[t + 1, 0], rec.sets[t, deepest + 1])
             np.testing.assert_array_equal(rec.cnts[t + 1, 0], rec.cnts[t, deepest + 1])
+
+
+def check_layer(up: Uploaded, t: int, l: int, out: np.ndarray, kind: str, tau: Optional[float] = None,
+                used=None, picked=None, what: str = "") -> float:
+    """One layer's output at step t against the oracle.
+
+    kind: "full" (warm-up, FULL mode, or a focal layer whose pick is unused:
+    full attention), "focal" (full attention; ``picked`` = (idx [B, k_max],
+    cnt [B]) is the kept set after the layer, checked by the band rule
+    against the oracle's scores) or "sparse" (attention over ``used`` =
+    (idx, cnt), the set the GPU attended with, plus every text row).
+    Returns the largest output error."""
+    wl = up.wl
+    tau = wl.tau if tau is None else tau
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    lens = up.st.lens(t)
+    K, V = up.kv64(l)
+    q = up.q[l][t].astype(np.float64)
+    worst = 0.0
+    for b in range(wl.batch):
+        n, length = int(lens[b, 0]), int(lens[b, 1])
+        if kind in ("full", "focal"):
+            want, p = full_attention(q[b], K[b], V[b], length, scale)
+            if kind == "focal":
+                idx, cnt = picked
+                check_set(idx[b, :int(cnt[b])], image_scores(p, n), kept_count(tau, n),
+                          f"{what} set t={t} l={l} b={b}")
+        else:
+            idx, cnt = used
+            want = sparse_attention(q[b], K[b], V[b], idx[b, :int(cnt[b])], n, length, scale)
+        worst = max(worst, check_out(out[b], want, wl.dtype, f"{what} out t={t} l={l} b={b}"))
+    return worst

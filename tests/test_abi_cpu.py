@@ -170,3 +170,92 @@ def test_pack_rows_rejects_bad_arguments():
     c = ctypes.c_void_p(0x200000)
     assert lib.fastocr_pack_rows(a, c, i32, i32, 1, 1, 8, 96, 1, None, None) == fo.ERR_INVALID_ARG
     assert lib.fastocr_pack_rows(a, c, i32, i32, 1, 1, 8, 64, 7, None, None) == fo.ERR_INVALID_ARG
+
+
+def _plan(num_cu=256, **kw):
+    base = dict(num_layers=4, num_q_heads=4, num_kv_heads=2, head_dim=64, batch=1, max_seq_len=304,
+                max_img_tokens=256, tau=0.1, num_focal=2, warmup_steps=4, dtype="f32")
+    base.update(kw)
+    return fo.fastocr_plan_launch(fo.Config(**base), num_cu)
+
+
+@pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
+def test_plan_rejects_what_create_rejects(bad):
+    with pytest.raises(fo.FastOCRError):
+        _plan(**bad)
+
+
+def test_plan_launch_null_and_cu_count():
+    lib = fo.lib()
+    c = _cfg()
+    info = fo._abi.Info()
+    assert lib.fastocr_plan_launch(None, 256, ctypes.byref(info)) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_plan_launch(ctypes.byref(c), 256, None) == fo.ERR_INVALID_ARG
+    assert lib.fastocr_plan_launch(ctypes.byref(c), 0, ctypes.byref(info)) == fo.ERR_INVALID_ARG
+
+
+MAX_MERGE_STATES = 1024  # merge states per head one merge workgroup holds in LDS
+MAX_PIPE_ROWS = 2048     # rows of one pipelined kept-token split (its row map lives in LDS)
+
+
+def _check_plan(info, S):
+    states = info["sparse_max_splits"] * (4 if info["sparse_wave_states"] else 1)
+    assert info["full_max_splits"] * info["full_rows_per_split"] >= S
+    assert info["full_max_splits"] <= MAX_MERGE_STATES
+    assert states <= MAX_MERGE_STATES
+    if info["sparse_pipe"]:
+        assert info["sparse_rows_per_split"] <= MAX_PIPE_ROWS
+        assert info["sparse_rows_per_split"] % 128 == 0
+    if info["sparse_wave_states"]:
+        assert states <= 64
+
+
+@pytest.mark.parametrize("pipe", ["", "1"])
+def test_plan_multi_million_rows_stays_within_merge_capacity(monkeypatch, pipe):
+    # a kept-token pass longer than 1024 pipelined splits of 2048 rows runs
+    # one-round splits instead, so the merge never sees more states than
+    # its LDS holds
+    monkeypatch.setenv("FASTOCR_SPARSE_PIPE", pipe)
+    for S in (2_200_000, 3_000_000, 8_000_000):
+        info = _plan(num_layers=2, num_q_heads=16, num_kv_heads=8, head_dim=128, batch=1, max_seq_len=S,
+                     max_img_tokens=S // 2, tau=0.05, num_focal=1, warmup_steps=1, dtype="bf16")
+        _check_plan(info, S)
+        if pipe and (info["k_max"] + S - S // 2 + MAX_PIPE_ROWS - 1) // MAX_PIPE_ROWS > MAX_MERGE_STATES:
+            assert info["sparse_pipe"] == 0
+
+
+def test_plan_random_configs_within_kernel_limits():
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        hkv = int(rng.integers(1, 9))
+        g = int(rng.integers(1, 17))
+        S = int(rng.integers(1, 3_000_000))
+        n = int(rng.integers(0, S + 1))
+        nmin = int(rng.integers(0, n + 1))
+        text = int(rng.integers(0, S + 1))
+        info = _plan(num_cu=int(rng.choice([80, 256, 304])), num_layers=2, num_q_heads=hkv * min(g, 128 // hkv),
+                     num_kv_heads=hkv, head_dim=int(rng.choice([64, 128])), batch=int(rng.integers(1, 65)),
+                     max_seq_len=S, max_img_tokens=n, min_img_tokens=nmin, max_text_tokens=text,
+                     tau=float(rng.uniform(0.01, 1.0)), num_focal=1, warmup_steps=1)
+        _check_plan(info, S)
+
+
+def test_plan_of_benchmark_workloads():
+    # 7B-like B=1: one-round kept-token splits with per-wave states;
+    # 72B-like B=8 at tau 0.2: pipelined kept-token splits
+    b1 = _plan(num_layers=28, num_q_heads=28, num_kv_heads=4, head_dim=128, batch=1, max_seq_len=7488,
+               max_img_tokens=6400, min_img_tokens=6400, max_text_tokens=64 + 1024, tau=0.05, num_focal=4,
+               warmup_steps=8, dtype="bf16")
+    assert b1["k_max"] == 320 and b1["sparse_wave_states"] == 1 and b1["sparse_pipe"] == 0
+    b8 = _plan(num_layers=80, num_q_heads=64, num_kv_heads=8, head_dim=128, batch=8, max_seq_len=14976,
+               max_img_tokens=12800, min_img_tokens=12800, max_text_tokens=128 + 2048, tau=0.2, num_focal=8,
+               warmup_steps=8, dtype="bf16")
+    assert b8["k_max"] == 2560 and b8["sparse_pipe"] == 1
+    for info in (b1, b8):
+        _check_plan(info, info["full_max_splits"] * info["full_rows_per_split"])
+
+
+def test_set_focal_layers_null_handle():
+    lib = fo.lib()
+    arr = (ctypes.c_int32 * 2)(1, 3)
+    assert lib.fastocr_set_focal_layers(None, arr, 2) == fo.ERR_INVALID_ARG

@@ -10,7 +10,8 @@ import dynamic_kv_cache_amd as fo
 from oracle import full_attention, kept_count, select_top, sparse_attention
 from workload import get_workload
 
-from gpu_harness import Checker, check_out, check_set, log, make_config, run, unused_picks, upload
+from gpu_harness import (Checker, check_layer, check_out, check_set, log, make_config, run, unused_picks,
+                         upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -372,7 +373,11 @@ APPEND_CASES = {
 def test_attend_append_equals_prewritten_row(monkeypatch, case):
     # the current token's K/V given to fastocr_attend_append (its cache row
     # holding NaN before the call) gives the outputs of fastocr_attend on a
-    # cache that already holds the row, bit for bit, and writes the row
+    # cache that already holds the row, bit for bit, and writes the row; the
+    # appending handle's outputs, focal set and kept sets also match the
+    # oracle (non-focal layers conditioned on the set the handle attended
+    # with)
+    from oracle import DecodeOracle
     name, over, mode, steps, env = APPEND_CASES[case]
     for k, v in env.items():
         monkeypatch.setenv(k, v)
@@ -385,9 +390,21 @@ def test_attend_append_equals_prewritten_row(monkeypatch, case):
     vb = [v.clone() for v in up.Vd]
     out_a = torch.empty((B, Hq, d), dtype=up.io_dtype, device=DEV)
     out_b = torch.empty_like(out_a)
+    k_max = fo.fastocr_get_info(hb)["k_max"]
+    sel = torch.zeros((B, k_max), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    orc = DecodeOracle(num_layers=L, num_q_heads=Hq, num_kv_heads=wl.num_kv_heads, head_dim=d, tau=wl.tau,
+                       num_focal=wl.num_focal, warmup_steps=wl.warmup_steps)
+    focal, worst = [], 0.0
     for t in range(steps):
+        pruned = mode == "pruned" and t >= wl.warmup_steps
+        if mode == "pruned" and t < wl.warmup_steps:
+            orc.step(t, lambda l: up.q[l][t].astype(np.float64), up.kv64, up.st.lens(t))
         if mode == "pruned" and t == wl.warmup_steps:
-            assert fo.fastocr_profile_warmup(ha) == fo.fastocr_profile_warmup(hb)
+            focal = fo.fastocr_profile_warmup(hb)
+            assert fo.fastocr_profile_warmup(ha) == focal
+            assert focal == [int(x) for x in orc.focal], (focal, list(orc.focal))
+        unused = unused_picks(focal, L) if pruned else set()
         cur = up.st.lens(t)[:, 1] - 1
         for l in range(L):
             bi = torch.arange(B, device=DEV)
@@ -396,15 +413,22 @@ def test_attend_append_equals_prewritten_row(monkeypatch, case):
             v_new = up.Vd[l][bi, :, ci].contiguous()
             kb[l][bi, :, ci] = float("nan")
             vb[l][bi, :, ci] = float("nan")
+            kind = "sparse" if pruned and l not in focal else ("focal" if pruned and l not in unused else "full")
+            if kind == "sparse":
+                fo.fastocr_get_selection(hb, sel, cnt)  # the set this layer attends with
             fo.fastocr_attend(ha, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out_a)
             fo.fastocr_attend_append(hb, l, up.Qd[l][t], k_new, v_new, kb[l], vb[l], up.lens[t], out_b)
+            if kind == "focal":
+                fo.fastocr_get_selection(hb, sel, cnt)  # the set this layer picked
             torch.cuda.synchronize()
             assert torch.equal(out_a, out_b), f"step {t} layer {l}"
+            s_np = (sel.cpu().numpy(), cnt.cpu().numpy())
+            worst = max(worst, check_layer(up, t, l, out_b.float().cpu().numpy().astype(np.float64), kind,
+                                           used=s_np, picked=s_np, what=f"append {case}"))
     for l in range(L):
         assert torch.equal(kb[l], up.Kd[l]) and torch.equal(vb[l], up.Vd[l]), f"layer {l} cache"
     assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
-    fo.fastocr_destroy(ha)
-    fo.fastocr_destroy(hb)
+    log(f"[append] {case}: focal {focal}, worst out vs oracle {worst:.2e}")
 
 
 # ---------------------------------------------------------------------------
@@ -481,6 +505,79 @@ def test_reprofile_follows_drift(name, over, R):
     assert fo.fastocr_get_status(h) == 0
     fo.fastocr_destroy(h)
     log(f"[reprofile] {name}: picks {picks}, worst out {worst:.2e}, mean Jaccard {np.mean(jac):.3f}")
+
+
+def test_set_focal_layers_ends_window_then_reprofiles():
+    # tiny fp32 page with re-selection after every R = 3 pruned steps.  The
+    # first window is ended by fastocr_set_focal_layers with a set of our
+    # choosing instead of the profiled one: the warm start is top-k of the
+    # window's last-step scores at the deepest given layer, the pruned steps
+    # run with that set, and the next window profiles itself at its end
+    # (the oracle is conditioned the same way: its focal set and warm start
+    # are replaced after its first window)
+    from oracle import DecodeOracle
+    R = 3
+    wl = get_workload("tiny-fp32").with_overrides(steps=4 + R + 4 + 2)
+    up = upload(wl)
+    L, B, Hq, d, w = wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim, wl.warmup_steps
+    h = fo.fastocr_create(make_config(up, reprofile_every=R))
+    orc = DecodeOracle(num_layers=L, num_q_heads=Hq, num_kv_heads=wl.num_kv_heads, head_dim=d, tau=wl.tau,
+                       num_focal=wl.num_focal, warmup_steps=w, reprofile_every=R)
+    k_max = fo.fastocr_get_info(h)["k_max"]
+    sel = torch.zeros((B, k_max), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=up.io_dtype, device=DEV)
+    chosen = [0, 2]  # the planted strong layers are {1, 3}
+    with pytest.raises(fo.FastOCRError) as err:
+        fo.fastocr_set_focal_layers(h, chosen)  # the window is not complete
+    assert err.value.code == fo.ERR_STATE
+    worst, focal = 0.0, None
+    for t in range(wl.steps):
+        lens = up.st.lens(t)
+        rec = orc.step(t, lambda l: up.q[l][t].astype(np.float64), up.kv64, lens)
+        if t == w - 1:
+            # condition the oracle: C and the warm start come from `chosen`
+            orc.focal = np.array(chosen)
+            orc.f_last = [select_top(orc.warm_scores[max(chosen)][b], kept_count(wl.tau, int(lens[b, 0])))
+                          for b in range(B)]
+        if t == w:
+            for bad in ([0, 1, 2], [1], [2, 2]):
+                with pytest.raises(fo.FastOCRError) as err:
+                    fo.fastocr_set_focal_layers(h, bad)
+                assert err.value.code == fo.ERR_INVALID_ARG, bad
+            fo.fastocr_set_focal_layers(h, chosen)
+            info = fo.fastocr_get_info(h)
+            assert info["profiles"] == 1 and info["phase"] == 2
+            assert fo.fastocr_get_focal_layers(h) == chosen
+            fo.fastocr_get_selection(h, sel, cnt)
+            s_np, c_np = sel.cpu().numpy(), cnt.cpu().numpy()
+            for b in range(B):
+                n = int(lens[b, 0])
+                check_set(s_np[b, :c_np[b]], orc.warm_scores[max(chosen)][b], kept_count(wl.tau, n),
+                          f"warm start b={b}")
+        for l in range(L):
+            pruned = rec.phase == "pruned"
+            focal_now = [int(x) for x in orc.focal] if orc.focal is not None else []
+            kind = "sparse" if pruned and l not in focal_now else (
+                "focal" if pruned and l not in unused_picks(focal_now, L) else "full")
+            if kind == "sparse":
+                fo.fastocr_get_selection(h, sel, cnt)
+            fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out)
+            if l == 0 and pruned:
+                focal = fo.fastocr_get_focal_layers(h)
+                assert focal == focal_now, (t, focal, focal_now)
+            if kind == "focal":
+                fo.fastocr_get_selection(h, sel, cnt)
+            torch.cuda.synchronize()
+            s_np = (sel.cpu().numpy(), cnt.cpu().numpy())
+            worst = max(worst, check_layer(up, t, l, out.float().cpu().numpy().astype(np.float64), kind,
+                                           used=s_np, picked=s_np, what="set-then-reprofile"))
+    # the second window (steps w+R .. w+R+w-1) was profiled by the GPU itself
+    assert fo.fastocr_get_info(h)["profiles"] == 2
+    assert focal == [int(x) for x in orc.profiles[-1][1]] != chosen, (focal, orc.profiles)
+    assert fo.fastocr_get_status(h) == 0
+    fo.fastocr_destroy(h)
+    log(f"[set-focal] chosen {chosen} then re-picked {focal}; worst out {worst:.2e}")
 
 
 # ---------------------------------------------------------------------------
@@ -693,7 +790,10 @@ def test_graph_replayed_steps_match_eager():
     # one pruned step captured as a graph (q and lens staged by copies, as
     # the benchmark does) and replayed step after step, with another
     # handle's eager steps and synchronisations in between: every replay's
-    # outputs and kept set equal the eager step's bit for bit
+    # outputs and kept set equal the eager step's bit for bit, and every
+    # replayed output matches the oracle (focal layers: full attention, their
+    # kept sets by the band rule; non-focal layers: attention over the set
+    # they used, recorded by the eager handle)
     wl = get_workload("7b-b1").with_overrides(num_layers=6, focal_band=(2, 3), num_focal=2, warmup_steps=2)
     T = 10
     up = upload(wl, steps=T)
@@ -702,21 +802,31 @@ def test_graph_replayed_steps_match_eager():
     ha = fo.fastocr_create(make_config(up), stream)
     hb = fo.fastocr_create(make_config(up), stream)
     io = up.io_dtype
+    k_max = fo.fastocr_get_info(ha)["k_max"]
+    rec_sel = torch.zeros((L, B, k_max), dtype=torch.int32, device=DEV)
+    rec_cnt = torch.zeros((L, B), dtype=torch.int32, device=DEV)
 
-    def eager(h, t, outs):
+    def eager(h, t, outs, focal=None):
+        # with `focal`: record the set each non-focal layer attends with and
+        # the set each focal layer picks
         for l in range(L):
+            if focal is not None and l not in focal:
+                fo.fastocr_get_selection(h, rec_sel[l], rec_cnt[l])
             fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], outs[l])
+            if focal is not None and l in focal:
+                fo.fastocr_get_selection(h, rec_sel[l], rec_cnt[l])
 
     scratch = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
     with torch.cuda.stream(stream):
         for t in range(wl.warmup_steps):
             eager(ha, t, scratch)
             eager(hb, t, scratch)
-    assert fo.fastocr_profile_warmup(ha) == fo.fastocr_profile_warmup(hb)
+    focal = fo.fastocr_profile_warmup(ha)
+    assert fo.fastocr_profile_warmup(hb) == focal
+    unused = unused_picks(focal, L)
     q_stage = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
     lens_stage = torch.empty((B, 2), dtype=torch.int32, device=DEV)
     out_stage = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
-    k_max = fo.fastocr_get_info(ha)["k_max"]
     sa, sb = (torch.zeros((B, k_max), dtype=torch.int32, device=DEV) for _ in range(2))
     ca, cb = (torch.zeros((B,), dtype=torch.int32, device=DEV) for _ in range(2))
     with torch.cuda.stream(stream):
@@ -729,6 +839,7 @@ def test_graph_replayed_steps_match_eager():
             fo.fastocr_attend(ha, l, q_stage[l], up.Kd[l], up.Vd[l], lens_stage, out_stage[l])
     torch.cuda.synchronize()
     out_b = torch.empty((L, B, Hq, d), dtype=io, device=DEV)
+    worst = 0.0
     for t in range(wl.warmup_steps, T):
         with torch.cuda.stream(stream):
             q_stage.copy_(torch.stack([up.Qd[l][t] for l in range(L)]))
@@ -736,14 +847,21 @@ def test_graph_replayed_steps_match_eager():
             g.replay()
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            eager(hb, t, out_b)
+            eager(hb, t, out_b, focal)
         torch.cuda.synchronize()
         assert torch.equal(out_stage, out_b), f"step {t}"
         fo.fastocr_get_selection(ha, sa, ca)
         fo.fastocr_get_selection(hb, sb, cb)
         torch.cuda.synchronize()
         assert torch.equal(ca, cb) and torch.equal(sa, sb), f"kept set after step {t}"
+        replayed = out_stage.float().cpu().numpy().astype(np.float64)
+        rs, rc = rec_sel.cpu().numpy(), rec_cnt.cpu().numpy()
+        for l in range(L):
+            kind = "full" if l in unused else ("focal" if l in focal else "sparse")
+            worst = max(worst, check_layer(up, t, l, replayed[l], kind, used=(rs[l], rc[l]),
+                                           picked=(rs[l], rc[l]), what="replay"))
     assert fo.fastocr_get_status(ha) == 0 and fo.fastocr_get_status(hb) == 0
+    log(f"[graph] focal {focal}, worst replayed out vs oracle {worst:.2e}")
     del g
 
 
