@@ -537,10 +537,10 @@ def main():
 
     def record_step(h, t, focal):
         k_max = fo.fastocr_get_info(h)["k_max"]
-        rec = {"t": t, "outs": torch.empty((L, B, Hq, d), dtype=io, device=dev),
-               "sel": torch.zeros((L, B, k_max), dtype=torch.int32, device=dev),
-               "cnt": torch.zeros((L, B), dtype=torch.int32, device=dev)}
         with torch.cuda.stream(stream):
+            rec = {"t": t, "outs": torch.empty((L, B, Hq, d), dtype=io, device=dev),
+                   "sel": torch.zeros((L, B, k_max), dtype=torch.int32, device=dev),
+                   "cnt": torch.zeros((L, B), dtype=torch.int32, device=dev)}
             for l in range(L):
                 if l not in focal:
                     fo.fastocr_get_selection(h, rec["sel"][l], rec["cnt"][l])
@@ -991,7 +991,7 @@ def cpu_baseline(wl, st, Kd, Vd, Qall, slot, focal_gpu, budget_s, recorded):
         return np.stack(outs), sets
 
     times = {np.float64: {"focal": [], "sparse": []}, np.float32: {"focal": [], "sparse": []}}
-    worst_abs, worst_rel, jac, checked = 0.0, 0.0, [], []
+    worst_abs, worst_rel, jac, checked, per_layer = 0.0, 0.0, [], [], []
     spent = 0.0
     for kind, l in order:
         if spent > budget_s and times[np.float64]["focal"] and times[np.float64]["sparse"]:
@@ -1008,8 +1008,10 @@ def cpu_baseline(wl, st, Kd, Vd, Qall, slot, focal_gpu, budget_s, recorded):
             if dtype is np.float64:
                 spent += dt
                 got = recorded["outs"][l]
-                worst_abs = max(worst_abs, float(np.abs(got - out).max()))
-                worst_rel = max(worst_rel, float(np.linalg.norm(got - out) / max(np.linalg.norm(out), 1e-30)))
+                err_abs = float(np.abs(got - out).max())
+                err_rel = float(np.linalg.norm(got - out) / max(np.linalg.norm(out), 1e-30))
+                worst_abs, worst_rel = max(worst_abs, err_abs), max(worst_rel, err_rel)
+                per_layer.append((err_rel, err_abs, l, kind))
                 checked.append(l)
                 for b, want in enumerate(sets):
                     gpu = set(int(j) for j in recorded["sel"][l, b, :int(recorded["cnt"][l, b])])
@@ -1039,7 +1041,9 @@ def cpu_baseline(wl, st, Kd, Vd, Qall, slot, focal_gpu, budget_s, recorded):
              "max_rel_l2": float(f"{worst_rel:.3e}"), "tolerance_abs": tol_abs, "tolerance_rel_l2": tol_rel,
              "within_tolerance": bool(worst_abs <= tol_abs and (tol_rel is None or worst_rel <= tol_rel)),
              "jaccard_vs_oracle_sets": round(float(np.mean(jac)), 4) if jac else None,
-             "focal_sets_compared": len(jac)}
+             "focal_sets_compared": len(jac),
+             "worst_layers": [{"layer": l, "kind": k, "max_abs": float(f"{a:.3e}"), "rel_l2": float(f"{r:.3e}")}
+                              for r, a, l, k in sorted(per_layer, reverse=True)[:6]]}
     return cpu, check
 
 

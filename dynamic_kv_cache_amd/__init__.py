@@ -20,7 +20,7 @@ from typing import Dict, List, Optional, Sequence
 
 from . import _abi
 from ._abi import (DTYPE_BF16, DTYPE_F32, ERR_HIP, ERR_INVALID_ARG, ERR_OOM, ERR_STATE,  # noqa: F401
-                   FLAG_INDEX_CLAMPED, FLAG_LENS_CLAMPED, FLAG_ROWS_TRUNCATED, KC_NAMES, MODE_FULL, MODE_PRUNED,
+                   FLAG_INDEX_CLAMPED, FLAG_LENS_CLAMPED, KC_NAMES, MODE_FULL, MODE_PRUNED,
                    OK)
 
 
@@ -122,12 +122,12 @@ class Handle:
         self.io_dtype = t.bfloat16 if cfg.dtype == "bf16" else t.float32
 
     def __del__(self):
-        if getattr(self, "ptr", None) is not None and self.ptr.value:
-            try:
+        try:
+            if getattr(self, "ptr", None) is not None and self.ptr.value:
                 _abi.load().fastocr_destroy(self.ptr)
-            except Exception:
-                pass
-            self.ptr = ctypes.c_void_p(0)
+                self.ptr = ctypes.c_void_p(0)
+        except Exception:  # interpreter shutdown: ctypes may already be gone
+            pass
 
 
 def fastocr_create(cfg: Config, stream=None) -> Handle:

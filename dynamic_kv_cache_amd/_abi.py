@@ -21,7 +21,6 @@ MODE_FULL = 1
 
 FLAG_LENS_CLAMPED = 1
 FLAG_INDEX_CLAMPED = 2
-FLAG_ROWS_TRUNCATED = 4
 
 KC_FULL_SPLIT = 0
 KC_FOCAL_SPLIT = 1
@@ -64,8 +63,6 @@ class Info(ctypes.Structure):
         ("sparse_rows_per_split", c_int32),
         ("sparse_max_splits", c_int32),
         ("sparse_direct", c_int32),
-        ("sparse_wave_states", c_int32),
-        ("sparse_pipe", c_int32),
         ("profiles", c_int32),
         ("scratch_bytes", c_int64),
     ]

@@ -95,13 +95,11 @@ int plan_rows_per_split(int64_t pairs, int rows, int target, int max_splits, con
 struct Plan {
   int n_cap = 0, n_stride = 0, k_max = 0;
   int full_R = 0, full_splits = 0, full_sure = 0;  // sure: splits that hold rows for any accepted sequence
-  int sparse_R = 0, sparse_splits = 0, sparse_sure = 0;
-  bool wave_states = false;      // kept-token splits write one state per wave
-  bool sparse_pipe = false;      // kept-token passes run pipelined multi-round splits
+  int sparse_R = 0, sparse_splits = 0;  // kept-token pass: rows per workgroup at the longest
+                                        // text the handle accepts, workgroups per pair
   bool keeps_all = false;        // tau = 1: non-focal layers run the full pass
   bool valu_full = false;        // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;   // a focal layer followed by a focal layer picks nothing
-  int states_per_sparse_split = 1;
   int max_splits = 0;            // merge states per head the scratch holds
   // scratch arena: byte offsets of each array, and the total
   size_t o_pstat = 0, o_po = 0, o_logits = 0, o_mz = 0, o_scores = 0, o_warm = 0, o_tm = 0, o_sel = 0,
@@ -131,7 +129,7 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
   // tokens, full step: 768-row splits (440 workgroups with rows) 1067 us,
   // 640 (516) 1247, 1024 (336) 1178, 1152 (304) 1224.
   int full_rows_est = c.max_seq_len;
-  int full_target = split_blocks_per_cu(KIND_FULL) * num_cu;
+  int full_target = kFullBlocksPerCU * num_cu;
   if (c.min_img_tokens > 0 && c.min_img_tokens < c.max_img_tokens) {
     full_rows_est = (c.min_img_tokens + c.max_img_tokens) / 2 + (c.max_seq_len - c.max_img_tokens);
     full_target = (int)std::max<int64_t>(full_target - pairs / 2, full_target / 2);
@@ -139,46 +137,30 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
   p.full_R = plan_rows_per_split(pairs, full_rows_est, full_target, kMaxMergeSplits, "FASTOCR_FULL_ROWS");
   while ((c.max_seq_len + p.full_R - 1) / p.full_R > kMaxMergeSplits) p.full_R += kRowsPerRound;
   p.full_splits = (c.max_seq_len + p.full_R - 1) / p.full_R;
-  // rows of a kept-token pass: kept image rows + text rows
+  // rows of a kept-token pass at the longest text the handle accepts: kept
+  // image rows + text rows
   int sparse_rows = c.max_seq_len;
   if (c.min_img_tokens > 0)
     sparse_rows = std::min(sparse_rows, p.k_max + c.max_seq_len - c.min_img_tokens);
   if (c.max_text_tokens > 0) sparse_rows = std::min(sparse_rows, p.k_max + c.max_text_tokens);
-  // Kept-token passes: one round per split, the most workgroups, dispatched
-  // split-major (measured faster than fewer, longer splits at every batch),
-  // or, pipelined, splits sized like a full pass's (whole rounds, about one
-  // wave of resident workgroups, at most kMaxPipeRows rows).
-  // Pipelined when the kept rows of all (sequence, KV head) pairs reach
-  // 64 x 2048: measured 2837 against 3104 us per step at 72B-like B=8,
-  // tau = 0.2 (2560 kept rows), but slower at tau <= 0.1 and at every
-  // smaller configuration.
   const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
-  const bool pipe_default = pairs * (int64_t)p.k_max >= 64 * 2048;
-  p.sparse_pipe = pruned && env_int("FASTOCR_SPARSE_PIPE", pipe_default ? 1 : 0) != 0;
-  if (p.sparse_pipe) {
-    int R = plan_rows_per_split(pairs, sparse_rows, split_blocks_per_cu(KIND_SPARSE, true) * num_cu,
-                                kMaxMergeSplits, "FASTOCR_SPARSE_ROWS");
-    R = std::min((int)align_up((size_t)R, kRowsPerRound), kMaxPipeRows);
-    // a pipelined split holds at most kMaxPipeRows rows (its row map lives
-    // in LDS); a pass that would need more than kMaxMergeSplits of them runs
-    // one-round splits instead
-    if ((sparse_rows + R - 1) / R > kMaxMergeSplits) p.sparse_pipe = false;
-    else p.sparse_R = R;
+  // Kept-token passes deal each pair's 16-row tiles round-robin to P
+  // workgroups, as many as fill one wave of resident workgroups over all
+  // pairs (a launch past one wave runs a second, mostly idle one: 72B-like
+  // B=8, P = 12 (768 workgroups) 16.9 us against P = 16 19.6 us; 32B-like
+  // B=4, P = 24 14.1 us against P = 25 16.4 us), but no more than the
+  // pair's tiles at the longest text and at most kMaxKeptSplits (7B-like
+  // B=1: P = 22-44 5.4 us, 64 5.5 us, 11 5.9 us).  FASTOCR_SPARSE_ROWS=R sets
+  // P for R rows per workgroup at that length instead.
+  if (pruned) {
+    const int64_t slots = (int64_t)kKeptBlocksPerCU * num_cu;
+    int P = (int)std::min<int64_t>(std::max<int64_t>(slots / pairs, 1), (sparse_rows + kTileRows - 1) / kTileRows);
+    const int R_env = env_int("FASTOCR_SPARSE_ROWS", 0);
+    if (R_env > 0) P = (sparse_rows + R_env - 1) / R_env;
+    P = std::min(std::max(P, 1), kMaxKeptSplits);
+    p.sparse_splits = P;
+    p.sparse_R = (int)align_up((size_t)((sparse_rows + P - 1) / P), kTileRows);
   }
-  if (!p.sparse_pipe)
-    p.sparse_R = plan_rows_per_split(pairs, sparse_rows, 1 << 30, kMaxMergeSplits / kSplitWaves,
-                                     "FASTOCR_SPARSE_ROWS");
-  p.sparse_splits = pruned ? (sparse_rows + p.sparse_R - 1) / p.sparse_R : 0;
-  // A kept-token pass of at most one workgroup per CU is latency-bound: its
-  // waves then write their states themselves (no cross-wave combine and
-  // barrier; measured 5.75 against 6.4 us per launch at 7B-like B=1), as
-  // long as the merge keeps one state per lane.  A larger pass streams, and
-  // there the 4x partial-output traffic costs more than the combine.
-  const bool ws_default = p.sparse_splits > 1 && pairs * p.sparse_splits <= num_cu &&
-                          p.sparse_splits * kSplitWaves <= 64;
-  p.wave_states = env_int("FASTOCR_WAVE_STATES", ws_default ? 1 : 0) != 0 && p.sparse_splits > 1 &&
-                  !p.sparse_pipe;
-  p.states_per_sparse_split = p.wave_states ? kSplitWaves : 1;
   p.skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
   // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
   // of at most kValuMaxGroup heads), to measure what the matrix cores buy
@@ -186,18 +168,15 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
                 G <= kValuMaxGroup;
   // k_b = n_b for every n_b exactly when tau = 1
   p.keeps_all = c.tau >= 1.0 && env_int("FASTOCR_KEPT_ALL_AS_FULL", 1) != 0;
-  // state slots per head (a direct kept-token pass writes none); the merge
-  // keeps one weight per state in LDS
-  p.max_splits = std::max(p.full_splits, p.sparse_splits * p.states_per_sparse_split);
+  // state slots per head; the merge keeps one weight per state in LDS
+  p.max_splits = std::max(p.full_splits, p.sparse_splits);
   if (p.max_splits > kMaxMergeSplits) return FASTOCR_ERR_INVALID_ARG;
   // Full passes: every sequence has at least min_img_tokens image rows and
   // the current token, so splits below that hold rows and load their K/V
   // ahead; the others (possibly empty for a short sequence of a ragged
-  // batch) wait for the extent.  Kept-token splits only load indices ahead,
-  // which costs an empty split nothing worth saving.
+  // batch) wait for the extent.
   const int min_full_rows = c.min_img_tokens + 1;
   p.full_sure = std::min((min_full_rows + p.full_R - 1) / p.full_R, p.full_splits);
-  p.sparse_sure = p.sparse_splits;
 
   // scratch arena
   const size_t B = c.batch, Hq = c.num_q_heads, L = c.num_layers, D = c.head_dim;
@@ -231,16 +210,13 @@ struct fastocr_handle {
   int device = 0;
   int G = 0, D = 0, n_cap = 0, n_stride = 0, k_max = 0;
   int full_R = 0, full_splits = 0, sparse_R = 0, sparse_splits = 0, max_splits = 0;
-  int full_sure = 0, sparse_sure = 0;  // splits that hold rows for any accepted sequence
-  bool wave_states = false;            // kept-token splits write one state per wave
+  int full_sure = 0;                   // full-pass splits that hold rows for any accepted sequence
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
-  bool sparse_pipe = false;            // kept-token passes run pipelined multi-round splits
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;         // a focal layer followed by a focal layer picks nothing
   Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
-  int states_per_sparse_split = 1;
 
   float scale_log2 = 0.f;
 
@@ -332,7 +308,7 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   p.max_splits = h->max_splits;
   p.rows_per_split = sparse ? h->sparse_R : h->full_R;
   p.grid_splits = sparse ? h->sparse_splits : h->full_splits;
-  p.sure_splits = sparse ? h->sparse_sure : h->full_sure;
+  p.sure_splits = sparse ? 0 : h->full_sure;
   p.scale_log2 = h->scale_log2;
   return p;
 }
@@ -359,17 +335,12 @@ MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool
   m.pstat = h->pstat;
   m.po = h->po;
   m.lens = lens;
-  m.sel_cnt = sparse ? h->sel_cnt : nullptr;
   m.out = out;
-  m.status = h->status;
   m.B = c.batch;
   m.Hq = c.num_q_heads;
-  m.S = c.max_seq_len;
   m.n_cap = h->n_cap;
-  m.k_stride = h->k_max;
   m.max_splits = h->max_splits;
-  m.rows_per_split = sparse ? h->sparse_R : h->full_R;
-  m.grid_splits = sparse ? h->sparse_splits * h->states_per_sparse_split : h->full_splits;  // states per head
+  m.grid_splits = sparse ? h->sparse_splits : h->full_splits;  // states per head
   m.n_stride = h->n_stride;
   return m;
 }
@@ -382,7 +353,6 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
   const fastocr_config& c = h->cfg;
   const bool focal = scores_dst != nullptr;
   SplitParams sp = split_params(h, q, k, v, lens, out, false);
-  sp.direct = 0;
   sp.valu = (h->valu_full && !focal && !h->app_k) ? 1 : 0;
   int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream, lt);
@@ -409,11 +379,8 @@ int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, c
                void* out) {
   const fastocr_config& c = h->cfg;
   SplitParams sp = split_params(h, q, k, v, lens, out, true);
-  sp.direct = h->sparse_splits <= 1 ? 1 : 0;
-  sp.wave_states = h->wave_states ? 1 : 0;
-  sp.pipe = h->sparse_pipe ? 1 : 0;
   int rc = timed(h, FASTOCR_KC_SPARSE_SPLIT, [&](const LaunchTiming& lt) {
-    return launch_split(c.dtype, c.head_dim, KIND_SPARSE, sp, h->stream, lt);
+    return launch_kept(c.dtype, c.head_dim, sp, h->stream, lt);
   });
   if (rc || h->sparse_splits <= 1) return rc;
   MergeParams mp = merge_params(h, lens, out, true);
@@ -607,13 +574,9 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   h->full_sure = plan.full_sure;
   h->sparse_R = plan.sparse_R;
   h->sparse_splits = plan.sparse_splits;
-  h->sparse_sure = plan.sparse_sure;
-  h->wave_states = plan.wave_states;
-  h->sparse_pipe = plan.sparse_pipe;
   h->keeps_all = plan.keeps_all;
   h->valu_full = plan.valu_full;
   h->skip_dead_picks = plan.skip_dead_picks;
-  h->states_per_sparse_split = plan.states_per_sparse_split;
   h->max_splits = plan.max_splits;
   if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
   const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
@@ -908,8 +871,6 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->full_max_splits = h->full_splits;
   info->sparse_rows_per_split = h->sparse_R;
   info->sparse_max_splits = h->sparse_splits;
-  info->sparse_wave_states = h->wave_states ? 1 : 0;
-  info->sparse_pipe = h->sparse_pipe ? 1 : 0;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->profiles = h->profiles;
   info->scratch_bytes = (int64_t)h->arena_bytes;
@@ -929,8 +890,6 @@ int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info*
   info->sparse_rows_per_split = p.sparse_R;
   info->sparse_max_splits = p.sparse_splits;
   info->sparse_direct = p.sparse_splits <= 1 ? 1 : 0;
-  info->sparse_wave_states = p.wave_states ? 1 : 0;
-  info->sparse_pipe = p.sparse_pipe ? 1 : 0;
   info->scratch_bytes = (int64_t)p.arena_bytes;
   return FASTOCR_OK;
 }

@@ -22,13 +22,14 @@ constexpr int kSplitWaves = 4;
 constexpr int kTilesPerWave = 2;
 constexpr int kRowsPerRound = kTileRows * kSplitWaves * kTilesPerWave;
 constexpr int kSplitThreads = kSplitWaves * 64;
-// Resident split workgroups per CU the registers allow: full passes keep two
-// rounds of K/V in registers, kept-token passes one.
-// Resident workgroups per CU a split kernel is compiled for: one register
-// buffer (single-round kept-token splits) or two (pipelined passes).
-constexpr int split_blocks_per_cu(int kind, bool pipe = false) { return kind == KIND_SPARSE && !pipe ? 3 : 2; }
-// Longest split of a pipelined kept-token pass (its row map lives in LDS).
-constexpr int kMaxPipeRows = 2048;
+// Resident workgroups per CU the kernels are compiled for: full passes keep
+// two rounds of K/V in registers, kept-token passes one.
+constexpr int kFullBlocksPerCU = 2;
+constexpr int kKeptBlocksPerCU = 3;
+// Kept-token passes (non-focal layers) run kept_attn_kernel: each (sequence,
+// KV head) pair's 16-row tiles are dealt round-robin to P workgroups
+// (P <= kMaxKeptSplits), whose states the merge kernel combines.
+constexpr int kMaxKeptSplits = 32;
 constexpr int kMergeThreads = 256;
 constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
 constexpr int kMaxHeads = 128;
@@ -41,27 +42,21 @@ struct SplitParams {
   const void* k;          // [B, Hkv, S, D]
   const void* v;          // [B, Hkv, S, D]
   const int32_t* lens;    // [B, 2]
-  const int32_t* sel;     // [B, k_stride]   (sparse)
-  const int32_t* sel_cnt; // [B]             (sparse)
+  const int32_t* sel;     // [B, k_stride]   kept set (kept-token pass)
+  const int32_t* sel_cnt; // [B]
   float* logits;          // [B, Hq, n_stride] log2-domain scaled logits (focal)
-  float4* pstat;          // [B, Hq, max_splits] (max, sum p, sum rounded p, text sum p): state
-                          // `split`, or split * kSplitWaves + wave with wave_states
+  float4* pstat;          // [B, Hq, max_splits] (max, sum p, sum rounded p, text sum p) of
+                          // each split
   float* po;              // [B, Hq, max_splits, D] unnormalised partial outputs
-  void* out;              // [B, Hq, D] in the io dtype (direct outputs)
+  void* out;              // [B, Hq, D] in the io dtype (a kept-token pass of one split per pair)
   int32_t* status;
   int32_t B, Hq, Hkv, S, n_cap, n_stride, k_stride, max_splits, rows_per_split;
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
-  int32_t sure_splits;    // splits that hold rows for every accepted sequence
-  int32_t direct;         // one split per sequence (grid_splits == 1): write outputs here;
-                          // otherwise every launched split writes its states (empty: max -inf)
-  int32_t wave_states;    // kept-token pass, not direct: one state per wave instead of a
-                          // cross-wave combine per workgroup
+  int32_t sure_splits;    // full pass: splits that hold rows for every accepted sequence
   const void* k_new;      // [B, Hkv, D] the current token's key and value, or null: when
   const void* v_new;      // set, cache row len-1 is read from here and written into the
   void* k_w;              // caches (k_w, v_w: the same buffers as k, v) by each pair's
   void* v_w;              // split 0
-  int32_t pipe;           // kept-token pass of multi-round splits (rows_per_split <=
-                          // kMaxPipeRows): row map in LDS, rounds double-buffered
   float scale_log2;       // logit scale * log2(e)
   int32_t valu;           // full kind, bf16, D = 128, Hq/Hkv <= kValuMaxGroup: the VALU
                           // variant (fp32 FMAs and 16-lane shuffle reductions instead of
@@ -75,11 +70,9 @@ struct MergeParams {
   const float4* pstat;
   const float* po;
   const int32_t* lens;
-  const int32_t* sel_cnt; // non-null: the split pass was sparse
   void* out;              // [B, Hq, D] in the io dtype
   float* text_mass;       // [B, Hq] or null
-  int32_t* status;
-  int32_t B, Hq, S, n_cap, k_stride, max_splits, rows_per_split;
+  int32_t B, Hq, n_cap, max_splits;
   int32_t grid_splits;    // states per head written by the split pass
   const float* logits;    // [B, Hq, n_stride]
   float* scores;          // [B, n_stride]
@@ -125,6 +118,8 @@ struct LaunchTiming {
 
 hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p,
                         hipStream_t stream, const LaunchTiming& timing = LaunchTiming{});
+hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_t stream,
+                       const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
                         const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream,

@@ -512,25 +512,13 @@ __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, co
 // split-K decode attention
 // ---------------------------------------------------------------------------
 
-// Splits holding rows of a sequence with `rows` attended rows.
-__device__ __forceinline__ int split_count(int rows, int rows_per_split, int grid_splits,
-                                           int32_t* status, bool report) {
-  int nsplit = (rows + rows_per_split - 1) / rows_per_split;
-  if (nsplit > grid_splits) {
-    // more rows than the launch was sized for (a sequence below the declared
-    // minimum image-token count): only the launched splits exist
-    if (report) atomicOr(status, FASTOCR_FLAG_ROWS_TRUNCATED);
-    nsplit = grid_splits;
-  }
-  return nsplit;
-}
-
-// PIPE (kept-token kind only): the split's kept-row map is built once in LDS
-// (coalesced index loads), then the rounds run double-buffered like a full
-// pass, their cache rows read from LDS, so no vector index load stands
-// between one round's K/V loads and the next's.
-template <typename T, int D, int KIND, int NW, int TPW, bool PIPE = false>
-__global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void split_attn_kernel(SplitParams p) {
+// Full-cache passes (warm-up, focal layers, the FULL baseline): each
+// workgroup streams one split of rows_per_split consecutive rows of one
+// (sequence, KV head) pair in 128-row rounds, double-buffered (the next
+// round's loads are issued before the current round is computed), and
+// writes one merge state per split.
+template <typename T, int D, int KIND, int NW, int TPW>
+__global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
   constexpr int RPR = NW * TPW * kTileRows;     // rows per round
@@ -543,18 +531,12 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
 
   __shared__ float s_stat[NW][16][4];
   __shared__ float s_o[NW][HH][OST];
-  static_assert(!PIPE || KIND == KIND_SPARSE, "pipelined passes gather kept rows");
-  constexpr int PMAP = PIPE ? kMaxPipeRows : 1;
-  __shared__ int s_rowmap[PMAP];  // cache row of virtual row begin + i (PIPE)
+  static_assert(KIND == KIND_FULL || KIND == KIND_FOCAL, "kept-token passes run kept_attn_kernel");
 
-  // Full passes: x = split, y = (sequence, KV head) pair, so workgroups
-  // dispatched together stream neighbouring rows.  Kept-token passes:
-  // x = pair, y = split, dispatched split-major, so the high splits that
-  // most sequences leave empty (the grid covers the longest text the handle
-  // accepts) come last and exit while the others stream.
-  constexpr bool SPLIT_MAJOR = KIND == KIND_SPARSE;
-  const int pair = SPLIT_MAJOR ? blockIdx.x : blockIdx.y;
-  const int split = SPLIT_MAJOR ? blockIdx.y : blockIdx.x;
+  // x = split, y = (sequence, KV head) pair, so workgroups dispatched
+  // together stream neighbouring rows
+  const int pair = blockIdx.y;
+  const int split = blockIdx.x;
   const int kvh = pair % p.Hkv;
   const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
@@ -568,13 +550,12 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
   const size_t row_base = ((size_t)b * p.Hkv + kvh) * (size_t)p.S;
   const T* __restrict__ Kb = reinterpret_cast<const T*>(p.k) + row_base * D;
   const T* __restrict__ Vb = reinterpret_cast<const T*>(p.v) + row_base * D;
-  const int32_t* __restrict__ selb = (KIND == KIND_SPARSE) ? p.sel + (size_t)b * p.k_stride : nullptr;
 
   // Loads that do not depend on the sequence extent are issued before it is
-  // read, so they are in flight together: the query slice and, for the first
-  // round, the kept indices (sparse kind) or the K/V rows themselves (full
-  // kinds).  Any row below S lies inside the cache allocation; rows past the
-  // extent get zero weight and their V values are zeroed once it is known.
+  // read, so they are in flight together: the query slice and the first
+  // round's K/V rows.  Any row below S lies inside the cache allocation; rows
+  // past the extent get zero weight and their V values are zeroed once it is
+  // known.
   uint32_t qw[KW];
   if (col < G) {
     const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D;
@@ -586,30 +567,11 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
   const int r_first = begin + wave * kTileRows;  // this wave's first tile row
   uint32_t kw[TPW][KW];
   uint32_t vw[TPW][4][VW];
-  int jpre[TPW][5];  // sparse: kept indices of the first round's rows
   // Splits below sure_splits hold rows for every sequence the handle
   // accepts: they load ahead.  The others may be empty and learn that
   // from the extent before loading anything.
-  const bool ahead = !PIPE && split < p.sure_splits;
-  // pipelined kept-token pass: this thread's share of the split's kept
-  // indices (virtual rows begin + tid + i*NT), coalesced
-  constexpr int PI = PIPE ? kMaxPipeRows / NT : 1;
-  int jmap[PI];
-  if constexpr (PIPE) {
-#pragma unroll
-    for (int i = 0; i < PI; ++i)
-      jmap[i] = tid + i * NT < p.rows_per_split ? selb[min(begin + tid + i * NT, p.k_stride - 1)] : 0;
-  }
-  if (!ahead) {
-  } else if constexpr (KIND == KIND_SPARSE) {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tile = r_first + u * NW * kTileRows;
-      jpre[u][0] = selb[min(tile + col, p.k_stride - 1)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) jpre[u][1 + j] = selb[min(tile + 4 * grp + j, p.k_stride - 1)];
-    }
-  } else {
+  const bool ahead = split < p.sure_splits;
+  if (ahead) {
     const int spec_end = min(begin + p.rows_per_split, p.S);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -642,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
     if (tid < C16) reinterpret_cast<uint4*>(kc)[tid] = reinterpret_cast<const uint4*>(knew)[tid];
     else if (tid < 2 * C16) reinterpret_cast<uint4*>(vc)[tid - C16] = reinterpret_cast<const uint4*>(vnew)[tid - C16];
   }
-  if (KIND != KIND_SPARSE && app && ahead) {
+  if (app && ahead) {
     // a full pass loaded this wave's first-round rows before the extent was
     // known: the current token's row, if among them, is reloaded from
     // k_new / v_new
@@ -658,49 +620,14 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
     }
   }
   if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
-  const int kept = (KIND == KIND_SPARSE) ? kept_rows(p.sel_cnt, b, n, p.k_stride) : n;
-  const int rows = (KIND == KIND_SPARSE) ? kept + (len - n) : len;
-  (void)split_count(rows, p.rows_per_split, p.grid_splits, p.status, reporter);
-  const bool direct = p.direct;  // one split per sequence: write the output here
+  const int rows = len;
   if (begin >= rows) {
-    if (direct) {  // no rows at all: zero output
-      T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
-      for (int i = tid; i < G * D; i += NT) store_out<T>(out + i, 0.f);
-    } else {
-      // an empty split: states that carry no weight in the merge (one per
-      // wave with per-wave states, one per workgroup otherwise)
-      const int SPW = (KIND == KIND_SPARSE && p.wave_states) ? NW : 1;
-      for (int i = tid; i < G * SPW; i += NT)
-        p.pstat[((size_t)b * p.Hq + kvh * G + i / SPW) * p.max_splits + (size_t)split * SPW + i % SPW] =
-            make_float4(-INFINITY, 0.f, 0.f, 0.f);
-    }
+    // an empty split: a state that carries no weight in the merge
+    for (int i = tid; i < G; i += NT)
+      p.pstat[((size_t)b * p.Hq + kvh * G + i) * p.max_splits + split] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
     return;
   }
   const int end = min(begin + p.rows_per_split, rows);
-
-  // Virtual row -> cache row (sparse kind), given the kept index j loaded
-  // for row r.  Branch-free, so the index loads of a round are all in
-  // flight together; a kept index outside [0, n) is clamped and reported
-  // once at the end.  Rows at or past `end` only need to stay inside the
-  // allocation.
-  bool bad_index = false;
-  auto sparse_row = [&](int r, int j) -> int {
-    const bool img = r < kept;
-    bad_index |= img && r < end && (j < 0 || j >= n);
-    const int jc = min(max(j, 0), max(n - 1, 0));
-    return img ? jc : min(n + (r - kept), p.S - 1);
-  };
-
-  if constexpr (PIPE) {
-    // the split's row map: cache row of virtual row begin + o (rows past
-    // the end map to row 0, inside the allocation; they carry no weight)
-#pragma unroll
-    for (int i = 0; i < PI; ++i) {
-      const int o = tid + i * NT;
-      if (o < p.rows_per_split) s_rowmap[o] = begin + o < end ? sparse_row(begin + o, jmap[i]) : 0;
-    }
-    __syncthreads();
-  }
 
   float m_run = -INFINITY, z = 0.f, lsum = 0.f, zt = 0.f;
   f32x4_t acc[NDB];
@@ -796,9 +723,7 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
         } else {
           pu[i] = pr[i];
         }
-        const int r = tile + 4 * grp + i;
-        const bool text = (KIND == KIND_SPARSE) ? (r >= kept) : (r >= n);
-        zt += text ? pr[i] : 0.f;
+        zt += (tile + 4 * grp + i >= n) ? pr[i] : 0.f;
       }
       z += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       lsum += (pu[0] + pu[1]) + (pu[2] + pu[3]);
@@ -824,26 +749,16 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
       }
     }
   };
-  // Rows of a round -> loads (the kept index of row r is j(r, i), i = 0 for
-  // the K row of the lane's column, 1 + j for its V rows).
-  auto load_round = [&](int r0, uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW], auto&& j_of) {
+  // The K/V loads of the round starting at row r0 (the K row of the lane's
+  // column, and its four V rows, per tile).
+  auto load_round = [&](int r0, uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW]) {
     int pk[TPW], pvr[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = r0 + u * NW * kTileRows;
-      if constexpr (PIPE) {
-        pk[u] = s_rowmap[tile + col - begin];
+      pk[u] = min(tile + col, p.S - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pvr[u][j] = s_rowmap[tile + 4 * grp + j - begin];
-      } else if constexpr (KIND == KIND_SPARSE) {
-        pk[u] = sparse_row(tile + col, j_of(u, 0, tile + col));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pvr[u][j] = sparse_row(tile + 4 * grp + j, j_of(u, 1 + j, tile + 4 * grp + j));
-      } else {
-        pk[u] = min(tile + col, p.S - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pvr[u][j] = min(tile + 4 * grp + j, p.S - 1);
-      }
+      for (int j = 0; j < 4; ++j) pvr[u][j] = min(tile + 4 * grp + j, p.S - 1);
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -855,43 +770,24 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
       }
     }
   };
-  auto j_loaded = [&](int, int, int r) { return selb[min(r, p.k_stride - 1)]; };
-
   // Round r covers rows [begin + r*RPR, +RPR); tile u of wave w in a round
   // starts at row (u*NW + w)*16, so neighbouring waves read neighbouring
-  // tiles.  The first round's loads (full kinds) or indices (sparse kind)
-  // are already in flight.
-  if constexpr (KIND == KIND_SPARSE && !PIPE) {
-    // kept-token passes are short (one or two rounds per split): one
-    // register buffer, higher occupancy
-    if (r_first < end) {
-      if (ahead) load_round(r_first, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
-      else load_round(r_first, kw, vw, j_loaded);
-      round(r_first, kw, vw);
-    }
-    for (int r0 = r_first + RPR; r0 < end; r0 += RPR) {
-      uint32_t kw2[TPW][KW];
-      uint32_t vw2[TPW][4][VW];
-      load_round(r0, kw2, vw2, j_loaded);
-      round(r0, kw2, vw2);
-    }
-  } else if (r_first < end) {
-    // full and pipelined kept-token passes: rounds alternate between two
-    // register buffers, the next round's loads are issued before the
-    // current round is computed
-    if (!ahead) load_round(r_first, kw, vw, j_loaded);
+  // tiles.  Rounds alternate between two register buffers; the next round's
+  // loads are issued before the current round is computed (the first
+  // round's loads are already in flight unless the split loaded nothing
+  // ahead).
+  if (r_first < end) {
+    if (!ahead) load_round(r_first, kw, vw);
     uint32_t kw2[TPW][KW];
     uint32_t vw2[TPW][4][VW];
     for (int r0 = r_first; r0 < end; r0 += 2 * RPR) {
-      if (r0 + RPR < end) load_round(r0 + RPR, kw2, vw2, j_loaded);
+      if (r0 + RPR < end) load_round(r0 + RPR, kw2, vw2);
       round(r0, kw, vw);
       if (r0 + RPR >= end) break;
-      if (r0 + 2 * RPR < end) load_round(r0 + 2 * RPR, kw, vw, j_loaded);
+      if (r0 + 2 * RPR < end) load_round(r0 + 2 * RPR, kw, vw);
       round(r0 + RPR, kw2, vw2);
     }
   }
-
-  if (KIND == KIND_SPARSE && bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
 
   // ---- per-wave totals (the 4 lane groups of a head hold partial sums)
   z += __shfl_xor(z, 16);
@@ -901,30 +797,6 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
   zt += __shfl_xor(zt, 16);
   zt += __shfl_xor(zt, 32);
 
-  if constexpr (KIND == KIND_SPARSE) {
-    if (p.wave_states) {
-      // One state per wave (state split * NW + wave), straight from
-      // registers: no cross-wave combine, no barrier.  Lane
-      // (c, g) holds head c's unnormalised outputs for d in [g*D/4, (g+1)*D/4),
-      // element d = (4g + i)*NDB + db in acc[db][i].  A wave without rows
-      // leaves max -inf, which the merge gives weight 0 without reading its
-      // partial output.
-      if (col < G) {
-        const size_t st = ((size_t)b * p.Hq + kvh * G + col) * p.max_splits + (size_t)split * NW + wave;
-        if (grp == 0) p.pstat[st] = make_float4(m_run, z, lsum, zt);
-        if (m_run != -INFINITY) {
-          float4* o = reinterpret_cast<float4*>(p.po + st * D + grp * (D / 4));
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int d4 = 0; d4 < NDB / 4; ++d4)
-              o[(i * NDB) / 4 + d4] = make_float4(acc[4 * d4][i], acc[4 * d4 + 1][i], acc[4 * d4 + 2][i],
-                                                  acc[4 * d4 + 3][i]);
-        }
-      }
-      return;
-    }
-  }
   if (grp == 0) {
     s_stat[wave][col][0] = m_run;
     s_stat[wave][col][1] = z;
@@ -936,7 +808,6 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
   // unscaled accumulator in LDS, and the reducing threads weight wave w by
   // exp2(m_w - M) themselves, so one barrier per round suffices
   const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
-  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
   for (int h0 = 0; h0 < G; h0 += HH) {
     if (h0 > 0) __syncthreads();  // the previous round has read s_o
     if (col >= h0 && col < h0 + HH) {
@@ -957,18 +828,13 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
         mw[w] = s_stat[w][h0 + h][0];
         M = fmaxf(M, mw[w]);
       }
-      float o = 0.f, L = 0.f;
+      float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float e = __builtin_amdgcn_exp2f(mw[w] - M);
-        o += s_o[w][h][d] * e;
-        L += s_stat[w][h0 + h][2] * e;
-      }
-      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, o / L);
-      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+      for (int w = 0; w < NW; ++w) o += s_o[w][h][d] * __builtin_amdgcn_exp2f(mw[w] - M);
+      p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
     }
   }
-  if (!direct && tid < G) {
+  if (tid < G) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][tid][0]);
@@ -976,6 +842,300 @@ __global__ __launch_bounds__(NW * 64, split_blocks_per_cu(KIND, PIPE)) void spli
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float e = __builtin_amdgcn_exp2f(s_stat[w][tid][0] - M);
+      zz += s_stat[w][tid][1] * e;
+      ll += s_stat[w][tid][2] * e;
+      tt += s_stat[w][tid][3] * e;
+    }
+    p.pstat[slot0 + (size_t)tid * p.max_splits] = make_float4(M, zz, ll, tt);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kept-token pass (non-focal layers)
+// ---------------------------------------------------------------------------
+
+// Attention of one (sequence, KV head) pair over its kept image rows
+// (gathered by index) and its text rows, as virtual rows r = 0 .. rows - 1:
+// r < kept is image token sel[r], the others are text row n + r - kept.  The
+// pair's 16-row tiles are dealt round-robin to its P workgroups (grid y):
+// workgroup s takes tiles s, s + P, s + 2P, ..., round j of it holding its
+// tiles j*TPR .. j*TPR + TPR - 1 (wave w, slot u: tile j*TPR + u*NW + w).
+// So at any step every workgroup of a pair has the same number of rows, to
+// within one tile, and a tile's rows do not depend on the pair's row count:
+// the kept indices of the first round load before the sequence extent is
+// read.  (Staging the workgroup's indices in LDS behind a barrier measured
+// ~1 us slower per launch: every wave then waits for all of them; loading a
+// round's indices during the previous round needs registers the kernel does
+// not have at 3 workgroups per CU, and the spills cost more than it saves.)
+// Each workgroup combines its waves' softmax states in LDS.  With one
+// workgroup per pair it writes the output; otherwise it writes its state for
+// the merge kernel.  (A variant in which the pair's last workgroup merged the
+// states itself, behind an arrival counter, measured no faster than the
+// merge launch with device-coherent state stores and 3-4x slower with
+// device-scope release/acquire fences, whose L2 write-back dominates.)
+template <typename T, int D, int NW, int TPW>
+__global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(SplitParams p) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int NT = NW * 64;                   // threads
+  constexpr int TPR = NW * TPW;                 // tiles per workgroup round
+  constexpr int E = D / 4;                      // K/q elements per lane
+  constexpr int KW = E * (int)sizeof(T) / 4;    // ... as 32-bit words
+  constexpr int NDB = D / 16;                   // PV d-blocks = V elements per row per lane
+  constexpr int VW = NDB * (int)sizeof(T) / 4;  // V words per row per lane
+  constexpr int HH = 8;                         // heads per LDS combine round
+  constexpr int OST = D + 1;                    // padded LDS row of partial outputs
+
+  __shared__ float s_stat[NW][16][4];
+  __shared__ float s_o[NW][HH][OST];
+
+  const int pair = blockIdx.x;
+  const int split = blockIdx.y;
+  const int P = p.grid_splits;
+  const int kvh = pair % p.Hkv;
+  const int b = pair / p.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+
+  const size_t row_base = ((size_t)b * p.Hkv + kvh) * (size_t)p.S;
+  const T* __restrict__ Kb = reinterpret_cast<const T*>(p.k) + row_base * D;
+  const T* __restrict__ Vb = reinterpret_cast<const T*>(p.v) + row_base * D;
+  const int32_t* __restrict__ selb = p.sel + (size_t)b * p.k_stride;
+  // first virtual row of this wave's tile in slot u of round j
+  auto tile_row = [&](int j, int u) { return (split + P * (j * TPR + u * NW + wave)) * kTileRows; };
+
+  // loads that do not depend on the sequence extent: the first round's kept
+  // indices (jpre[u][0] for the K row of the lane's column, jpre[u][1 + j]
+  // for its V rows) and the query slice
+  int jpre[TPW][5];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = tile_row(0, u);
+    jpre[u][0] = selb[min(tile + col, p.k_stride - 1)];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) jpre[u][1 + jj] = selb[min(tile + 4 * grp + jj, p.k_stride - 1)];
+  }
+  uint32_t qw[KW];
+  if (col < G) {
+    const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D;
+    load_slice<T, KW>(qw, qp, grp);
+  } else {
+#pragma unroll
+    for (int i = 0; i < KW; ++i) qw[i] = 0u;
+  }
+
+  int n, len;
+  const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
+  const bool reporter = split == 0 && kvh == 0 && tid == 0;
+  if (clamped && reporter) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
+
+  // Fused append: the current token (cache row len - 1, a text row) comes
+  // from k_new / v_new in every load of this launch, and workgroup 0 of the
+  // pair writes it into the caches for later steps.
+  const int cur = len - 1;
+  const bool app = p.k_new != nullptr && len > 0;
+  const T* __restrict__ knew = app ? reinterpret_cast<const T*>(p.k_new) + ((size_t)b * p.Hkv + kvh) * D : nullptr;
+  const T* __restrict__ vnew = app ? reinterpret_cast<const T*>(p.v_new) + ((size_t)b * p.Hkv + kvh) * D : nullptr;
+  if (app && split == 0) {
+    constexpr int C16 = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    T* kc = reinterpret_cast<T*>(p.k_w) + (row_base + cur) * D;
+    T* vc = reinterpret_cast<T*>(p.v_w) + (row_base + cur) * D;
+    if (tid < C16) reinterpret_cast<uint4*>(kc)[tid] = reinterpret_cast<const uint4*>(knew)[tid];
+    else if (tid < 2 * C16) reinterpret_cast<uint4*>(vc)[tid - C16] = reinterpret_cast<const uint4*>(vnew)[tid - C16];
+  }
+  const int kept = kept_rows(p.sel_cnt, b, n, p.k_stride);
+  const int rows = kept + (len - n);
+
+  // virtual row -> cache row, given the kept index j loaded for row r
+  // (branch-free; an index outside [0, n) is clamped and reported once)
+  bool bad_index = false;
+  auto cache_row = [&](int r, int j) -> int {
+    const bool img = r < kept;
+    bad_index |= img && r < rows && (j < 0 || j >= n);
+    const int jc = min(max(j, 0), max(n - 1, 0));
+    return img ? jc : min(n + (r - kept), p.S - 1);
+  };
+
+  float m_run = -INFINITY, z = 0.f, lsum = 0.f, zt = 0.f;
+  f32x4_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One round of this wave: tiles starting at virtual rows tb[u], whose K/V
+  // words are in kw / vw.  Rows at or past `rows` carry no weight.
+  auto round = [&](const int (&tb)[TPW], uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW]) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = tb[u] + 4 * grp + j < rows;
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vw[u][j][w] = ok ? vw[u][j][w] : 0u;
+      }
+    float x[TPW][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[u][i] = -INFINITY;
+      if (tb[u] >= rows) continue;  // uniform over the wave
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF) {
+#pragma unroll
+        for (int kk = 0; kk < E / 4; ++kk)
+          s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(kw[u][2 * kk], kw[u][2 * kk + 1]),
+                                                        as_bf16x4(qw[2 * kk], qw[2 * kk + 1]), s, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < E; ++kk)
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kw[u][kk]), __uint_as_float(qw[kk]), s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[u][i] = (tb[u] + 4 * grp + i < rows) ? s[i] * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[u][i]);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    z *= alpha;
+    lsum *= alpha;
+    zt *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (tb[u] >= rows) continue;
+      float pr[4], pu[4];
+      uint32_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[u][i] - m_new);
+        if constexpr (BF) {
+          pb[i] = f32_to_bf16(pr[i]);
+          pu[i] = bf16_to_f32(pb[i]);
+        } else {
+          pu[i] = pr[i];
+        }
+        zt += (tb[u] + 4 * grp + i >= kept) ? pr[i] : 0.f;
+      }
+      z += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      lsum += (pu[0] + pu[1]) + (pu[2] + pu[3]);
+      if constexpr (BF) {
+        const bf16x4_t pv = as_bf16x4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int w = db >> 1;
+          const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo = __builtin_amdgcn_perm(vw[u][1][w], vw[u][0][w], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vw[u][3][w], vw[u][2][w], sel);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(lo, hi), pv, acc[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vw[u][i][db]), pr[i], acc[db], 0, 0, 0);
+      }
+    }
+  };
+  // The K/V loads of a round (the K row of the lane's column and its four V
+  // rows, per tile); the kept index of row r is j_of(u, i, r), i = 0 for the
+  // K row, 1 + j for the V rows.
+  auto load_round = [&](const int (&tb)[TPW], uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW], auto&& j_of) {
+    int pk[TPW], pvr[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      pk[u] = cache_row(tb[u] + col, j_of(u, 0, tb[u] + col));
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        pvr[u][jj] = cache_row(tb[u] + 4 * grp + jj, j_of(u, 1 + jj, tb[u] + 4 * grp + jj));
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (tb[u] < rows) {  // uniform over the wave
+        load_slice<T, KW>(kw[u], app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D, grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          load_words(vw[u][j], (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB, VW);
+      }
+    }
+  };
+  for (int j = 0; tile_row(j, 0) < rows; ++j) {
+    int tb[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) tb[u] = tile_row(j, u);
+    uint32_t kw[TPW][KW];
+    uint32_t vw[TPW][4][VW];
+    if (j == 0) load_round(tb, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
+    else load_round(tb, kw, vw, [&](int, int, int r) { return selb[min(r, p.k_stride - 1)]; });
+    round(tb, kw, vw);
+  }
+  if (bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);
+
+  // ---- combine the waves: per-wave totals, then rounds of HH heads (each
+  // wave leaves its unscaled accumulator in LDS; the reducing threads weight
+  // wave w by exp2(m_w - M)); a workgroup without rows has M = -inf
+  z += __shfl_xor(z, 16);
+  z += __shfl_xor(z, 32);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  zt += __shfl_xor(zt, 16);
+  zt += __shfl_xor(zt, 32);
+  if (grp == 0) {
+    s_stat[wave][col][0] = m_run;
+    s_stat[wave][col][1] = z;
+    s_stat[wave][col][2] = lsum;
+    s_stat[wave][col][3] = zt;
+  }
+  const bool direct = P == 1;
+  const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + kvh * G) * D;
+  for (int h0 = 0; h0 < G; h0 += HH) {
+    if (h0 > 0) __syncthreads();  // the previous round has read s_o
+    if (col >= h0 && col < h0 + HH) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i];
+    }
+    __syncthreads();
+    const int hn = min(HH, G - h0);
+    for (int idx = tid; idx < hn * D; idx += NT) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][h0 + h][0]);
+      float o = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_stat[w][h0 + h][0];
+        const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        o += s_o[w][h][d] * e;
+        L += s_stat[w][h0 + h][2] * e;
+      }
+      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, M == -INFINITY ? 0.f : o / L);
+      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+    }
+  }
+  if (direct) return;
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][tid][0]);
+    float zz = 0.f, ll = 0.f, tt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_stat[w][tid][0];
+      const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       zz += s_stat[w][tid][1] * e;
       ll += s_stat[w][tid][2] * e;
       tt += s_stat[w][tid][3] * e;
@@ -1030,7 +1190,6 @@ __global__ __launch_bounds__(256, 2) void split_valu_kernel(SplitParams p) {
   int n, len;
   const bool clamped = seq_extent(p.lens, b, p.S, p.n_cap, n, len);
   if (clamped && split == 0 && kvh == 0 && tid == 0) atomicOr(p.status, FASTOCR_FLAG_LENS_CLAMPED);
-  (void)split_count(len, p.rows_per_split, p.grid_splits, p.status, split == 0 && kvh == 0 && tid == 0);
   const size_t slot0 = ((size_t)b * p.Hq + kvh * G) * p.max_splits + split;
   if (begin >= len) {
     if (tid < G) p.pstat[slot0 + (size_t)tid * p.max_splits] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
@@ -1524,8 +1683,7 @@ static hipError_t launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
 template <typename T, int D>
 static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream,
                                  const LaunchTiming& timing) {
-  const dim3 block(kSplitThreads);
-  const dim3 grid = kind == KIND_SPARSE ? dim3(p.Hkv * p.B, p.grid_splits) : dim3(p.grid_splits, p.Hkv * p.B);
+  const dim3 block(kSplitThreads), grid(p.grid_splits, p.Hkv * p.B);
   switch (kind) {
     case KIND_FULL:
       if constexpr (sizeof(T) == 2 && D == 128)
@@ -1535,14 +1693,24 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
     case KIND_FOCAL:
       return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, kTilesPerWave>, grid, block, stream,
                     timing, p);
-    case KIND_SPARSE:
-      if (p.pipe)
-        return launch(split_attn_kernel<T, D, KIND_SPARSE, kSplitWaves, kTilesPerWave, true>, grid, block,
-                      stream, timing, p);
-      return launch(split_attn_kernel<T, D, KIND_SPARSE, kSplitWaves, kTilesPerWave>, grid, block, stream,
-                    timing, p);
+    default:
+      return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t launch_kept_t(const SplitParams& p, hipStream_t stream, const LaunchTiming& timing) {
+  const dim3 block(kSplitThreads), grid(p.Hkv * p.B, p.grid_splits);
+  return launch(kept_attn_kernel<T, D, kSplitWaves, kTilesPerWave>, grid, block, stream, timing, p);
+}
+
+hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_t stream,
+                       const LaunchTiming& timing) {
+  if (dtype == FASTOCR_DTYPE_BF16)
+    return head_dim == 128 ? launch_kept_t<uint16_t, 128>(p, stream, timing)
+                           : launch_kept_t<uint16_t, 64>(p, stream, timing);
+  return head_dim == 128 ? launch_kept_t<float, 128>(p, stream, timing)
+                         : launch_kept_t<float, 64>(p, stream, timing);
 }
 
 hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitParams& p, hipStream_t stream,

@@ -38,15 +38,12 @@
  * Environment settings, read once by fastocr_create (for measurement and
  * tests; results do not depend on them beyond rounding order):
  *   FASTOCR_FULL_ROWS=R     rows per split of full passes (multiple of 16)
- *   FASTOCR_SPARSE_ROWS=R   rows per split of kept-token passes; R at least the
- *                           longest kept-token pass gives one split per
- *                           sequence that writes the output (no merge)
- *   FASTOCR_WAVE_STATES=0|1 kept-token splits write one merge state per wave
- *                           (default: only for passes of at most one workgroup
- *                           per CU)
- *   FASTOCR_SPARSE_PIPE=0|1 kept-token passes of multi-round splits sized like
- *                           a full pass's, the split's row map in LDS (default:
- *                           when batch x num_kv_heads x k_max >= 131072)
+ *   FASTOCR_SPARSE_ROWS=R   kept-token passes: as many workgroups per (sequence,
+ *                           KV head) pair as R rows each need at the longest
+ *                           text the handle accepts (default: the workgroups
+ *                           that fill one wave of the device); R at least that
+ *                           length gives one workgroup per pair, which writes
+ *                           the output (no merge)
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
@@ -90,9 +87,6 @@ extern "C" {
 /* ---- device status flags (fastocr_get_status) ---------------------------- */
 #define FASTOCR_FLAG_LENS_CLAMPED 1 /* a lens entry was out of range and was clamped */
 #define FASTOCR_FLAG_INDEX_CLAMPED 2 /* a selected index was out of range and was clamped */
-#define FASTOCR_FLAG_ROWS_TRUNCATED 4 /* a sequence had fewer image tokens than min_img_tokens
-                                        or more text tokens than max_text_tokens; its kept-token
-                                        rows beyond the launch were not attended */
 
 /* ---- kernel classes timed by fastocr_get_timing -------------------------- */
 #define FASTOCR_KC_FULL_SPLIT 0   /* split-K full attention (warm-up, FULL mode) */
@@ -114,16 +108,16 @@ typedef struct fastocr_config {
   int32_t max_seq_len;    /* S: row stride of the KV cache (capacity per sequence) */
   int32_t max_img_tokens; /* upper bound on image tokens per sequence (<= S) */
   int32_t min_img_tokens; /* lower bound on image tokens per sequence, 0 if unknown;
-                             only used to size the sparse launch */
+                             only used to size launches (a sequence outside the
+                             declared bounds is still attended in full) */
   int32_t dtype;          /* FASTOCR_DTYPE_* */
   int32_t num_focal;      /* |C|, 1 <= |C| <= L */
   int32_t warmup_steps;   /* w >= 1 */
   int32_t mode;           /* FASTOCR_MODE_* */
   int32_t max_text_tokens; /* upper bound on a sequence's text tokens len_b - n_img_b
                               (prompt + generated), 0 if unknown; only used to size
-                              the sparse launch.  A sequence beyond the bounds given
-                              by min_img_tokens / max_text_tokens is truncated to
-                              the launched splits and flagged (FASTOCR_FLAG_ROWS_TRUNCATED). */
+                              the kept-token launch (a sequence beyond it is still
+                              attended in full) */
   int32_t reprofile_every; /* R >= 0: after every R pruned steps the next w steps are a new
                               warm-up window and the focal set is picked again from that
                               window alone (periodic re-selection; 0 = pick once) */
@@ -136,11 +130,10 @@ typedef struct fastocr_info {
   int32_t k_max;          /* capacity of the kept-set buffer per sequence */
   int32_t full_rows_per_split;
   int32_t full_max_splits;
-  int32_t sparse_rows_per_split;
-  int32_t sparse_max_splits;
-  int32_t sparse_direct;  /* 1: non-focal layers finish in one split (no merge launch) */
-  int32_t sparse_wave_states; /* 1: kept-token splits write one merge state per wave */
-  int32_t sparse_pipe;    /* 1: kept-token passes run pipelined multi-round splits */
+  int32_t sparse_rows_per_split; /* kept-token pass: rows per workgroup at the longest text */
+  int32_t sparse_max_splits;     /* kept-token pass: workgroups per (sequence, KV head) pair */
+  int32_t sparse_direct;  /* 1: non-focal layers finish in one workgroup per (sequence, KV head)
+                             pair (no merge launch) */
   int32_t profiles;       /* focal-set picks so far (first warm-up and re-selections) */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;

@@ -195,33 +195,25 @@ def test_plan_launch_null_and_cu_count():
 
 
 MAX_MERGE_STATES = 1024  # merge states per head one merge workgroup holds in LDS
-MAX_PIPE_ROWS = 2048     # rows of one pipelined kept-token split (its row map lives in LDS)
+MAX_KEPT_SPLITS = 32     # workgroups per (sequence, KV head) pair of a kept-token pass
 
 
 def _check_plan(info, S):
-    states = info["sparse_max_splits"] * (4 if info["sparse_wave_states"] else 1)
     assert info["full_max_splits"] * info["full_rows_per_split"] >= S
     assert info["full_max_splits"] <= MAX_MERGE_STATES
-    assert states <= MAX_MERGE_STATES
-    if info["sparse_pipe"]:
-        assert info["sparse_rows_per_split"] <= MAX_PIPE_ROWS
-        assert info["sparse_rows_per_split"] % 128 == 0
-    if info["sparse_wave_states"]:
-        assert states <= 64
+    assert 1 <= info["sparse_max_splits"] <= MAX_KEPT_SPLITS
+    assert info["sparse_direct"] == (info["sparse_max_splits"] == 1)
 
 
-@pytest.mark.parametrize("pipe", ["", "1"])
-def test_plan_multi_million_rows_stays_within_merge_capacity(monkeypatch, pipe):
-    # a kept-token pass longer than 1024 pipelined splits of 2048 rows runs
-    # one-round splits instead, so the merge never sees more states than
-    # its LDS holds
-    monkeypatch.setenv("FASTOCR_SPARSE_PIPE", pipe)
+def test_plan_multi_million_rows_stays_within_merge_capacity():
+    # full passes of millions of rows grow their splits, and kept-token
+    # passes their rows per workgroup, so the merge never sees more states
+    # than its LDS holds
     for S in (2_200_000, 3_000_000, 8_000_000):
         info = _plan(num_layers=2, num_q_heads=16, num_kv_heads=8, head_dim=128, batch=1, max_seq_len=S,
                      max_img_tokens=S // 2, tau=0.05, num_focal=1, warmup_steps=1, dtype="bf16")
         _check_plan(info, S)
-        if pipe and (info["k_max"] + S - S // 2 + MAX_PIPE_ROWS - 1) // MAX_PIPE_ROWS > MAX_MERGE_STATES:
-            assert info["sparse_pipe"] == 0
+        assert info["sparse_max_splits"] * info["sparse_rows_per_split"] >= info["k_max"] + S - S // 2
 
 
 def test_plan_random_configs_within_kernel_limits():
@@ -241,17 +233,26 @@ def test_plan_random_configs_within_kernel_limits():
 
 
 def test_plan_of_benchmark_workloads():
-    # 7B-like B=1: one-round kept-token splits with per-wave states;
-    # 72B-like B=8 at tau 0.2: pipelined kept-token splits
-    b1 = _plan(num_layers=28, num_q_heads=28, num_kv_heads=4, head_dim=128, batch=1, max_seq_len=7488,
-               max_img_tokens=6400, min_img_tokens=6400, max_text_tokens=64 + 1024, tau=0.05, num_focal=4,
-               warmup_steps=8, dtype="bf16")
-    assert b1["k_max"] == 320 and b1["sparse_wave_states"] == 1 and b1["sparse_pipe"] == 0
-    b8 = _plan(num_layers=80, num_q_heads=64, num_kv_heads=8, head_dim=128, batch=8, max_seq_len=14976,
-               max_img_tokens=12800, min_img_tokens=12800, max_text_tokens=128 + 2048, tau=0.2, num_focal=8,
-               warmup_steps=8, dtype="bf16")
-    assert b8["k_max"] == 2560 and b8["sparse_pipe"] == 1
-    for info in (b1, b8):
+    # kept-token passes: each pair's tiles dealt to the workgroups that fill
+    # one wave of resident workgroups (3 per CU), at most one per 16-row tile
+    # at the longest text and at most 32
+    def plan(**kw):
+        base = dict(num_layers=80, num_q_heads=64, num_kv_heads=8, head_dim=128, batch=8, max_seq_len=14976,
+                    max_img_tokens=12800, min_img_tokens=12800, max_text_tokens=128 + 2048, tau=0.05,
+                    num_focal=8, warmup_steps=8, dtype="bf16")
+        base.update(kw)
+        return _plan(**base)
+    b1 = plan(num_layers=28, num_q_heads=28, num_kv_heads=4, batch=1, max_seq_len=7488, max_img_tokens=6400,
+              min_img_tokens=6400, max_text_tokens=64 + 1024, num_focal=4)
+    assert b1["k_max"] == 320 and b1["sparse_max_splits"] == 32
+    w8 = plan()
+    assert w8["k_max"] == 640 and w8["sparse_max_splits"] == 3 * 256 // 64
+    b4 = plan(num_layers=64, num_q_heads=40, num_kv_heads=8, batch=4, max_seq_len=20608, max_img_tokens=16384,
+              min_img_tokens=16384, max_text_tokens=128 + 4096, num_focal=6)
+    assert b4["k_max"] == 820 and b4["sparse_max_splits"] == 3 * 256 // 32
+    t2 = plan(tau=0.2)
+    assert t2["k_max"] == 2560 and t2["sparse_max_splits"] == 12
+    for info in (b1, w8, b4, t2):
         _check_plan(info, info["full_max_splits"] * info["full_rows_per_split"])
 
 

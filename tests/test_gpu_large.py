@@ -101,7 +101,8 @@ def run_sampled(wl, sample_steps):
 
 
 # oracle image-attention ratio of every layer per input set (workload name,
-# seed): tau does not enter the inputs, so the tests of a tau sweep share them
+# seed, query noise): tau does not enter the inputs, so the tests of a tau
+# sweep share them
 _RATIOS = {}
 
 
@@ -109,7 +110,7 @@ def oracle_ratios(run):
     """Mean warm-up image mass of every layer (over steps, sequences and
     heads), from the keys and queries the GPU consumed."""
     wl, st = run["wl"], run["st"]
-    key = (wl.name, wl.seed)
+    key = (wl.name, wl.seed, wl.sigma)
     if key in _RATIOS:
         return _RATIOS[key]
     L, B, w = wl.num_layers, wl.batch, wl.warmup_steps

@@ -98,18 +98,22 @@ def test_topk_bit_exact(tau, n_cap):
         np.testing.assert_array_equal(idx[b, :k], want, err_msg=f"b={b} n={n} k={k}")
 
 
-# kept-token pass variants: split + merge with one state per workgroup (a
-# cross-wave combine) or one per wave, one split per sequence (no merge), and
-# pipelined multi-round splits (row map in LDS) with and without a merge
-SPARSE_VARIANTS = pytest.mark.parametrize(
-    "rows", [("", "0", "0"), ("", "1", "0"), ("16384", "", "0"), ("384", "0", "1"), ("16384", "", "1")],
-    ids=["split-merge", "wave-states", "direct", "pipelined", "pipelined-direct"])
+# kept-token pass variants (environment, expected plan): each pair's tiles
+# dealt round-robin to the workgroups that fill one wave, merged by the merge
+# kernel; a few workgroups per pair (several rounds each); one workgroup per
+# pair (no merge)
+KEPT_VARIANTS = {
+    "kept": ({}, dict(sparse_direct=0)),
+    "kept-few-splits": ({"FASTOCR_SPARSE_ROWS": "1024"}, dict()),
+    "direct": ({"FASTOCR_SPARSE_ROWS": "16384"}, dict(sparse_direct=1)),
+}
+SPARSE_VARIANTS = pytest.mark.parametrize("rows", list(KEPT_VARIANTS), ids=list(KEPT_VARIANTS))
 
 
 def _sparse_variant(monkeypatch, rows):
-    monkeypatch.setenv("FASTOCR_SPARSE_ROWS", rows[0])
-    monkeypatch.setenv("FASTOCR_WAVE_STATES", rows[1])
-    monkeypatch.setenv("FASTOCR_SPARSE_PIPE", rows[2])
+    monkeypatch.delenv("FASTOCR_SPARSE_ROWS", raising=False)
+    for k, v in KEPT_VARIANTS[rows][0].items():
+        monkeypatch.setenv(k, v)
 
 
 @SPARSE_VARIANTS
@@ -121,10 +125,8 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
                 steps=3)
     h = fo.fastocr_create(make_config(up))
     info = fo.fastocr_get_info(h)
-    if rows[2] != "1":  # a pipelined split holds at most 2048 rows
-        assert info["sparse_direct"] == (1 if rows[0] == "16384" else 0)
-    assert info["sparse_wave_states"] == (1 if rows[1] == "1" else 0)
-    assert info["sparse_pipe"] == (1 if rows[2] == "1" else 0)
+    for key, value in KEPT_VARIANTS[rows][1].items():
+        assert info[key] == value, (rows, key, info)
     wl = up.wl
     for l in range(wl.num_layers):  # one warm-up step
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
@@ -194,10 +196,11 @@ def test_lens_out_of_range_sets_flag():
     assert fo.fastocr_get_status(h) & fo.FLAG_LENS_CLAMPED
 
 
-def test_text_beyond_declared_bound_sets_flag():
-    # max_text_tokens = 1 sizes the kept-token launch for k + 1 rows (three
-    # 128-row splits for k = 320); 66 text rows exceed it: the rows beyond the
-    # launch are dropped and the handle reports it
+def test_text_beyond_declared_bound(monkeypatch):
+    # max_text_tokens = 1 declares at most one text row; the sequence has 66.
+    # The kept-token kernel deals whatever rows a pair has to its workgroups,
+    # so every row is still attended: no flag, the oracle's output
+    monkeypatch.delenv("FASTOCR_SPARSE_ROWS", raising=False)
     up = upload(get_workload("7b-b1").with_overrides(num_layers=2, warmup_steps=1, num_focal=1), steps=2)
     h = fo.fastocr_create(make_config(up, max_text_tokens=1))
     wl = up.wl
@@ -207,10 +210,15 @@ def test_text_beyond_declared_bound_sets_flag():
     fo.fastocr_profile_warmup(h)
     assert fo.fastocr_get_status(h) == 0
     fo.fastocr_set_focal_layers(h, [1])
+    k_max = fo.fastocr_get_info(h)["k_max"]
+    sel = torch.zeros((1, k_max), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((1,), dtype=torch.int32, device=DEV)
     fo.fastocr_attend(h, 0, up.Qd[0][1], up.Kd[0], up.Vd[0], up.lens[1], out)  # non-focal
+    fo.fastocr_get_selection(h, sel, cnt)
     torch.cuda.synchronize()
-    assert fo.fastocr_get_status(h) & fo.FLAG_ROWS_TRUNCATED
-    assert torch.isfinite(out.float()).all()
+    assert fo.fastocr_get_status(h) == 0
+    check_layer(up, 1, 0, out.float().cpu().numpy().astype(np.float64), "sparse",
+                used=(sel.cpu().numpy(), cnt.cpu().numpy()), what="undeclared text")
 
 
 def test_state_machine_errors():
@@ -360,12 +368,12 @@ APPEND_CASES = {
     "tiny-full": ("tiny-fp32", dict(), "full", 6, {}),
     "tiny-pruned": ("tiny-fp32", dict(), "pruned", 7, {}),
     "7b-pruned": ("7b-b1", dict(num_layers=3, warmup_steps=1, num_focal=1), "pruned", 4, {}),
-    "ragged-pipelined": ("7b-b16-ragged", dict(batch=4, num_layers=4, focal_band=(1, 2), num_focal=1,
-                                               warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
-                         "pruned", 5, {"FASTOCR_SPARSE_PIPE": "1", "FASTOCR_SPARSE_ROWS": "384"}),
-    "ragged-wave-states": ("7b-b16-ragged", dict(batch=2, num_layers=4, focal_band=(1, 2), num_focal=1,
-                                                 warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
-                           "pruned", 5, {"FASTOCR_WAVE_STATES": "1"}),
+    "ragged-few-splits": ("7b-b16-ragged", dict(batch=4, num_layers=4, focal_band=(1, 2), num_focal=1,
+                                                warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
+                          "pruned", 5, {"FASTOCR_SPARSE_ROWS": "384"}),
+    "ragged-direct": ("7b-b16-ragged", dict(batch=2, num_layers=4, focal_band=(1, 2), num_focal=1,
+                                            warmup_steps=2, n_img_range=(100, 700), n_prompt=(5, 40)),
+                      "pruned", 5, {"FASTOCR_SPARSE_ROWS": "16384"}),
 }
 
 
@@ -560,14 +568,14 @@ def test_set_focal_layers_ends_window_then_reprofiles():
             focal_now = [int(x) for x in orc.focal] if orc.focal is not None else []
             kind = "sparse" if pruned and l not in focal_now else (
                 "focal" if pruned and l not in unused_picks(focal_now, L) else "full")
-            if kind == "sparse":
-                fo.fastocr_get_selection(h, sel, cnt)
             fo.fastocr_attend(h, l, up.Qd[l][t], up.Kd[l], up.Vd[l], up.lens[t], out)
             if l == 0 and pruned:
                 focal = fo.fastocr_get_focal_layers(h)
                 assert focal == focal_now, (t, focal, focal_now)
-            if kind == "focal":
-                fo.fastocr_get_selection(h, sel, cnt)
+            # the set after the call: the one a non-focal layer attended with
+            # (a layer-0 call that ends a window re-initialises it first) or
+            # the one a focal layer picked
+            fo.fastocr_get_selection(h, sel, cnt)
             torch.cuda.synchronize()
             s_np = (sel.cpu().numpy(), cnt.cpu().numpy())
             worst = max(worst, check_layer(up, t, l, out.float().cpu().numpy().astype(np.float64), kind,
