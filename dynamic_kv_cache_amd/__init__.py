@@ -19,9 +19,9 @@ from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
 from . import _abi
-from ._abi import (DTYPE_BF16, DTYPE_F32, ERR_HIP, ERR_INVALID_ARG, ERR_OOM, ERR_STATE,  # noqa: F401
+from ._abi import (DTYPE_BF16, DTYPE_F32, ERR_HIP, ERR_INVALID_ARG, ERR_OOM, ERR_SCRATCH, ERR_STATE,  # noqa: F401
                    FLAG_INDEX_CLAMPED, FLAG_LENS_CLAMPED, KC_NAMES, MODE_FULL, MODE_PRUNED,
-                   OK)
+                   OK, STATIC_SCRATCH_MIB)
 
 
 class FastOCRError(RuntimeError):
@@ -135,6 +135,16 @@ def fastocr_create(cfg: Config, stream=None) -> Handle:
     out = ctypes.c_void_p(0)
     _check("fastocr_create", lib().fastocr_create(ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)),
                                                   ctypes.byref(out)))
+    return Handle(out.value, cfg, stream)
+
+
+def fastocr_create_static(cfg: Config, stream=None) -> Handle:
+    """fastocr_create without device allocation: the scratch lives in the
+    library's static array (at most one live static handle per GPU)."""
+    c = cfg.to_c()
+    out = ctypes.c_void_p(0)
+    _check("fastocr_create_static", lib().fastocr_create_static(
+        ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)), ctypes.byref(out)))
     return Handle(out.value, cfg, stream)
 
 

@@ -13,6 +13,8 @@ ERR_INVALID_ARG = -1
 ERR_STATE = -2
 ERR_HIP = -3
 ERR_OOM = -4
+ERR_SCRATCH = -5
+STATIC_SCRATCH_MIB = 64  # FASTOCR_STATIC_SCRATCH_MIB
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -78,6 +80,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfastocr.
 # (name, restype, argtypes)
 SIGNATURES = [
     ("fastocr_create", c_int32, [ctypes.POINTER(Config), c_void_p, ctypes.POINTER(c_void_p)]),
+    ("fastocr_create_static", c_int32, [ctypes.POINTER(Config), c_void_p, ctypes.POINTER(c_void_p)]),
     ("fastocr_attend", c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     ("fastocr_attend_append", c_int32,
      [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

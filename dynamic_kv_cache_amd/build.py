@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libfastocr.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["kernels.hip", "probe.hip", "fastocr_api.cpp"]
+SOURCES = ["kernels.hip", "probe.hip", "static_scratch.hip", "fastocr_api.cpp"]
 ARCH = os.environ.get("FASTOCR_OFFLOAD_ARCH", "gfx950")
 
 

@@ -231,6 +231,8 @@ struct fastocr_handle {
 
   void* arena = nullptr;
   size_t arena_bytes = 0;
+  bool owns_arena = true;              // false: placed by the caller (fastocr_create_static)
+  void (*on_destroy)(int device) = nullptr;
   float4* pstat = nullptr;
   float* po = nullptr;
   float* logits = nullptr;
@@ -533,11 +535,22 @@ const char* fastocr_error_string(int32_t code) {
     case FASTOCR_ERR_STATE: return "call out of order for the handle state";
     case FASTOCR_ERR_HIP: return "HIP runtime error";
     case FASTOCR_ERR_OOM: return "device allocation failed";
+    case FASTOCR_ERR_SCRATCH: return "configuration needs more scratch than the static array holds";
     default: return "unknown status";
   }
 }
 
 int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out) {
+  return fastocr::create_handle(cfg, hip_stream, out, nullptr, 0, nullptr);
+}
+
+}  // extern "C"
+
+// fastocr_create, with the scratch arena either allocated here (arena null)
+// or placed at `arena` (device memory of arena_cap bytes that the caller
+// keeps; `on_destroy(device)` is called when the handle is destroyed).
+int fastocr::create_handle(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out, void* arena,
+                           size_t arena_cap, void (*on_destroy)(int)) {
   if (!cfg || !out) return FASTOCR_ERR_INVALID_ARG;
   *out = nullptr;
   if (!config_ok(*cfg)) return FASTOCR_ERR_INVALID_ARG;
@@ -584,10 +597,21 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
                o_scores = plan.o_scores, o_warm = plan.o_warm, o_tm = plan.o_tm, o_sel = plan.o_sel,
                o_cnt = plan.o_cnt, o_status = plan.o_status, o_lens = plan.o_lens, o_hist0 = plan.o_hist0;
   h->arena_bytes = plan.arena_bytes;
-  hipError_t e = hipMalloc(&h->arena, h->arena_bytes);
-  if (e != hipSuccess) {
-    delete h;
-    return e == hipErrorOutOfMemory ? FASTOCR_ERR_OOM : FASTOCR_ERR_HIP;
+  hipError_t e = hipSuccess;
+  if (arena) {
+    if (h->arena_bytes > arena_cap) {
+      delete h;
+      return FASTOCR_ERR_SCRATCH;
+    }
+    h->arena = arena;
+    h->owns_arena = false;
+    h->on_destroy = on_destroy;
+  } else {
+    e = hipMalloc(&h->arena, h->arena_bytes);
+    if (e != hipSuccess) {
+      delete h;
+      return e == hipErrorOutOfMemory ? FASTOCR_ERR_OOM : FASTOCR_ERR_HIP;
+    }
   }
   char* base = static_cast<char*>(h->arena);
   h->pstat = reinterpret_cast<float4*>(base + o_pstat);
@@ -605,7 +629,7 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   e = hipMemsetAsync(h->arena, 0, h->arena_bytes, h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) {
-    (void)hipFree(h->arena);
+    if (h->owns_arena) (void)hipFree(h->arena);
     delete h;
     return FASTOCR_ERR_HIP;
   }
@@ -613,6 +637,8 @@ int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle**
   *out = h;
   return FASTOCR_OK;
 }
+
+extern "C" {
 
 // Focal Layer Selection at the end of a warm-up window (the first one, or a
 // periodic re-selection window): synchronises the stream.
@@ -774,7 +800,11 @@ int fastocr_destroy(fastocr_handle* h) {
   int rc = FASTOCR_OK;
   if (hipStreamSynchronize(h->stream) != hipSuccess) rc = FASTOCR_ERR_HIP;
   for (auto& ev : h->events) (void)hipEventDestroy(ev.end);
-  if (h->arena && hipFree(h->arena) != hipSuccess) rc = FASTOCR_ERR_HIP;
+  if (h->owns_arena) {
+    if (h->arena && hipFree(h->arena) != hipSuccess) rc = FASTOCR_ERR_HIP;
+  } else if (h->on_destroy) {
+    h->on_destroy(h->device);
+  }
   delete h;
   return rc;
 }

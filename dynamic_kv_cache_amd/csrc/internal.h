@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/fastocr.h"
+
 namespace fastocr {
 
 // Kinds of split-K attention pass.
@@ -125,5 +127,11 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream,
                        const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_pack(const PackParams& p, hipStream_t stream);
+
+// fastocr_create with the scratch arena allocated (arena null) or placed at
+// `arena` (arena_cap bytes of device memory the caller keeps; a larger plan
+// fails with FASTOCR_ERR_SCRATCH; on_destroy(device) runs at destroy).
+int create_handle(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out, void* arena,
+                  size_t arena_cap, void (*on_destroy)(int));
 
 }  // namespace fastocr

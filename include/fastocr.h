@@ -75,6 +75,8 @@ extern "C" {
 #define FASTOCR_ERR_STATE (-2)       /* call out of order for the handle's state machine */
 #define FASTOCR_ERR_HIP (-3)         /* HIP runtime failure (no device, launch error, ...) */
 #define FASTOCR_ERR_OOM (-4)         /* scratch allocation failed */
+#define FASTOCR_ERR_SCRATCH (-5)     /* fastocr_create_static: the configuration needs more scratch
+                                        than the static array holds */
 
 /* ---- element types of q, k_cache, v_cache and out ------------------------ */
 #define FASTOCR_DTYPE_F32 0
@@ -152,6 +154,24 @@ typedef struct fastocr_handle fastocr_handle;
  * INVALID_ARG (cfg or out null, a field out of range), HIP (no device or
  * runtime failure), OOM (scratch allocation failed). */
 int fastocr_create(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out);
+
+/* fastocr_create_static: fastocr_create without any device allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc).  The handle's scratch
+ * is placed in a static device array of FASTOCR_STATIC_SCRATCH_MIB MiB that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of memory from hipMalloc; nothing else differs (same kernels, same
+ * results).  Every static handle on a GPU shares that GPU's array, so at most
+ * one is live per GPU at a time: a second fastocr_create_static on the same
+ * device before fastocr_destroy of the first returns FASTOCR_ERR_STATE (two
+ * handles using the array at once would race).  The array keeps the last
+ * handle's contents; creation clears the part a handle uses.  fastocr_destroy
+ * releases the array for the next static handle and frees nothing.  The host
+ * handle object itself is ordinary host memory.  Errors: as fastocr_create,
+ * and FASTOCR_ERR_SCRATCH when the configuration's scratch (fastocr_info
+ * scratch_bytes, also given by fastocr_plan_launch) exceeds the array. */
+#define FASTOCR_STATIC_SCRATCH_MIB 64
+int fastocr_create_static(const fastocr_config* cfg, void* hip_stream, fastocr_handle** out);
 
 /* fastocr_attend: decode attention of one layer at the current step
  * (Method / Focal-Guided Pruning / Cross-Layer Propagation; Cross-Step
