@@ -100,6 +100,7 @@ struct Plan {
   bool keeps_all = false;        // tau = 1: non-focal layers run the full pass
   bool valu_full = false;        // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;   // a focal layer followed by a focal layer picks nothing
+  bool focal_staged = false;     // focal passes stage a split's logits in LDS
   int max_splits = 0;            // merge states per head the scratch holds
   // scratch arena: byte offsets of each array, and the total
   size_t o_pstat = 0, o_po = 0, o_logits = 0, o_mz = 0, o_scores = 0, o_warm = 0, o_tm = 0, o_sel = 0,
@@ -162,6 +163,17 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
     p.sparse_R = (int)align_up((size_t)((sparse_rows + P - 1) / P), kTileRows);
   }
   p.skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
+  // A focal pass with long splits keeps a split's image-token logits in LDS
+  // and writes each head's run once the split's rows are done, when they fit.
+  // Measured per focal pass, staged against stored as computed: 72B-like B=8
+  // (1920-row splits) 91.2 us against 100.9 (82.9 with no export at all);
+  // 32B-like B=4 (1408) 62.9 against 67.2; 7B-like B=16 (1152) 39.2 against
+  // 41.1; but 7B-like B=1 (128-row splits, one round) 7.9 against 6.7, where
+  // the write-out only lengthens the tail.  FASTOCR_FOCAL_STAGE=0 never
+  // stages, =1 stages whenever the logits fit.
+  const bool stage_fits = (int64_t)G * (p.full_R + kLogitStagePad) <= kLogitStageFloats;
+  const int stage_env = env_int("FASTOCR_FOCAL_STAGE", -1);
+  p.focal_staged = stage_fits && (stage_env < 0 ? p.full_R >= kLogitStageMinRows : stage_env != 0);
   // FASTOCR_VALU_FULL=1: full passes without MFMA (bf16, head_dim 128, groups
   // of at most kValuMaxGroup heads), to measure what the matrix cores buy
   p.valu_full = env_int("FASTOCR_VALU_FULL", 0) != 0 && c.dtype == FASTOCR_DTYPE_BF16 && c.head_dim == 128 &&
@@ -214,6 +226,7 @@ struct fastocr_handle {
   bool keeps_all = false;              // tau = 1: non-focal layers run the full pass
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;         // a focal layer followed by a focal layer picks nothing
+  bool focal_staged = false;           // focal passes stage a split's logits in LDS
   Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
@@ -356,6 +369,7 @@ int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, con
   const bool focal = scores_dst != nullptr;
   SplitParams sp = split_params(h, q, k, v, lens, out, false);
   sp.valu = (h->valu_full && !focal && !h->app_k) ? 1 : 0;
+  sp.stage_logits = (focal && h->focal_staged) ? 1 : 0;
   int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&](const LaunchTiming& lt) {
     return launch_split(c.dtype, c.head_dim, focal ? KIND_FOCAL : KIND_FULL, sp, h->stream, lt);
   });
@@ -590,6 +604,7 @@ int fastocr::create_handle(const fastocr_config* cfg, void* hip_stream, fastocr_
   h->keeps_all = plan.keeps_all;
   h->valu_full = plan.valu_full;
   h->skip_dead_picks = plan.skip_dead_picks;
+  h->focal_staged = plan.focal_staged;
   h->max_splits = plan.max_splits;
   if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
   const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
@@ -902,6 +917,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->sparse_rows_per_split = h->sparse_R;
   info->sparse_max_splits = h->sparse_splits;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
+  info->focal_staged = h->focal_staged ? 1 : 0;
   info->profiles = h->profiles;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;
@@ -920,6 +936,7 @@ int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info*
   info->sparse_rows_per_split = p.sparse_R;
   info->sparse_max_splits = p.sparse_splits;
   info->sparse_direct = p.sparse_splits <= 1 ? 1 : 0;
+  info->focal_staged = p.focal_staged ? 1 : 0;
   info->scratch_bytes = (int64_t)p.arena_bytes;
   return FASTOCR_OK;
 }

@@ -32,6 +32,12 @@ constexpr int kKeptBlocksPerCU = 3;
 // KV head) pair's 16-row tiles are dealt round-robin to P workgroups
 // (P <= kMaxKeptSplits), whose states the merge kernel combines.
 constexpr int kMaxKeptSplits = 32;
+// Focal passes stage a split's image-token logits in LDS (heads x
+// (rows_per_split + kLogitStagePad) floats) when they fit in this many floats
+// (66 KB, two workgroups per CU).
+constexpr int kLogitStagePad = 16;
+constexpr int kLogitStageFloats = 8 * (2048 + kLogitStagePad);
+constexpr int kLogitStageMinRows = 512;  // shorter splits store the logits as computed
 constexpr int kMergeThreads = 256;
 constexpr int kMaxMergeSplits = 1024;  // split weights one merge workgroup keeps in LDS
 constexpr int kMaxHeads = 128;
@@ -60,6 +66,9 @@ struct SplitParams {
   void* k_w;              // caches (k_w, v_w: the same buffers as k, v) by each pair's
   void* v_w;              // split 0
   float scale_log2;       // logit scale * log2(e)
+  int32_t stage_logits;   // focal kind: stage the logits in LDS (G * (rows_per_split +
+                          // kLogitStagePad) <= kLogitStageFloats) and write them after the
+                          // split's rows; 0: store them as they are computed
   int32_t valu;           // full kind, bf16, D = 128, Hq/Hkv <= kValuMaxGroup: the VALU
                           // variant (fp32 FMAs and 16-lane shuffle reductions instead of
                           // MFMA; a measurement override, same states)

@@ -98,13 +98,6 @@ __device__ __forceinline__ bool seq_extent(const int32_t* lens, int b, int S, in
   return n != n0 || len != l0;
 }
 
-// Rows attended by one sequence in a split pass, in "virtual row" order:
-// full kinds visit [0, len); the sparse kind visits the kept set first, then
-// the text rows [n, len).
-__device__ __forceinline__ int kept_rows(const int32_t* sel_cnt, int b, int n, int k_stride) {
-  return min(max(sel_cnt[b], 0), min(n, k_stride));
-}
-
 // This lane's slice of a K row (or of its query row): 16-byte pieces
 // i*4 + grp of the row, i = 0 .. KW/4 - 1.  The four lane groups of a column
 // therefore read 64 contiguous bytes per load instruction.
@@ -530,7 +523,12 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   constexpr int OST = D + 1;                    // padded LDS row of partial outputs
 
   __shared__ float s_stat[NW][16][4];
-  __shared__ float s_o[NW][HH][OST];
+  // the wave combine's partial outputs, and before them (focal kind) the
+  // split's staged image-token logits
+  constexpr int ON = NW * HH * OST;
+  constexpr int POOL = (KIND == KIND_FOCAL && kLogitStageFloats > ON) ? kLogitStageFloats : ON;
+  __shared__ __align__(16) float s_pool[POOL];
+  float (*s_o)[HH][OST] = reinterpret_cast<float (*)[HH][OST]>(s_pool);
   static_assert(KIND == KIND_FULL || KIND == KIND_FOCAL, "kept-token passes run kept_attn_kernel");
 
   // x = split, y = (sequence, KV head) pair, so workgroups dispatched
@@ -541,7 +539,7 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile rows stay scalar
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
@@ -629,6 +627,8 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   }
   const int end = min(begin + p.rows_per_split, rows);
 
+  const int lg_stride = p.rows_per_split + kLogitStagePad;  // staged logits per head (LDS)
+  const bool stage = KIND == KIND_FOCAL && p.stage_logits && G * lg_stride <= kLogitStageFloats;
   float m_run = -INFINITY, z = 0.f, lsum = 0.f, zt = 0.f;
   f32x4_t acc[NDB];
 #pragma unroll
@@ -678,12 +678,17 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
       }
       if constexpr (KIND == KIND_FOCAL) {
         // this lane's 4 logits are consecutive image rows of one head: one
-        // 16-byte store (rows are a multiple of 4, n_stride too)
+        // 16-byte store (rows are a multiple of 4, n_stride too), into LDS
+        // when staged (rows past the image rows are never written out)
         if (col < G) {
           float* lg = p.logits + ((size_t)b * p.Hq + kvh * G + col) * p.n_stride;
           const int r = tile + 4 * grp;
           const int lim = min(end, n);
-          if (r + 3 < lim) {
+          if (stage) {
+            if (r < lim)
+              *reinterpret_cast<float4*>(&s_pool[col * lg_stride + (r - begin)]) =
+                  make_float4(x[u][0], x[u][1], x[u][2], x[u][3]);
+          } else if (r + 3 < lim) {
             *reinterpret_cast<float4*>(lg + r) = make_float4(x[u][0], x[u][1], x[u][2], x[u][3]);
           } else {
 #pragma unroll
@@ -786,6 +791,28 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
       if (r0 + RPR >= end) break;
       if (r0 + 2 * RPR < end) load_round(r0 + 2 * RPR, kw, vw);
       round(r0 + RPR, kw2, vw2);
+    }
+  }
+
+  if constexpr (KIND == KIND_FOCAL) {
+    // staged logits: each head's image rows of the split leave as one
+    // contiguous run (stored while K/V streamed in, the 64-byte pieces of
+    // every head cost about twice as much)
+    if (stage) {
+      __syncthreads();
+      const int lim = min(end, n) - begin;
+      for (int h = 0; h < G; ++h) {
+        float* lg = p.logits + ((size_t)b * p.Hq + kvh * G + h) * p.n_stride + begin;
+        const float* sl = s_pool + h * lg_stride;
+        for (int i = 4 * tid; i < lim; i += 4 * NT) {
+          if (i + 3 < lim) {
+            *reinterpret_cast<float4*>(lg + i) = *reinterpret_cast<const float4*>(sl + i);
+          } else {
+            for (int t = i; t < lim; ++t) lg[t] = sl[t];
+          }
+        }
+      }
+      __syncthreads();  // s_o reuses the staging buffer
     }
   }
 
@@ -895,7 +922,7 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
   const int b = pair / p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile rows stay scalar
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int G = p.Hq / p.Hkv;
@@ -907,17 +934,19 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
   // first virtual row of this wave's tile in slot u of round j
   auto tile_row = [&](int j, int u) { return (split + P * (j * TPR + u * NW + wave)) * kTileRows; };
 
-  // loads that do not depend on the sequence extent: the first round's kept
-  // indices (jpre[u][0] for the K row of the lane's column, jpre[u][1 + j]
-  // for its V rows) and the query slice
-  int jpre[TPW][5];
+  // A lane holds the kept index of row `col` of each of its tiles; the index
+  // of V row 4*grp + jj is read from the lane of that column.  The first
+  // round's indices and the query slice do not depend on the sequence extent
+  // and load before it is read.
+  auto load_idx = [&](int j, int (&jk)[TPW]) {
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = tile_row(0, u);
-    jpre[u][0] = selb[min(tile + col, p.k_stride - 1)];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) jpre[u][1 + jj] = selb[min(tile + 4 * grp + jj, p.k_stride - 1)];
-  }
+    for (int u = 0; u < TPW; ++u) jk[u] = selb[min(tile_row(j, u) + col, p.k_stride - 1)];
+  };
+  int jk[TPW];
+  load_idx(0, jk);
+  // the kept count loads here too: the stores below may alias it, so a load
+  // written after them could not be issued before them
+  const int sel_cnt_b = p.sel_cnt[b];
   uint32_t qw[KW];
   if (col < G) {
     const T* qp = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.Hq + kvh * G + col) * D;
@@ -946,7 +975,7 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
     if (tid < C16) reinterpret_cast<uint4*>(kc)[tid] = reinterpret_cast<const uint4*>(knew)[tid];
     else if (tid < 2 * C16) reinterpret_cast<uint4*>(vc)[tid - C16] = reinterpret_cast<const uint4*>(vnew)[tid - C16];
   }
-  const int kept = kept_rows(p.sel_cnt, b, n, p.k_stride);
+  const int kept = min(max(sel_cnt_b, 0), min(n, p.k_stride));
   const int rows = kept + (len - n);
 
   // virtual row -> cache row, given the kept index j loaded for row r
@@ -954,7 +983,7 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
   bool bad_index = false;
   auto cache_row = [&](int r, int j) -> int {
     const bool img = r < kept;
-    bad_index |= img && r < rows && (j < 0 || j >= n);
+    bad_index |= img & ((unsigned)j >= (unsigned)n);
     const int jc = min(max(j, 0), max(n - 1, 0));
     return img ? jc : min(n + (r - kept), p.S - 1);
   };
@@ -1047,16 +1076,18 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
     }
   };
   // The K/V loads of a round (the K row of the lane's column and its four V
-  // rows, per tile); the kept index of row r is j_of(u, i, r), i = 0 for the
-  // K row, 1 + j for the V rows.
-  auto load_round = [&](const int (&tb)[TPW], uint32_t (&kw)[TPW][KW], uint32_t (&vw)[TPW][4][VW], auto&& j_of) {
+  // rows, per tile), given the kept indices jk of the round's tiles.
+  auto load_round = [&](const int (&tb)[TPW], const int (&jk)[TPW], uint32_t (&kw)[TPW][KW],
+                        uint32_t (&vw)[TPW][4][VW]) {
     int pk[TPW], pvr[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      pk[u] = cache_row(tb[u] + col, j_of(u, 0, tb[u] + col));
+      pk[u] = cache_row(tb[u] + col, jk[u]);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        pvr[u][jj] = cache_row(tb[u] + 4 * grp + jj, j_of(u, 1 + jj, tb[u] + 4 * grp + jj));
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jv = __builtin_amdgcn_ds_bpermute((grp << 4) + 4 * jj, jk[u]);
+        pvr[u][jj] = cache_row(tb[u] + 4 * grp + jj, jv);
+      }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -1068,14 +1099,16 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
       }
     }
   };
+  // Each round issues its K/V loads, then the next round's kept indices, so
+  // that the next round's K/V addresses are known when it starts.
   for (int j = 0; tile_row(j, 0) < rows; ++j) {
     int tb[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) tb[u] = tile_row(j, u);
     uint32_t kw[TPW][KW];
     uint32_t vw[TPW][4][VW];
-    if (j == 0) load_round(tb, kw, vw, [&](int u, int i, int) { return jpre[u][i]; });
-    else load_round(tb, kw, vw, [&](int, int, int r) { return selb[min(r, p.k_stride - 1)]; });
+    load_round(tb, jk, kw, vw);
+    load_idx(j + 1, jk);  // (clamped to the index array past the last round)
     round(tb, kw, vw);
   }
   if (bad_index) atomicOr(p.status, FASTOCR_FLAG_INDEX_CLAMPED);

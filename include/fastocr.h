@@ -47,6 +47,10 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
+ *   FASTOCR_FOCAL_STAGE=0|1 focal passes never stage a split's image-token
+ *                           logits in LDS (0: stored as they are computed), or
+ *                           stage them whenever they fit (1); default: stage
+ *                           them when they fit and a split has at least 512 rows
  *   FASTOCR_SKIP_DEAD_PICKS=0|1  a focal layer directly followed by another
  *                           focal layer skips its scores and top-k (default 1;
  *                           the outputs and the kept sets any layer uses are
@@ -136,6 +140,8 @@ typedef struct fastocr_info {
   int32_t sparse_max_splits;     /* kept-token pass: workgroups per (sequence, KV head) pair */
   int32_t sparse_direct;  /* 1: non-focal layers finish in one workgroup per (sequence, KV head)
                              pair (no merge launch) */
+  int32_t focal_staged;   /* 1: focal passes keep a split's image-token logits in LDS and write
+                             them once its rows are done (0: as they are computed) */
   int32_t profiles;       /* focal-set picks so far (first warm-up and re-selections) */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
@@ -296,8 +302,8 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info);
  * would choose for cfg on a device with num_cu compute units (the FASTOCR_*
  * environment overrides included), written to the plan fields of *info
  * (k_max, rows per split and splits of the full and kept-token passes,
- * sparse_direct / wave_states / pipe, scratch_bytes; the state fields are
- * those of a new handle).  Host only: no device is used.  Errors:
+ * sparse_direct, focal_staged, scratch_bytes; the state fields are those of
+ * a new handle).  Host only: no device is used.  Errors:
  * INVALID_ARG (null, a configuration fastocr_create rejects, num_cu < 1). */
 int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info* info);
 

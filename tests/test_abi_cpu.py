@@ -254,6 +254,41 @@ def test_plan_of_benchmark_workloads():
     assert t2["k_max"] == 2560 and t2["sparse_max_splits"] == 12
     for info in (b1, w8, b4, t2):
         _check_plan(info, info["full_max_splits"] * info["full_rows_per_split"])
+    # focal passes stage their logits at 1920- and 1408-row splits, not at
+    # B=1's 128-row splits
+    assert (b1["focal_staged"], w8["focal_staged"], b4["focal_staged"], t2["focal_staged"]) == (0, 1, 1, 1)
+
+
+LOGIT_STAGE_FLOATS = 8 * (2048 + 16)  # LDS floats a focal pass stages a split's logits in
+LOGIT_STAGE_MIN_ROWS = 512               # rows per split from which it stages them by default
+
+
+@pytest.mark.parametrize("env", [None, "0", "1"])
+def test_plan_focal_logit_staging(monkeypatch, env):
+    # a focal pass stages its split's image-token logits in LDS only when the
+    # group's heads x (rows per split + 16 padding) fit; by default only for
+    # splits of at least 512 rows; FASTOCR_FOCAL_STAGE=0 never, =1 whenever
+    # they fit
+    if env is None:
+        monkeypatch.delenv("FASTOCR_FOCAL_STAGE", raising=False)
+    else:
+        monkeypatch.setenv("FASTOCR_FOCAL_STAGE", env)
+    rng = np.random.default_rng(12)
+    seen = set()
+    for _ in range(300):
+        hkv = int(rng.integers(1, 9))
+        g = int(rng.integers(1, 17))
+        S = int(rng.integers(1, 200_000))
+        info = _plan(num_cu=int(rng.choice([80, 256])), num_layers=2, num_q_heads=hkv * min(g, 128 // hkv),
+                     num_kv_heads=hkv, head_dim=128, batch=int(rng.integers(1, 65)), max_seq_len=S,
+                     max_img_tokens=int(rng.integers(0, S + 1)), tau=0.05, num_focal=1, warmup_steps=1,
+                     dtype="bf16")
+        R = info["full_rows_per_split"]
+        fits = min(g, 128 // hkv) * (R + 16) <= LOGIT_STAGE_FLOATS
+        want = fits and {None: R >= LOGIT_STAGE_MIN_ROWS, "0": False, "1": True}[env]
+        assert info["focal_staged"] == int(want), info
+        seen.add(want)
+    assert seen == ({False} if env == "0" else {True, False})
 
 
 def test_set_focal_layers_null_handle():
