@@ -17,8 +17,10 @@ enum SplitKind : int {
 };
 
 // Split kernel geometry: a wave consumes 16-row MFMA tiles and loads
-// kTilesPerWave of them before computing any; a workgroup is kSplitWaves
-// waves, so one round of a workgroup covers kRowsPerRound cache rows.
+// kTilesPerWave of them (one for fp32 rows of 128 elements) before computing
+// any; a workgroup is kSplitWaves waves, so one round of a workgroup covers
+// kRowsPerRound cache rows (half that for fp32 rows of 128; full-pass splits
+// are whole multiples of kRowsPerRound either way).
 constexpr int kTileRows = 16;
 constexpr int kSplitWaves = 4;
 constexpr int kTilesPerWave = 2;

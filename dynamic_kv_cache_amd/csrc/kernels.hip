@@ -1713,19 +1713,23 @@ static hipError_t launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s
   return hipGetLastError();
 }
 
+// Tiles a wave loads per round: fp32 rows of 128 elements take twice the
+// registers of bf16 ones, and two tiles of them per wave would spill.
+template <typename T, int D>
+constexpr int tiles_per_wave() { return (sizeof(T) == 4 && D == 128) ? 1 : kTilesPerWave; }
+
 template <typename T, int D>
 static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream_t stream,
                                  const LaunchTiming& timing) {
   const dim3 block(kSplitThreads), grid(p.grid_splits, p.Hkv * p.B);
+  constexpr int TPW = tiles_per_wave<T, D>();
   switch (kind) {
     case KIND_FULL:
       if constexpr (sizeof(T) == 2 && D == 128)
         if (p.valu) return launch(split_valu_kernel<kValuMaxGroup>, grid, block, stream, timing, p);
-      return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, kTilesPerWave>, grid, block, stream,
-                    timing, p);
+      return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, TPW>, grid, block, stream, timing, p);
     case KIND_FOCAL:
-      return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, kTilesPerWave>, grid, block, stream,
-                    timing, p);
+      return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, TPW>, grid, block, stream, timing, p);
     default:
       return hipErrorInvalidValue;
   }
@@ -1734,7 +1738,7 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
 template <typename T, int D>
 static hipError_t launch_kept_t(const SplitParams& p, hipStream_t stream, const LaunchTiming& timing) {
   const dim3 block(kSplitThreads), grid(p.Hkv * p.B, p.grid_splits);
-  return launch(kept_attn_kernel<T, D, kSplitWaves, kTilesPerWave>, grid, block, stream, timing, p);
+  return launch(kept_attn_kernel<T, D, kSplitWaves, tiles_per_wave<T, D>()>, grid, block, stream, timing, p);
 }
 
 hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_t stream,
