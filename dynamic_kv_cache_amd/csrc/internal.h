@@ -9,11 +9,11 @@
 
 namespace fastocr {
 
-// Kinds of split-K attention pass.
+// Kinds of full-row split-K attention pass (kept-token passes run
+// kept_attn_kernel).
 enum SplitKind : int {
   KIND_FULL = 0,    // all rows [0, len_b)
   KIND_FOCAL = 1,   // all rows, and export the image-token logits
-  KIND_SPARSE = 2,  // kept image rows (gathered by index) + rows [n_img_b, len_b)
 };
 
 // Split kernel geometry: a wave consumes 16-row MFMA tiles and loads

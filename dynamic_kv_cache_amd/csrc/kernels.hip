@@ -7,20 +7,26 @@
 //
 // Kernels
 //   split_attn_kernel  split-K decode attention of one (sequence, KV head)
-//                      over one chunk of rows per workgroup.  Three kinds:
-//                      full rows, full rows + image-logit export (focal
-//                      layers), and kept image rows gathered by index + every
-//                      text row (non-focal layers).  Writes one partial
-//                      softmax state per split, or the output itself when a
-//                      sequence's rows fit one split.
+//                      over one chunk of consecutive rows per workgroup, in
+//                      two kinds: all rows (warm-up, FULL mode, tau = 1), and
+//                      all rows + the image-token logit export (focal
+//                      layers; staged in LDS for long splits).  Writes one
+//                      partial softmax state per split.
+//   kept_attn_kernel   attention of one (sequence, KV head) over its kept
+//                      image rows, gathered by index, and every text row
+//                      (non-focal layers): the pair's 16-row tiles dealt
+//                      round-robin to its workgroups.  Writes one state per
+//                      workgroup, or the output when a pair has one.
 //   merge_kernel       one workgroup per head merges the split states into
 //                      the output (and the head's text-probability mass);
 //                      for focal layers, score workgroups compute the
 //                      head-summed probability of every image token.
 //   topk_kernel        the k_b highest scores per sequence, ties to the lower
 //                      index, ascending output.
+//   pack_rows_kernel   one-time image-first gather of a multi-span cache.
 // Workgroups never wait on each other inside a kernel: on this GPU a device
-// fence plus an arrival atomic costs more than the next kernel launch.
+// fence plus an arrival atomic, or the same chain kept inside one XCD's L2,
+// costs as much as the next kernel launch or more.
 //
 // Matrix layout on the MFMA units.  A wave consumes 16 cache rows per tile.
 // The GQA query group of one KV head (up to 16 heads, zero padded) is the N
@@ -1547,8 +1553,9 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
 // kMergeThreads image tokens each.  Each score workgroup derives every
 // head's softmax max and sum from the split states itself (16 lanes per
 // head), so it does not depend on the merge workgroups.  The token's logits
-// of up to kScoreRegHeads heads are loaded before anything else.
-constexpr int kScoreRegHeads = 32;
+// of up to kScoreRegHeads heads are loaded before anything else, those of
+// further heads 16 at a time.
+constexpr int kScoreRegHeads = 64;
 constexpr int kScorePrefetchPasses = 4;  // heads whose split states load up front: 4 x 16
 
 __device__ void score_block(const MergeParams& p, int b, int sb) {
@@ -1628,8 +1635,14 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
   if (j < p.n_stride) {
 #pragma unroll
     for (int h = 0; h < kScoreRegHeads; ++h) s += __builtin_amdgcn_exp2f(x[h] - s_mz[h].x) * s_mz[h].y;
-    for (int h = kScoreRegHeads; h < p.Hq; ++h)
-      s += __builtin_amdgcn_exp2f(lg[(size_t)h * p.n_stride] - s_mz[h].x) * s_mz[h].y;
+    for (int h0 = kScoreRegHeads; h0 < p.Hq; h0 += 16) {
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = h0 + i < p.Hq ? lg[(size_t)(h0 + i) * p.n_stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (h0 + i < p.Hq) s += __builtin_amdgcn_exp2f(y[i] - s_mz[h0 + i].x) * s_mz[h0 + i].y;
+    }
     p.scores[(size_t)b * p.n_stride + j] = s;
   }
   if (p.hist0) {
