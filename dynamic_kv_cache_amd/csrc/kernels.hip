@@ -896,15 +896,18 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
 // So at any step every workgroup of a pair has the same number of rows, to
 // within one tile, and a tile's rows do not depend on the pair's row count:
 // the kept indices of the first round load before the sequence extent is
-// read.  (Staging the workgroup's indices in LDS behind a barrier measured
-// ~1 us slower per launch: every wave then waits for all of them; loading a
-// round's indices during the previous round needs registers the kernel does
-// not have at 3 workgroups per CU, and the spills cost more than it saves.)
-// Each workgroup combines its waves' softmax states in LDS.  With one
-// workgroup per pair it writes the output; otherwise it writes its state for
-// the merge kernel.  (A variant in which the pair's last workgroup merged the
-// states itself, behind an arrival counter, measured no faster than the
-// merge launch with device-coherent state stores and 3-4x slower with
+// read, and each round loads the next round's with its K/V rows.  (Staging
+// the workgroup's indices in LDS behind a barrier measured ~1 us slower per
+// launch: every wave then waits for all of them; five indices per tile in
+// registers spill at 3 workgroups per CU; one index per tile plus lane
+// permutes fits.  Two more tiles per wave loaded straight to LDS, at 2
+// workgroups per CU, measured slower at every size.)  Each workgroup
+// combines its waves' softmax states in LDS.  With one workgroup per pair it
+// writes the output; otherwise it writes its state for the merge kernel.  (A
+// variant in which the pair's last workgroup merged the states itself,
+// behind an arrival counter, measured no faster than the merge launch with
+// device-coherent state stores, as slow or slower with the workgroups of a
+// pair kept on one XCD and the exchange in its L2, and 3-4x slower with
 // device-scope release/acquire fences, whose L2 write-back dominates.)
 template <typename T, int D, int NW, int TPW>
 __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(SplitParams p) {
