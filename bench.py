@@ -115,7 +115,7 @@ def kernel_class(name):
         return "full_split"  # the VALU variant of the full pass
     if "fastocr::kept_attn_kernel<" in head:
         return "sparse_split"
-    if "fastocr::merge_kernel<" in head:
+    if "fastocr::merge_kernel<" in head or "fastocr::kept_merge_kernel<" in head:
         return "merge"
     if "fastocr::topk_kernel" in head:
         return "topk"

@@ -401,7 +401,7 @@ int run_sparse(fastocr_handle* h, const void* q, const void* k, const void* v, c
   if (rc || h->sparse_splits <= 1) return rc;
   MergeParams mp = merge_params(h, lens, out, true);
   return timed(h, FASTOCR_KC_MERGE,
-               [&](const LaunchTiming& lt) { return launch_merge(c.dtype, c.head_dim, mp, h->stream, lt); });
+               [&](const LaunchTiming& lt) { return launch_kept_merge(c.dtype, c.head_dim, mp, h->stream, lt); });
 }
 
 void select_focal(const double* ratios, int L, int num_focal, int32_t* out) {

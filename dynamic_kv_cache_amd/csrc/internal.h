@@ -135,6 +135,9 @@ hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_
                        const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
                         const LaunchTiming& timing = LaunchTiming{});
+// Merge of a kept-token pass (grid_splits <= 64, no scores, no text mass).
+hipError_t launch_kept_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
+                             const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream,
                        const LaunchTiming& timing = LaunchTiming{});
 hipError_t launch_pack(const PackParams& p, hipStream_t stream);
