@@ -919,10 +919,10 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
   constexpr int NDB = D / 16;                   // PV d-blocks = V elements per row per lane
   constexpr int VW = NDB * (int)sizeof(T) / 4;  // V words per row per lane
   constexpr int HH = 8;                         // heads per LDS combine round
-  constexpr int OST = D + 1;                    // padded LDS row of partial outputs
+  constexpr int OST = D + 4;                    // padded LDS row of partial outputs (16-byte aligned)
 
   __shared__ float s_stat[NW][16][4];
-  __shared__ float s_o[NW][HH][OST];
+  __shared__ __align__(16) float s_o[NW][HH][OST];
 
   const int pair = blockIdx.x;
   const int split = blockIdx.y;
@@ -1149,23 +1149,47 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
         for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i];
     }
     __syncthreads();
+    // thread t reduces the 4 consecutive outputs (h, 4*c4 .. 4*c4 + 3) of
+    // float4 column c4 = t % (D/4) of head h = t / (D/4) (+ NT/(D/4) per
+    // further pass): one weight per wave and head, one 16-byte LDS read per
+    // wave, one 16-byte store
     const int hn = min(HH, G - h0);
-    for (int idx = tid; idx < hn * D; idx += NT) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[w][h0 + h][0]);
-      float o = 0.f, L = 0.f;
+    constexpr int C4 = D / 4;
+    for (int idx = tid; idx < hn * C4; idx += NT) {
+      const int h = idx / C4;
+      const int c4 = idx - h * C4;
+      float mv[NW], lv[NW];
+      float4 ov[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = s_stat[w][h0 + h][0];
-        const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        o += s_o[w][h][d] * e;
-        L += s_stat[w][h0 + h][2] * e;
+        mv[w] = s_stat[w][h0 + h][0];
+        lv[w] = s_stat[w][h0 + h][2];
+        ov[w] = *reinterpret_cast<const float4*>(&s_o[w][h][4 * c4]);
       }
-      if (direct) store_out<T>(out + (size_t)(h0 + h) * D + d, M == -INFINITY ? 0.f : o / L);
-      else p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mv[w]);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float e = mv[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[w] - M);
+        o.x += ov[w].x * e;
+        o.y += ov[w].y * e;
+        o.z += ov[w].z * e;
+        o.w += ov[w].w * e;
+        L += lv[w] * e;
+      }
+      if (direct) {
+        T* od = out + (size_t)(h0 + h) * D + 4 * c4;
+        const bool none = M == -INFINITY;
+        store_out<T>(od + 0, none ? 0.f : o.x / L);
+        store_out<T>(od + 1, none ? 0.f : o.y / L);
+        store_out<T>(od + 2, none ? 0.f : o.z / L);
+        store_out<T>(od + 3, none ? 0.f : o.w / L);
+      } else {
+        *reinterpret_cast<float4*>(p.po + (slot0 + (size_t)(h0 + h) * p.max_splits) * D + 4 * c4) = o;
+      }
     }
   }
   if (direct) return;
