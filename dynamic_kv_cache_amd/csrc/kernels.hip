@@ -526,7 +526,7 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   constexpr int NDB = D / 16;                   // PV d-blocks = V elements per row per lane
   constexpr int VW = NDB * (int)sizeof(T) / 4;  // V words per row per lane
   constexpr int HH = 8;                         // heads per LDS merge round
-  constexpr int OST = D + 1;                    // padded LDS row of partial outputs
+  constexpr int OST = D + 4;                    // padded LDS row of partial outputs (16-byte aligned)
 
   __shared__ float s_stat[NW][16][4];
   // the wave combine's partial outputs, and before them (focal kind) the
@@ -850,21 +850,32 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
         for (int i = 0; i < 4; ++i) s_o[wave][col - h0][(4 * grp + i) * NDB + db] = acc[db][i];
     }
     __syncthreads();
+    // thread t reduces the 4 consecutive outputs of float4 column t % (D/4)
+    // of head t / (D/4) (+ NT/(D/4) heads per further pass)
     const int hn = min(HH, G - h0);
-    for (int idx = tid; idx < hn * D; idx += NT) {
-      const int h = idx / D;
-      const int d = idx - h * D;
+    constexpr int C4 = D / 4;
+    for (int idx = tid; idx < hn * C4; idx += NT) {
+      const int h = idx / C4;
+      const int c4 = idx - h * C4;
       float mw[NW];
+      float4 ov[NW];
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         mw[w] = s_stat[w][h0 + h][0];
+        ov[w] = *reinterpret_cast<const float4*>(&s_o[w][h][4 * c4]);
         M = fmaxf(M, mw[w]);
       }
-      float o = 0.f;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) o += s_o[w][h][d] * __builtin_amdgcn_exp2f(mw[w] - M);
-      p.po[(slot0 + (size_t)(h0 + h) * p.max_splits) * D + d] = o;
+      for (int w = 0; w < NW; ++w) {
+        const float e = __builtin_amdgcn_exp2f(mw[w] - M);
+        o.x += ov[w].x * e;
+        o.y += ov[w].y * e;
+        o.z += ov[w].z * e;
+        o.w += ov[w].w * e;
+      }
+      *reinterpret_cast<float4*>(p.po + (slot0 + (size_t)(h0 + h) * p.max_splits) * D + 4 * c4) = o;
     }
   }
   if (tid < G) {
