@@ -1711,33 +1711,42 @@ __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p
   const int P = p.grid_splits;
   const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
   // lane s holds state s; thread (d4, sl) the partial outputs of states
-  // sl, sl + SL, ... in column d4
-  const float4 q = lane < P ? p.pstat[slot0 + lane] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+  // sl, sl + SL, ... in column d4.  Every load is issued unconditionally from
+  // an index clamped to the last state (dropped below), so that all of them
+  // are in flight together: a load under a lane condition made the compiler
+  // wait for it before issuing the next ones.
+  // (No early exit either: the compiler would move the loads below it.)
+  const float4 qr = p.pstat[slot0 + min(lane, P - 1)];
   const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
   float4 pv[PF];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int s = sl + i * SL;
-    pv[i] = s < P ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int i = 0; i < PF; ++i) pv[i] = po[(size_t)min(sl + i * SL, P - 1) * D4];
+  __builtin_amdgcn_sched_barrier(0);  // all loads issue before the first use of any
   T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
-  const float M = wave_max(q.x);
-  if (M == -INFINITY) {  // no rows at all: zero output
-    for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
-    return;
-  }
-  const float w = q.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(q.x - M);
-  const float L = wave_sum(q.z * w);
+  const bool mine = lane < P;
+  const float M = wave_max(mine ? qr.x : -INFINITY);
+  const bool none = M == -INFINITY;  // no rows at all: zero output
+  // lanes past P and states without rows get weight 0 (and add 0 to L: a
+  // state's sums are finite)
+  const float w = (mine && qr.x != -INFINITY) ? __builtin_amdgcn_exp2f(qr.x - M) : 0.f;
+  const float L = wave_sum(qr.z * w);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  {
+    // products and sums rounded separately, as in the general merge; a state
+    // not used (past P or of weight 0) is multiplied by 0 and adds exactly 0
+    // (its partial outputs are finite), so every loaded value is used and no
+    // load is moved under a condition
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int s = sl + i * SL;
-    const float ws = __shfl(w, s);
-    const bool use = s < P && ws != 0.f;  // a state of weight 0 adds exactly 0
-    a0 += use ? pv[i].x * ws : 0.f;
-    a1 += use ? pv[i].y * ws : 0.f;
-    a2 += use ? pv[i].z * ws : 0.f;
-    a3 += use ? pv[i].w * ws : 0.f;
+    for (int i = 0; i < PF; ++i) {
+      const int s = sl + i * SL;
+      const float ws = __shfl(w, s);
+      const float wu = (s < P && ws != 0.f) ? ws : 0.f;
+      a0 += pv[i].x * wu;
+      a1 += pv[i].y * wu;
+      a2 += pv[i].z * wu;
+      a3 += pv[i].w * wu;
+    }
   }
   a0 = group_sum<SL>(a0);
   a1 = group_sum<SL>(a1);
@@ -1745,10 +1754,10 @@ __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p
   a3 = group_sum<SL>(a3);
   if (sl == 0) {
     const float inv = 1.f / L;
-    store_out<T>(out + 4 * d4 + 0, a0 * inv);
-    store_out<T>(out + 4 * d4 + 1, a1 * inv);
-    store_out<T>(out + 4 * d4 + 2, a2 * inv);
-    store_out<T>(out + 4 * d4 + 3, a3 * inv);
+    store_out<T>(out + 4 * d4 + 0, none ? 0.f : a0 * inv);
+    store_out<T>(out + 4 * d4 + 1, none ? 0.f : a1 * inv);
+    store_out<T>(out + 4 * d4 + 2, none ? 0.f : a2 * inv);
+    store_out<T>(out + 4 * d4 + 3, none ? 0.f : a3 * inv);
   }
 }
 
@@ -1872,7 +1881,8 @@ hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitPara
 
 hipError_t launch_kept_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
                              const LaunchTiming& timing) {
-  if (p.grid_splits > 64 || p.score_blocks != 0 || p.text_mass != nullptr) return hipErrorInvalidValue;
+  if (p.grid_splits < 1 || p.grid_splits > 64 || p.score_blocks != 0 || p.text_mass != nullptr)
+    return hipErrorInvalidValue;
   const dim3 grid(p.Hq, p.B), block(kMergeThreads);
   if (dtype == FASTOCR_DTYPE_BF16)
     return head_dim == 128 ? launch(kept_merge_kernel<uint16_t, 128>, grid, block, stream, timing, p)
