@@ -1426,6 +1426,77 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
+// merge_head for up to 64 splits: every wave derives the head's softmax
+// totals itself (lane s holds split s's state) and weights its partial
+// outputs from their own maxima, so no workgroup barrier.  A thread uses
+// NV = ceil(splits / SL) slots (the same count for the whole launch); the
+// body is instantiated per count, so each thread issues exactly the loads
+// it uses, all at once from indices clamped to the last split, with no
+// branch between the loads and their use (a lane-conditional load, or an
+// early exit, made the compiler wait for one load before issuing the next).
+template <typename T, int D, int NV>
+__device__ __forceinline__ void merge_head_small(const MergeParams& p, int b, int h) {
+  constexpr int D4 = D / 4;
+  constexpr int SL = kMergeThreads / D4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
+  const int d4 = tid / SL, sl = tid % SL;
+  const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
+  const int nsplit = p.grid_splits;
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  const int last = nsplit - 1;
+  const float4 qr = p.pstat[slot0 + min(lane, last)];
+  float4 pv[NV];
+  float mxr[NV];  // maxima of the splits this thread accumulates
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int s = min(sl + i * SL, last);
+    pv[i] = po[(size_t)s * D4];
+    mxr[i] = p.pstat[slot0 + s].x;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issue before the first use of any
+  const bool mine = lane < nsplit;
+  const float M = wave_max(mine ? qr.x : -INFINITY);
+  const bool none = M == -INFINITY;  // no rows at all: zero output and no image mass
+  // lanes past the last split and empty splits get weight 0; a state's sums
+  // are finite (an empty split's are 0), so they add exactly 0
+  const float w = (mine && qr.x != -INFINITY) ? __builtin_amdgcn_exp2f(qr.x - M) : 0.f;
+  const float Z = wave_sum(qr.y * w);
+  const float L = wave_sum(qr.z * w);
+  const float Zt = wave_sum(qr.w * w);
+  // branch-free sums: a split of weight 0 adds exactly 0 whatever its
+  // partial output holds (an empty split's is not written this launch)
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float wsv = (sl + i * SL < nsplit && mxr[i] != -INFINITY) ? __builtin_amdgcn_exp2f(mxr[i] - M) : 0.f;
+    const bool use = wsv != 0.f;
+    a0 += use ? pv[i].x * wsv : 0.f;
+    a1 += use ? pv[i].y * wsv : 0.f;
+    a2 += use ? pv[i].z * wsv : 0.f;
+    a3 += use ? pv[i].w * wsv : 0.f;
+  }
+  a0 = group_sum<SL>(a0);
+  a1 = group_sum<SL>(a1);
+  a2 = group_sum<SL>(a2);
+  a3 = group_sum<SL>(a3);
+  if (sl == 0) {
+    const float inv = 1.f / L;
+    store_out<T>(out + 4 * d4 + 0, none ? 0.f : a0 * inv);
+    store_out<T>(out + 4 * d4 + 1, none ? 0.f : a1 * inv);
+    store_out<T>(out + 4 * d4 + 2, none ? 0.f : a2 * inv);
+    store_out<T>(out + 4 * d4 + 3, none ? 0.f : a3 * inv);
+  }
+  if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = none ? 1.f : Zt / Z;  // image mass = 1 - this
+}
+
+template <typename T, int D, int NV>
+__device__ __forceinline__ void merge_head_small_dispatch(const MergeParams& p, int b, int h, int nv) {
+  if constexpr (NV > 1)
+    if (nv < NV) return merge_head_small_dispatch<T, D, NV - 1>(p, b, h, nv);
+  merge_head_small<T, D, NV>(p, b, h);
+}
+
 // Workgroups [0, Hq): merge head h's split states into its output.  Thread
 // t covers float4 column t / SL of the output and splits s = t % SL (mod SL).
 // Every launched split has written a state this launch (an empty split one
@@ -1443,68 +1514,23 @@ __device__ void merge_head(const MergeParams& p, int b, int h) {
   const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
   const int d4 = tid / SL, sl = tid % SL;
   const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
+  const int nsplit = p.grid_splits;
+  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  if (nsplit <= 64) {
+    merge_head_small_dispatch<T, D, 64 / SL>(p, b, h, (nsplit + SL - 1) / SL);
+    return;
+  }
   float4 st[NST];
 #pragma unroll
   for (int i = 0; i < NST; ++i) {
     const int s = tid + i * kMergeThreads;
-    st[i] = s < p.grid_splits ? p.pstat[slot0 + s] : make_float4(0.f, 0.f, 0.f, 0.f);
+    st[i] = s < nsplit ? p.pstat[slot0 + s] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 pv[PF];
-  float mxs[PF];  // maxima of the splits this thread accumulates
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int s = sl + i * SL;
-    pv[i] = s < p.grid_splits ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    mxs[i] = s < p.grid_splits ? p.pstat[slot0 + s].x : -INFINITY;
-  }
-  // up to 64 splits: lane s of every wave holds split s's state
-  const float4 q = (p.grid_splits <= 64 && lane < p.grid_splits) ? p.pstat[slot0 + lane]
-                                                                   : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-
-  const int nsplit = p.grid_splits;
-  T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
-  if (nsplit <= 64) {
-    // Up to 64 splits: every wave derives the head's softmax totals itself
-    // and takes the weights of its partial outputs by lane permutes: no
-    // workgroup barrier.
-    const float M = wave_max(q.x);
-    if (M == -INFINITY) {  // no rows at all: zero output and no image mass
-      for (int d = tid; d < D; d += kMergeThreads) store_out<T>(out + d, 0.f);
-      if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = 1.f;  // image mass = 1 - this
-      return;
-    }
-    const float w = q.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(q.x - M);
-    const float Z = wave_sum(q.y * w);
-    const float L = wave_sum(q.z * w);
-    const float Zt = wave_sum(q.w * w);
-    // the weights of this thread's splits, from their own maxima (no lane
-    // exchange), then branch-free sums: a state of weight 0 adds exactly 0
-    // whatever its partial output holds
-    float wsv[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) wsv[i] = mxs[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mxs[i] - M);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const bool use = sl + i * SL < nsplit && wsv[i] != 0.f;
-      a0 += use ? pv[i].x * wsv[i] : 0.f;
-      a1 += use ? pv[i].y * wsv[i] : 0.f;
-      a2 += use ? pv[i].z * wsv[i] : 0.f;
-      a3 += use ? pv[i].w * wsv[i] : 0.f;
-    }
-    a0 = group_sum<SL>(a0);
-    a1 = group_sum<SL>(a1);
-    a2 = group_sum<SL>(a2);
-    a3 = group_sum<SL>(a3);
-    if (sl == 0) {
-      const float inv = 1.f / L;
-      store_out<T>(out + 4 * d4 + 0, a0 * inv);
-      store_out<T>(out + 4 * d4 + 1, a1 * inv);
-      store_out<T>(out + 4 * d4 + 2, a2 * inv);
-      store_out<T>(out + 4 * d4 + 3, a3 * inv);
-    }
-    if (tid == 0 && p.text_mass) p.text_mass[b * p.Hq + h] = Zt / Z;
-    return;
+    pv[i] = s < nsplit ? po[(size_t)s * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float m = -INFINITY;
 #pragma unroll
@@ -1700,11 +1726,14 @@ __device__ void score_block(const MergeParams& p, int b, int sb) {
 // 72B-like B=8 graph, 2.9 against 3.3 at 7B-like B=1 (measured after a
 // kernel writing the states, in isolation).
 static_assert(kMaxKeptSplits <= 64, "a kept-token pass's states fit one wave's lanes");
-template <typename T, int D>
-__global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p) {
+// A thread uses NV = ceil(P / SL) state slots (the same count for the whole
+// launch): the body is instantiated per count, so each thread issues exactly
+// the loads it uses, all before the first use of any, and the compiler waits
+// for them one by one.
+template <typename T, int D, int NV>
+__device__ __forceinline__ void kept_merge_body(const MergeParams& p) {
   constexpr int D4 = D / 4;
   constexpr int SL = kMergeThreads / D4;  // lanes sharing an output column
-  constexpr int PF = 64 / SL;             // states per lane
   const int b = blockIdx.y, h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int d4 = tid / SL, sl = tid % SL;
@@ -1712,15 +1741,14 @@ __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p
   const size_t slot0 = ((size_t)b * p.Hq + h) * p.max_splits;
   // lane s holds state s; thread (d4, sl) the partial outputs of states
   // sl, sl + SL, ... in column d4.  Every load is issued unconditionally from
-  // an index clamped to the last state (dropped below), so that all of them
-  // are in flight together: a load under a lane condition made the compiler
-  // wait for it before issuing the next ones.
-  // (No early exit either: the compiler would move the loads below it.)
+  // an index clamped to the last state (dropped below): a load under a lane
+  // condition, or before an early exit, made the compiler wait for it before
+  // issuing the next ones.
   const float4 qr = p.pstat[slot0 + min(lane, P - 1)];
   const float4* po = reinterpret_cast<const float4*>(p.po + slot0 * D) + d4;
-  float4 pv[PF];
+  float4 pv[NV];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) pv[i] = po[(size_t)min(sl + i * SL, P - 1) * D4];
+  for (int i = 0; i < NV; ++i) pv[i] = po[(size_t)min(sl + i * SL, P - 1) * D4];
   __builtin_amdgcn_sched_barrier(0);  // all loads issue before the first use of any
   T* out = reinterpret_cast<T*>(p.out) + ((size_t)b * p.Hq + h) * D;
   const bool mine = lane < P;
@@ -1738,7 +1766,7 @@ __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p
     // load is moved under a condition
 #pragma clang fp contract(off)
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int s = sl + i * SL;
       const float ws = __shfl(w, s);
       const float wu = (s < P && ws != 0.f) ? ws : 0.f;
@@ -1759,6 +1787,20 @@ __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p
     store_out<T>(out + 4 * d4 + 2, none ? 0.f : a2 * inv);
     store_out<T>(out + 4 * d4 + 3, none ? 0.f : a3 * inv);
   }
+}
+
+template <typename T, int D, int NV>
+__device__ __forceinline__ void kept_merge_dispatch(const MergeParams& p, int nv) {
+  if constexpr (NV > 1)
+    if (nv < NV) return kept_merge_dispatch<T, D, NV - 1>(p, nv);
+  kept_merge_body<T, D, NV>(p);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p) {
+  constexpr int SL = kMergeThreads / (D / 4);
+  constexpr int PF = 64 / SL;  // slots per thread for 64 states
+  kept_merge_dispatch<T, D, PF>(p, (p.grid_splits + SL - 1) / SL);
 }
 
 template <typename T, int D>
