@@ -574,18 +574,19 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   // Splits below sure_splits hold rows for every sequence the handle
   // accepts: they load ahead.  The others may be empty and learn that
   // from the extent before loading anything.
+  // The first round's tiles all lie in the split's rows (a split is at least
+  // one round), so they load without a condition (rows clamped to the cache;
+  // a tile past its end is never weighted): a per-tile condition made the
+  // compiler wait for one tile's K before issuing the next tile's loads.
   const bool ahead = split < p.sure_splits;
   if (ahead) {
-    const int spec_end = min(begin + p.rows_per_split, p.S);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = r_first + u * NW * kTileRows;
-      if (tile < spec_end) {  // uniform over the wave
-        load_slice<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
+      load_slice<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          load_words(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
-      }
+      for (int j = 0; j < 4; ++j)
+        load_words(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
     }
   }
 
