@@ -129,6 +129,13 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
     info = fo.fastocr_get_info(h)
     for key, value in KEPT_VARIANTS[rows][1].items():
         assert info[key] == value, (rows, key, info)
+    _check_injected_sets(up, h)
+
+
+def _check_injected_sets(up, h):
+    # one warm-up step, then layer 2 made the focal layer and two kept sets
+    # injected in turn (a full one and one of 17 tokens): layers 0 and 1
+    # attend with them, checked against the oracle's kept-token attention
     wl = up.wl
     for l in range(wl.num_layers):  # one warm-up step
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=up.io_dtype, device=DEV)
@@ -155,8 +162,67 @@ def test_sparse_conditioned_on_injected_sets(monkeypatch, rows, tau):
             K, V = up.kv64(l)
             want = sparse_attention(up.q[l][t][0].astype(np.float64), K[0], V[0], chosen, n, length,
                                     scale)
-            check_out(outs[l].float().cpu().numpy()[0], want, "bf16", f"sparse t={t} l={l}")
+            check_out(outs[l].float().cpu().numpy()[0], want, wl.dtype, f"sparse t={t} l={l}")
     assert fo.fastocr_get_status(h) == 0
+
+
+# The merges are instantiated per count of state slots a thread uses,
+# ceil(states / lanes per output column) (8 lanes at head_dim 128, 16 at
+# 64), and the general merge has its own path past 64 states: every count
+# is forced through a rows-per-split override, found from the host-side
+# launch plan for this device, and checked against the oracle.
+
+
+def _rows_for_slots(monkeypatch, cfg, env, key, lanes, nv, step):
+    # the largest override (a multiple of `step` rows) whose plan gives nv
+    # slots per thread (nv = 0: more than 64 states), with more than one state
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for rows in range(8192, 0, -step):
+        monkeypatch.setenv(env, str(rows))
+        n = fo.fastocr_plan_launch(cfg, ncu)[key]
+        if n > 1 and (0 if n > 64 else -(-n // lanes)) == nv:
+            return rows, n
+    pytest.fail(f"no {env} gives {nv} slots")
+
+
+GENERAL_MERGE_CASES = [(128, nv) for nv in range(9)] + [(64, nv) for nv in range(5)]
+
+
+@pytest.mark.parametrize("d,nv", GENERAL_MERGE_CASES,
+                         ids=[f"d{d}-slots{nv if nv else 'over64'}" for d, nv in GENERAL_MERGE_CASES])
+def test_general_merge_slot_counts(monkeypatch, d, nv):
+    up = upload(get_workload("7b-b1").with_overrides(num_layers=2, head_dim=d), steps=2)
+    cfg = make_config(up, mode="full")
+    rows, splits = _rows_for_slots(monkeypatch, cfg, "FASTOCR_FULL_ROWS", "full_max_splits",
+                                   8 if d == 128 else 16, nv, 16)
+    h = fo.fastocr_create(cfg)
+    assert fo.fastocr_get_info(h)["full_max_splits"] == splits
+    rec = run(up, h, 2)
+    assert rec.status == 0
+    scale = 1 / math.sqrt(d)
+    for t in range(2):
+        length = int(up.st.lens(t)[0, 1])
+        for l in range(2):
+            K, V = up.kv64(l)
+            want, _ = full_attention(up.q[l][t][0].astype(np.float64), K[0], V[0], length, scale)
+            check_out(rec.outs[t, l, 0], want, up.wl.dtype, f"{splits} splits of {rows} t={t} l={l}")
+
+
+# a kept-token pass has at most 32 workgroups per pair: slots 1..4 at
+# head_dim 128, 1..2 at 64
+KEPT_MERGE_CASES = [(128, nv) for nv in range(1, 5)] + [(64, nv) for nv in range(1, 3)]
+
+
+@pytest.mark.parametrize("d,nv", KEPT_MERGE_CASES, ids=[f"d{d}-slots{nv}" for d, nv in KEPT_MERGE_CASES])
+def test_kept_merge_slot_counts(monkeypatch, d, nv):
+    up = upload(get_workload("7b-b1").with_overrides(num_layers=3, warmup_steps=1, num_focal=1, head_dim=d),
+                steps=3)
+    cfg = make_config(up)
+    _, P = _rows_for_slots(monkeypatch, cfg, "FASTOCR_SPARSE_ROWS", "sparse_max_splits",
+                           8 if d == 128 else 16, nv, 1)
+    h = fo.fastocr_create(cfg)
+    assert fo.fastocr_get_info(h)["sparse_max_splits"] == P
+    _check_injected_sets(up, h)
 
 
 @SPARSE_VARIANTS
