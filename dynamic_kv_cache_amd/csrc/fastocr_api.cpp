@@ -353,6 +353,7 @@ MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool
   m.out = out;
   m.B = c.batch;
   m.Hq = c.num_q_heads;
+  m.Hkv = c.num_kv_heads;
   m.n_cap = h->n_cap;
   m.max_splits = h->max_splits;
   m.grid_splits = sparse ? h->sparse_splits : h->full_splits;  // states per head

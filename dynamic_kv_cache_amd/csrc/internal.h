@@ -85,7 +85,7 @@ struct MergeParams {
   const int32_t* lens;
   void* out;              // [B, Hq, D] in the io dtype
   float* text_mass;       // [B, Hq] or null
-  int32_t B, Hq, n_cap, max_splits;
+  int32_t B, Hq, Hkv, n_cap, max_splits;
   int32_t grid_splits;    // states per head written by the split pass
   const float* logits;    // [B, Hq, n_stride]
   float* scores;          // [B, n_stride]

@@ -1735,7 +1735,15 @@ template <typename T, int D, int NV>
 __device__ __forceinline__ void kept_merge_body(const MergeParams& p) {
   constexpr int D4 = D / 4;
   constexpr int SL = kMergeThreads / D4;  // lanes sharing an output column
-  const int b = blockIdx.y, h = blockIdx.x;
+  // Workgroup (pair, g) is block pair + (B * Hkv) * g.  Block i runs on XCD
+  // i mod 8, so with B * Hkv a multiple of 8 it shares the XCD (and its L2)
+  // of the pair's kept-token workgroups (blocks pair + (B * Hkv) * split),
+  // and a state line is only ever written and read there.  That measured
+  // faster kept-token passes at 7B-like B=16 (9.3 against 9.5 us with the
+  // heads in (head, sequence) order, 9.8 with every pair's merge one XCD
+  // over) and made no difference at 32B- and 72B-like sizes.
+  const int G = p.Hq / p.Hkv;
+  const int b = blockIdx.x / p.Hkv, h = (blockIdx.x % p.Hkv) * G + blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int d4 = tid / SL, sl = tid % SL;
   const int P = p.grid_splits;
@@ -1924,9 +1932,10 @@ hipError_t launch_split(int dtype, int head_dim, SplitKind kind, const SplitPara
 
 hipError_t launch_kept_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
                              const LaunchTiming& timing) {
-  if (p.grid_splits < 1 || p.grid_splits > 64 || p.score_blocks != 0 || p.text_mass != nullptr)
+  if (p.grid_splits < 1 || p.grid_splits > 64 || p.score_blocks != 0 || p.text_mass != nullptr ||
+      p.Hkv < 1 || p.Hq % p.Hkv != 0)
     return hipErrorInvalidValue;
-  const dim3 grid(p.Hq, p.B), block(kMergeThreads);
+  const dim3 grid(p.B * p.Hkv, p.Hq / p.Hkv), block(kMergeThreads);
   if (dtype == FASTOCR_DTYPE_BF16)
     return head_dim == 128 ? launch(kept_merge_kernel<uint16_t, 128>, grid, block, stream, timing, p)
                            : launch(kept_merge_kernel<uint16_t, 64>, grid, block, stream, timing, p);
