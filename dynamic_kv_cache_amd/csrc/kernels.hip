@@ -921,7 +921,7 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
 // device-coherent state stores, as slow or slower with the workgroups of a
 // pair kept on one XCD and the exchange in its L2, and 3-4x slower with
 // device-scope release/acquire fences, whose L2 write-back dominates.)
-template <typename T, int D, int NW, int TPW>
+template <typename T, int D, int NW, int TPW, bool PAD>
 __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
@@ -936,7 +936,14 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
   __shared__ float s_stat[NW][16][4];
   __shared__ __align__(16) float s_o[NW][HH][OST];
 
+  // Grid x is the pair count, rounded up to a multiple of 8 when it is not
+  // one (PAD: the extra blocks exit at once), so block pair + gridDim.x *
+  // split runs on XCD pair mod 8 for every split.  (The check waits for the
+  // kernel arguments before the rest of them load, so only a padded grid
+  // has it.)
   const int pair = blockIdx.x;
+  if constexpr (PAD)
+    if (pair >= p.B * p.Hkv) return;
   const int split = blockIdx.y;
   const int P = p.grid_splits;
   const int kvh = pair % p.Hkv;
@@ -1735,9 +1742,9 @@ template <typename T, int D, int NV>
 __device__ __forceinline__ void kept_merge_body(const MergeParams& p) {
   constexpr int D4 = D / 4;
   constexpr int SL = kMergeThreads / D4;  // lanes sharing an output column
-  // Workgroup (pair, g) is block pair + (B * Hkv) * g.  Block i runs on XCD
-  // i mod 8, so with B * Hkv a multiple of 8 it shares the XCD (and its L2)
-  // of the pair's kept-token workgroups (blocks pair + (B * Hkv) * split),
+  // Workgroup (pair, g) is block pair + X * g, X = B * Hkv rounded up to a
+  // multiple of 8.  Block i runs on XCD i mod 8, so it shares the XCD (and
+  // its L2) of the pair's kept-token workgroups (blocks pair + X * split),
   // and a state line is only ever written and read there.  That measured
   // faster kept-token passes at 7B-like B=16 (9.3 against 9.5 us with the
   // heads in (head, sequence) order, 9.8 with every pair's merge one XCD
@@ -1805,10 +1812,12 @@ __device__ __forceinline__ void kept_merge_dispatch(const MergeParams& p, int nv
   kept_merge_body<T, D, NV>(p);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAD>
 __global__ __launch_bounds__(kMergeThreads) void kept_merge_kernel(MergeParams p) {
   constexpr int SL = kMergeThreads / (D / 4);
   constexpr int PF = 64 / SL;  // slots per thread for 64 states
+  if constexpr (PAD)
+    if ((int)blockIdx.x >= p.B * p.Hkv) return;  // (grid x rounded up to a multiple of 8)
   kept_merge_dispatch<T, D, PF>(p, (p.grid_splits + SL - 1) / SL);
 }
 
@@ -1906,10 +1915,17 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
   }
 }
 
+// Both kept-token kernels take grid x = the (sequence, KV head) pairs rounded
+// up to a multiple of 8, so a pair's blocks all run on one XCD.
+static int kept_grid_x(int pairs) { return (pairs + 7) / 8 * 8; }
+
 template <typename T, int D>
 static hipError_t launch_kept_t(const SplitParams& p, hipStream_t stream, const LaunchTiming& timing) {
-  const dim3 block(kSplitThreads), grid(p.Hkv * p.B, p.grid_splits);
-  return launch(kept_attn_kernel<T, D, kSplitWaves, tiles_per_wave<T, D>()>, grid, block, stream, timing, p);
+  constexpr int TPW = tiles_per_wave<T, D>();
+  const int pairs = p.Hkv * p.B;
+  const dim3 block(kSplitThreads), grid(kept_grid_x(pairs), p.grid_splits);
+  if (pairs % 8 != 0) return launch(kept_attn_kernel<T, D, kSplitWaves, TPW, true>, grid, block, stream, timing, p);
+  return launch(kept_attn_kernel<T, D, kSplitWaves, TPW, false>, grid, block, stream, timing, p);
 }
 
 hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_t stream,
@@ -1935,12 +1951,20 @@ hipError_t launch_kept_merge(int dtype, int head_dim, const MergeParams& p, hipS
   if (p.grid_splits < 1 || p.grid_splits > 64 || p.score_blocks != 0 || p.text_mass != nullptr ||
       p.Hkv < 1 || p.Hq % p.Hkv != 0)
     return hipErrorInvalidValue;
-  const dim3 grid(p.B * p.Hkv, p.Hq / p.Hkv), block(kMergeThreads);
+  const int pairs = p.B * p.Hkv;
+  const dim3 grid(kept_grid_x(pairs), p.Hq / p.Hkv), block(kMergeThreads);
+  if (pairs % 8 != 0) {
+    if (dtype == FASTOCR_DTYPE_BF16)
+      return head_dim == 128 ? launch(kept_merge_kernel<uint16_t, 128, true>, grid, block, stream, timing, p)
+                             : launch(kept_merge_kernel<uint16_t, 64, true>, grid, block, stream, timing, p);
+    return head_dim == 128 ? launch(kept_merge_kernel<float, 128, true>, grid, block, stream, timing, p)
+                           : launch(kept_merge_kernel<float, 64, true>, grid, block, stream, timing, p);
+  }
   if (dtype == FASTOCR_DTYPE_BF16)
-    return head_dim == 128 ? launch(kept_merge_kernel<uint16_t, 128>, grid, block, stream, timing, p)
-                           : launch(kept_merge_kernel<uint16_t, 64>, grid, block, stream, timing, p);
-  return head_dim == 128 ? launch(kept_merge_kernel<float, 128>, grid, block, stream, timing, p)
-                         : launch(kept_merge_kernel<float, 64>, grid, block, stream, timing, p);
+    return head_dim == 128 ? launch(kept_merge_kernel<uint16_t, 128, false>, grid, block, stream, timing, p)
+                           : launch(kept_merge_kernel<uint16_t, 64, false>, grid, block, stream, timing, p);
+  return head_dim == 128 ? launch(kept_merge_kernel<float, 128, false>, grid, block, stream, timing, p)
+                         : launch(kept_merge_kernel<float, 64, false>, grid, block, stream, timing, p);
 }
 
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, hipStream_t stream,
