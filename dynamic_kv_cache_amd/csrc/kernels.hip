@@ -70,6 +70,7 @@ __device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x4_t, u32x2_t{lo, hi});
 }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -117,6 +118,38 @@ __device__ __forceinline__ void load_slice(uint32_t* dst, const T* row, int grp)
     dst[4 * i + 1] = v.y;
     dst[4 * i + 2] = v.z;
     dst[4 * i + 3] = v.w;
+  }
+}
+
+// Streaming forms of load_slice / load_words (non-temporal loads).
+template <typename T, int KW>
+__device__ __forceinline__ void load_slice_nt(uint32_t* dst, const T* row, int grp) {
+  constexpr int PIECE = 16 / (int)sizeof(T);
+#pragma unroll
+  for (int i = 0; i < KW / 4; ++i) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + (i * 4 + grp) * PIECE));
+    dst[4 * i] = v[0];
+    dst[4 * i + 1] = v[1];
+    dst[4 * i + 2] = v[2];
+    dst[4 * i + 3] = v[3];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_words_nt(uint32_t* dst, const T* src, int nwords) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+  if ((nwords & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < nwords; i += 4) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(s + i));
+      dst[i] = v[0]; dst[i + 1] = v[1]; dst[i + 2] = v[2]; dst[i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < nwords; i += 2) {
+      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(s + i));
+      dst[i] = v[0]; dst[i + 1] = v[1];
+    }
   }
 }
 
@@ -921,7 +954,11 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
 // device-coherent state stores, as slow or slower with the workgroups of a
 // pair kept on one XCD and the exchange in its L2, and 3-4x slower with
 // device-scope release/acquire fences, whose L2 write-back dominates.)
-template <typename T, int D, int NW, int TPW, bool PAD>
+// STREAM: the K/V rows are loaded non-temporally, which the launch plan
+// picks when one step's kept rows exceed the last-level cache (they would
+// not be found there on the next step, and the kept indices and merge
+// states then stay cached).  PAD: see the grid below.
+template <typename T, int D, int NW, int TPW, bool PAD, bool STREAM>
 __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
@@ -1120,10 +1157,15 @@ __global__ __launch_bounds__(NW * 64, kKeptBlocksPerCU) void kept_attn_kernel(Sp
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (tb[u] < rows) {  // uniform over the wave
-        load_slice<T, KW>(kw[u], app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D, grp);
+        const T* kr = app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D;
+        if constexpr (STREAM) load_slice_nt<T, KW>(kw[u], kr, grp);
+        else load_slice<T, KW>(kw[u], kr, grp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          load_words(vw[u][j], (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB, VW);
+        for (int j = 0; j < 4; ++j) {
+          const T* vr = (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB;
+          if constexpr (STREAM) load_words_nt(vw[u][j], vr, VW);
+          else load_words(vw[u][j], vr, VW);
+        }
       }
     }
   };
@@ -1924,8 +1966,11 @@ static hipError_t launch_kept_t(const SplitParams& p, hipStream_t stream, const 
   constexpr int TPW = tiles_per_wave<T, D>();
   const int pairs = p.Hkv * p.B;
   const dim3 block(kSplitThreads), grid(kept_grid_x(pairs), p.grid_splits);
-  if (pairs % 8 != 0) return launch(kept_attn_kernel<T, D, kSplitWaves, TPW, true>, grid, block, stream, timing, p);
-  return launch(kept_attn_kernel<T, D, kSplitWaves, TPW, false>, grid, block, stream, timing, p);
+  if (pairs % 8 != 0)
+    return p.stream_rows ? launch(kept_attn_kernel<T, D, kSplitWaves, TPW, true, true>, grid, block, stream, timing, p)
+                         : launch(kept_attn_kernel<T, D, kSplitWaves, TPW, true, false>, grid, block, stream, timing, p);
+  return p.stream_rows ? launch(kept_attn_kernel<T, D, kSplitWaves, TPW, false, true>, grid, block, stream, timing, p)
+                       : launch(kept_attn_kernel<T, D, kSplitWaves, TPW, false, false>, grid, block, stream, timing, p);
 }
 
 hipError_t launch_kept(int dtype, int head_dim, const SplitParams& p, hipStream_t stream,

@@ -257,6 +257,51 @@ def test_plan_of_benchmark_workloads():
     # focal passes stage their logits at 1920- and 1408-row splits, not at
     # B=1's 128-row splits
     assert (b1["focal_staged"], w8["focal_staged"], b4["focal_staged"], t2["focal_staged"]) == (0, 1, 1, 1)
+    # kept-token passes stream their rows (non-temporal loads) when a step's
+    # kept rows exceed the 256 MiB last-level cache: not at B=1 (69 MB)
+    assert (b1["kept_stream"], w8["kept_stream"], b4["kept_stream"], t2["kept_stream"]) == (0, 1, 1, 1)
+
+
+LAST_LEVEL_CACHE_BYTES = 256 << 20
+
+
+@pytest.mark.parametrize("env", [None, "0", "1"])
+def test_plan_kept_row_streaming(monkeypatch, env):
+    # pruned handles load kept-token rows non-temporally when the non-focal
+    # layers' kept rows at the longest text (k_max image rows + the text
+    # bound) exceed the last-level cache; FASTOCR_KEPT_STREAM overrides; full
+    # handles run no kept-token pass
+    if env is None:
+        monkeypatch.delenv("FASTOCR_KEPT_STREAM", raising=False)
+    else:
+        monkeypatch.setenv("FASTOCR_KEPT_STREAM", env)
+    rng = np.random.default_rng(13)
+    seen = set()
+    for _ in range(300):
+        hkv = int(rng.integers(1, 9))
+        S = int(rng.integers(16, 40_000))
+        n_img = int(rng.integers(1, S + 1))
+        min_img = int(rng.integers(0, n_img + 1))
+        max_text = int(rng.choice([0, int(rng.integers(1, S + 1))]))
+        L = int(rng.integers(2, 81))
+        C = int(rng.integers(1, L + 1))
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        mode = str(rng.choice(["pruned", "full"]))
+        B = int(rng.integers(1, 33))
+        info = _plan(num_layers=L, num_q_heads=hkv * 2, num_kv_heads=hkv, head_dim=d,
+                     batch=B, max_seq_len=S, max_img_tokens=n_img, min_img_tokens=min_img,
+                     max_text_tokens=max_text, tau=0.05, num_focal=C, warmup_steps=1, dtype=dtype, mode=mode)
+        rows = S
+        if min_img > 0:
+            rows = min(rows, info["k_max"] + S - min_img)
+        if max_text > 0:
+            rows = min(rows, info["k_max"] + max_text)
+        step_bytes = (L - C) * B * hkv * rows * 2 * d * (2 if dtype == "bf16" else 4)
+        want = mode == "pruned" and {None: step_bytes > LAST_LEVEL_CACHE_BYTES, "0": False, "1": True}[env]
+        assert info["kept_stream"] == int(want), (info, step_bytes)
+        seen.add(want)
+    assert seen == ({False} if env == "0" else {True, False})
 
 
 LOGIT_STAGE_FLOATS = 8 * (2048 + 16)  # LDS floats a focal pass stages a split's logits in

@@ -100,12 +100,16 @@ def test_topk_bit_exact(tau, n_cap):
 
 # kept-token pass variants (environment, expected plan): each pair's tiles
 # dealt round-robin to the workgroups that fill one wave, merged by the merge
-# kernel, with the focal passes staging their logits in LDS; a few workgroups
-# per pair (several rounds each), the focal passes storing their logits as
-# they are computed; one workgroup per pair (no merge)
+# kernel, rows loaded non-temporally, with the focal passes staging their
+# logits in LDS; a few workgroups per pair (several rounds each), plain row
+# loads, the focal passes storing their logits as they are computed; one
+# workgroup per pair (no merge).  With batches of 4 (16 pairs) and 5 or 1
+# (pair grids padded to a multiple of 8) every kept-token kernel form runs.
 KEPT_VARIANTS = {
-    "kept": ({"FASTOCR_FOCAL_STAGE": "1"}, dict(sparse_direct=0, focal_staged=1)),
-    "kept-few-splits": ({"FASTOCR_SPARSE_ROWS": "1024", "FASTOCR_FOCAL_STAGE": "0"}, dict(focal_staged=0)),
+    "kept": ({"FASTOCR_FOCAL_STAGE": "1", "FASTOCR_KEPT_STREAM": "1"},
+             dict(sparse_direct=0, focal_staged=1, kept_stream=1)),
+    "kept-few-splits": ({"FASTOCR_SPARSE_ROWS": "1024", "FASTOCR_FOCAL_STAGE": "0", "FASTOCR_KEPT_STREAM": "0"},
+                        dict(focal_staged=0, kept_stream=0)),
     "direct": ({"FASTOCR_SPARSE_ROWS": "16384"}, dict(sparse_direct=1)),
 }
 SPARSE_VARIANTS = pytest.mark.parametrize("rows", list(KEPT_VARIANTS), ids=list(KEPT_VARIANTS))
@@ -114,6 +118,7 @@ SPARSE_VARIANTS = pytest.mark.parametrize("rows", list(KEPT_VARIANTS), ids=list(
 def _sparse_variant(monkeypatch, rows):
     monkeypatch.delenv("FASTOCR_SPARSE_ROWS", raising=False)
     monkeypatch.delenv("FASTOCR_FOCAL_STAGE", raising=False)
+    monkeypatch.delenv("FASTOCR_KEPT_STREAM", raising=False)
     for k, v in KEPT_VARIANTS[rows][0].items():
         monkeypatch.setenv(k, v)
 
