@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--workload", default="72b-b8-sweep")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--sigma", type=float, default=None)
+    ap.add_argument("--tp-shard", type=int, default=1, metavar="T",
+                    help="time one tensor-parallel rank's share of the workload: 1/T of its KV and query "
+                         "heads, everything else unchanged (the rank picks from its own heads' scores; the "
+                         "cross-rank score all-reduce a T-GPU run adds per focal layer is not included)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline sample (0 disables it)")
@@ -294,6 +298,11 @@ def main():
     import dynamic_kv_cache_amd as fo
     from workload import DeviceGenerator, get_workload, make_structure
 
+    base = get_workload(args.workload)
+    if args.tp_shard < 1 or base.num_kv_heads % args.tp_shard or base.num_q_heads % args.tp_shard:
+        print(f"--tp-shard {args.tp_shard} must divide the workload's {base.num_kv_heads} KV heads and "
+              f"{base.num_q_heads} query heads", file=sys.stderr)
+        sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     overrides = {}
@@ -301,6 +310,10 @@ def main():
         overrides["tau"] = args.tau
     if args.sigma is not None:
         overrides["sigma"] = args.sigma
+    T = args.tp_shard
+    if T != 1:
+        overrides["num_kv_heads"] = base.num_kv_heads // T
+        overrides["num_q_heads"] = base.num_q_heads // T
     wl = get_workload(args.workload, **overrides)
     st = make_structure(wl)
     gen = DeviceGenerator(wl, st, device=dev)
@@ -788,7 +801,9 @@ def main():
                    "num_focal": wl.num_focal, "warmup_steps": w,
                    "timing": "hip graph replay" if not args.no_graph else "eager",
                    "decode_steps": wl.steps,
-                   "timed_steps": f"{K} per phase, spread over decode steps {t_timed}..{wl.steps - 1}"},
+                   "timed_steps": f"{K} per phase, spread over decode steps {t_timed}..{wl.steps - 1}",
+                   **({"tp_shard": T, "tp_note": f"one rank of {T}: 1/{T} of the heads; the per-focal-layer "
+                       "score all-reduce across ranks is not included"} if T != 1 else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         **extra,

@@ -89,3 +89,11 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+@pytest.mark.parametrize("workload,shard", [("72b-b8-sweep", 3), ("7b-b1", 8), ("32b-b4-longpage", 0)])
+def test_tp_shard_must_divide_the_heads(workload, shard):
+    # a tensor-parallel rank's share needs a whole number of KV and query heads
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
+                        "--tp-shard", str(shard)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "must divide" in r.stderr, r.stderr
