@@ -370,24 +370,31 @@ def test_trajectory_tiny_images(monkeypatch, rows):
     log(f"[tiny images] n={up.st.n_img.tolist()} focal {rec.focal}, worst out {chk.worst_out:.2e}")
 
 
+@pytest.mark.parametrize("stream", ["0", "1"], ids=["plain-rows", "streamed-rows"])
 @pytest.mark.parametrize("name,dtype,head_dim,steps", [
     ("tiny-fp32", "bf16", 64, None),    # bf16 kernels at d = 64
     ("tiny-fp32", "f32", 128, None),    # fp32 kernels at d = 128
+    ("tiny-fp32", "f32", 64, None),     # fp32 kernels at d = 64
     ("7b-b1", "bf16", 64, 10),          # several splits per sequence at d = 64
 ])
-def test_trajectory_other_dtype_and_head_dim(name, dtype, head_dim, steps):
+def test_trajectory_other_dtype_and_head_dim(monkeypatch, name, dtype, head_dim, steps, stream):
+    # every kept-token kernel form: both dtypes and head sizes, plain and
+    # non-temporal row loads
+    monkeypatch.setenv("FASTOCR_KEPT_STREAM", stream)
     wl = get_workload(name).with_overrides(dtype=dtype, head_dim=head_dim)
     if name == "7b-b1":
         wl = wl.with_overrides(num_layers=4, focal_band=(1, 2), num_focal=2, warmup_steps=2)
     up = upload(wl, steps=steps)
     T = up.wl.steps
-    rec = run(up, fo.fastocr_create(make_config(up)), T)
+    h = fo.fastocr_create(make_config(up))
+    assert fo.fastocr_get_info(h)["kept_stream"] == int(stream)
+    rec = run(up, h, T)
     assert rec.status == 0
     chk = Checker(up, rec)
     chk.warmup()
     for t in range(wl.warmup_steps, T):
         chk.pruned_step(t)
-    log(f"[{name} {dtype} d={head_dim}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
+    log(f"[{name} {dtype} d={head_dim} stream {stream}] focal {rec.focal}, worst out {chk.worst_out:.2e}")
 
 
 def test_trajectory_layer0_focal():
