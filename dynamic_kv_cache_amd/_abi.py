@@ -66,7 +66,7 @@ class Info(ctypes.Structure):
         ("sparse_max_splits", c_int32),
         ("sparse_direct", c_int32),
         ("focal_staged", c_int32),
-        ("kept_stream", c_int32),
+        ("stream_rows", c_int32),
         ("profiles", c_int32),
         ("scratch_bytes", c_int64),
     ]

@@ -101,7 +101,7 @@ struct Plan {
   bool valu_full = false;        // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;   // a focal layer followed by a focal layer picks nothing
   bool focal_staged = false;     // focal passes stage a split's logits in LDS
-  bool kept_stream = false;      // kept-token passes load K/V rows non-temporally
+  bool stream_rows = false;      // kept-token and focal passes load K/V rows non-temporally
   int max_splits = 0;            // merge states per head the scratch holds
   // scratch arena: byte offsets of each array, and the total
   size_t o_pstat = 0, o_po = 0, o_logits = 0, o_mz = 0, o_scores = 0, o_warm = 0, o_tm = 0, o_sel = 0,
@@ -162,19 +162,22 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
     P = std::min(std::max(P, 1), kMaxKeptSplits);
     p.sparse_splits = P;
     p.sparse_R = (int)align_up((size_t)((sparse_rows + P - 1) / P), kTileRows);
-    // Kept-token K/V rows are loaded non-temporally when the kept rows of one
-    // step's non-focal layers (at the longest text) exceed the last-level
-    // cache: the next step would not find them there anyway, and streaming
-    // them keeps the kept indices and the merge states cached.  Measured per
-    // step, streaming against plain: 72B-like B=8 2115 against 2173-2178
-    // us, 32B-like B=4 1396 against 1434, 7B-like B=16 500-501 against
-    // 505-506; but 7B-like B=1 (69 MB of kept rows a step) 259.3 against
-    // 257.6-258.3, where plain loads find the previous step's rows in that
-    // cache.  FASTOCR_KEPT_STREAM=0|1 overrides.
+    // Kept-token and focal passes load their K/V rows non-temporally when the
+    // kept rows of one step's non-focal layers (at the longest text) exceed
+    // the last-level cache: the next step would not find them there anyway,
+    // and streaming keeps the kept indices, the merge states and the focal
+    // logits cached.  Measured per step, streamed kept-token rows against
+    // plain: 72B-like B=8 2115 against 2173-2178 us, 32B-like B=4 1396
+    // against 1434, 7B-like B=16 500-501 against 505-506, but 7B-like B=1
+    // (69 MB of kept rows a step) 259.3 against 257.6-258.3, where plain
+    // loads find the previous step's rows in that cache; streamed focal rows
+    // on top, with the cache scrubbed before every step: 72B-like 2053-2057
+    // against 2083-2084 us (the focal pass 84.8 against 91.7), the others
+    // unchanged.  FASTOCR_STREAM_ROWS=0|1 overrides.
     const int64_t row_bytes = 2 * (int64_t)c.head_dim * (c.dtype == FASTOCR_DTYPE_BF16 ? 2 : 4);
     const int64_t step_bytes = (int64_t)(c.num_layers - c.num_focal) * pairs * sparse_rows * row_bytes;
-    const int stream_env = env_int("FASTOCR_KEPT_STREAM", -1);
-    p.kept_stream = stream_env < 0 ? step_bytes > kLastLevelCacheBytes : stream_env != 0;
+    const int stream_env = env_int("FASTOCR_STREAM_ROWS", -1);
+    p.stream_rows = stream_env < 0 ? step_bytes > kLastLevelCacheBytes : stream_env != 0;
   }
   p.skip_dead_picks = env_int("FASTOCR_SKIP_DEAD_PICKS", 1) != 0;
   // A focal pass with long splits keeps a split's image-token logits in LDS
@@ -241,7 +244,7 @@ struct fastocr_handle {
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;         // a focal layer followed by a focal layer picks nothing
   bool focal_staged = false;           // focal passes stage a split's logits in LDS
-  bool kept_stream = false;            // kept-token passes load K/V rows non-temporally
+  bool stream_rows = false;            // kept-token and focal passes load K/V rows non-temporally
   Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
@@ -339,7 +342,7 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   p.rows_per_split = sparse ? h->sparse_R : h->full_R;
   p.grid_splits = sparse ? h->sparse_splits : h->full_splits;
   p.sure_splits = sparse ? 0 : h->full_sure;
-  p.stream_rows = (sparse && h->kept_stream) ? 1 : 0;
+  p.stream_rows = h->stream_rows ? 1 : 0;  // (kept-token and focal kinds only)
   p.scale_log2 = h->scale_log2;
   return p;
 }
@@ -622,7 +625,7 @@ int fastocr::create_handle(const fastocr_config* cfg, void* hip_stream, fastocr_
   h->valu_full = plan.valu_full;
   h->skip_dead_picks = plan.skip_dead_picks;
   h->focal_staged = plan.focal_staged;
-  h->kept_stream = plan.kept_stream;
+  h->stream_rows = plan.stream_rows;
   h->max_splits = plan.max_splits;
   if (env_int("FASTOCR_TRACE", 0) != 0) h->roctx = open_roctx();
   const bool pruned = c.mode == FASTOCR_MODE_PRUNED;
@@ -936,7 +939,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info) {
   info->sparse_max_splits = h->sparse_splits;
   info->sparse_direct = h->sparse_splits <= 1 ? 1 : 0;
   info->focal_staged = h->focal_staged ? 1 : 0;
-  info->kept_stream = h->kept_stream ? 1 : 0;
+  info->stream_rows = h->stream_rows ? 1 : 0;
   info->profiles = h->profiles;
   info->scratch_bytes = (int64_t)h->arena_bytes;
   return FASTOCR_OK;
@@ -956,7 +959,7 @@ int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info*
   info->sparse_max_splits = p.sparse_splits;
   info->sparse_direct = p.sparse_splits <= 1 ? 1 : 0;
   info->focal_staged = p.focal_staged ? 1 : 0;
-  info->kept_stream = p.kept_stream ? 1 : 0;
+  info->stream_rows = p.stream_rows ? 1 : 0;
   info->scratch_bytes = (int64_t)p.arena_bytes;
   return FASTOCR_OK;
 }

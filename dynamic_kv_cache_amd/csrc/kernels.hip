@@ -549,7 +549,10 @@ __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, co
 // (sequence, KV head) pair in 128-row rounds, double-buffered (the next
 // round's loads are issued before the current round is computed), and
 // writes one merge state per split.
-template <typename T, int D, int KIND, int NW, int TPW>
+// STREAM (focal kind only): the K/V rows are loaded non-temporally, which
+// the launch plan picks when one step's kept rows exceed the last-level
+// cache (the logits written here and read by the merge then stay cached).
+template <typename T, int D, int KIND, int NW, int TPW, bool STREAM>
 __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * 64;                   // threads
@@ -569,6 +572,7 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   __shared__ __align__(16) float s_pool[POOL];
   float (*s_o)[HH][OST] = reinterpret_cast<float (*)[HH][OST]>(s_pool);
   static_assert(KIND == KIND_FULL || KIND == KIND_FOCAL, "kept-token passes run kept_attn_kernel");
+  static_assert(!STREAM || KIND == KIND_FOCAL, "full passes load their rows plainly");
 
   // x = split, y = (sequence, KV head) pair, so workgroups dispatched
   // together stream neighbouring rows
@@ -616,10 +620,12 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = r_first + u * NW * kTileRows;
-      load_slice<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
+      if constexpr (STREAM) load_slice_nt<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
+      else load_slice<T, KW>(kw[u], Kb + (size_t)min(tile + col, p.S - 1) * D, grp);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        load_words(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
+        if constexpr (STREAM) load_words_nt(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
+        else load_words(vw[u][j], Vb + (size_t)min(tile + 4 * grp + j, p.S - 1) * D + col * NDB, VW);
     }
   }
 
@@ -808,10 +814,15 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (r0 + u * NW * kTileRows < end) {  // uniform over the wave
-        load_slice<T, KW>(kw[u], app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D, grp);
+        const T* kr = app && pk[u] == cur ? knew : Kb + (size_t)pk[u] * D;
+        if constexpr (STREAM) load_slice_nt<T, KW>(kw[u], kr, grp);
+        else load_slice<T, KW>(kw[u], kr, grp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          load_words(vw[u][j], (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB, VW);
+        for (int j = 0; j < 4; ++j) {
+          const T* vr = (app && pvr[u][j] == cur ? vnew : Vb + (size_t)pvr[u][j] * D) + col * NDB;
+          if constexpr (STREAM) load_words_nt(vw[u][j], vr, VW);
+          else load_words(vw[u][j], vr, VW);
+        }
       }
     }
   };
@@ -1949,9 +1960,11 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
     case KIND_FULL:
       if constexpr (sizeof(T) == 2 && D == 128)
         if (p.valu) return launch(split_valu_kernel<kValuMaxGroup>, grid, block, stream, timing, p);
-      return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, TPW>, grid, block, stream, timing, p);
+      return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, TPW, false>, grid, block, stream, timing, p);
     case KIND_FOCAL:
-      return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, TPW>, grid, block, stream, timing, p);
+      if (p.stream_rows)
+        return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, TPW, true>, grid, block, stream, timing, p);
+      return launch(split_attn_kernel<T, D, KIND_FOCAL, kSplitWaves, TPW, false>, grid, block, stream, timing, p);
     default:
       return hipErrorInvalidValue;
   }

@@ -47,10 +47,11 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
- *   FASTOCR_KEPT_STREAM=0|1 kept-token passes load their K/V rows plainly (0) or
- *                           non-temporally (1); default: non-temporally when
- *                           one step's kept rows of the non-focal layers, at the
- *                           longest text, exceed the 256 MiB last-level cache
+ *   FASTOCR_STREAM_ROWS=0|1 kept-token and focal passes load their K/V rows
+ *                           plainly (0) or non-temporally (1); default:
+ *                           non-temporally when one step's kept rows of the
+ *                           non-focal layers, at the longest text, exceed the
+ *                           256 MiB last-level cache
  *   FASTOCR_FOCAL_STAGE=0|1 focal passes never stage a split's image-token
  *                           logits in LDS (0: stored as they are computed), or
  *                           stage them whenever they fit (1); default: stage
@@ -146,8 +147,8 @@ typedef struct fastocr_info {
                              pair (no merge launch) */
   int32_t focal_staged;   /* 1: focal passes keep a split's image-token logits in LDS and write
                              them once its rows are done (0: as they are computed) */
-  int32_t kept_stream;    /* 1: kept-token passes load their K/V rows non-temporally (one
-                             step's kept rows exceed the 256 MiB last-level cache) */
+  int32_t stream_rows;    /* 1: kept-token and focal passes load their K/V rows non-temporally
+                             (one step's kept rows exceed the 256 MiB last-level cache) */
   int32_t profiles;       /* focal-set picks so far (first warm-up and re-selections) */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
@@ -308,7 +309,7 @@ int fastocr_get_info(fastocr_handle* h, fastocr_info* info);
  * would choose for cfg on a device with num_cu compute units (the FASTOCR_*
  * environment overrides included), written to the plan fields of *info
  * (k_max, rows per split and splits of the full and kept-token passes,
- * sparse_direct, focal_staged, kept_stream, scratch_bytes; the state fields are those of
+ * sparse_direct, focal_staged, stream_rows, scratch_bytes; the state fields are those of
  * a new handle).  Host only: no device is used.  Errors:
  * INVALID_ARG (null, a configuration fastocr_create rejects, num_cu < 1). */
 int fastocr_plan_launch(const fastocr_config* cfg, int32_t num_cu, fastocr_info* info);

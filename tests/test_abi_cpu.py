@@ -259,7 +259,7 @@ def test_plan_of_benchmark_workloads():
     assert (b1["focal_staged"], w8["focal_staged"], b4["focal_staged"], t2["focal_staged"]) == (0, 1, 1, 1)
     # kept-token passes stream their rows (non-temporal loads) when a step's
     # kept rows exceed the 256 MiB last-level cache: not at B=1 (69 MB)
-    assert (b1["kept_stream"], w8["kept_stream"], b4["kept_stream"], t2["kept_stream"]) == (0, 1, 1, 1)
+    assert (b1["stream_rows"], w8["stream_rows"], b4["stream_rows"], t2["stream_rows"]) == (0, 1, 1, 1)
 
 
 LAST_LEVEL_CACHE_BYTES = 256 << 20
@@ -269,12 +269,12 @@ LAST_LEVEL_CACHE_BYTES = 256 << 20
 def test_plan_kept_row_streaming(monkeypatch, env):
     # pruned handles load kept-token rows non-temporally when the non-focal
     # layers' kept rows at the longest text (k_max image rows + the text
-    # bound) exceed the last-level cache; FASTOCR_KEPT_STREAM overrides; full
+    # bound) exceed the last-level cache; FASTOCR_STREAM_ROWS overrides; full
     # handles run no kept-token pass
     if env is None:
-        monkeypatch.delenv("FASTOCR_KEPT_STREAM", raising=False)
+        monkeypatch.delenv("FASTOCR_STREAM_ROWS", raising=False)
     else:
-        monkeypatch.setenv("FASTOCR_KEPT_STREAM", env)
+        monkeypatch.setenv("FASTOCR_STREAM_ROWS", env)
     rng = np.random.default_rng(13)
     seen = set()
     for _ in range(300):
@@ -299,7 +299,7 @@ def test_plan_kept_row_streaming(monkeypatch, env):
             rows = min(rows, info["k_max"] + max_text)
         step_bytes = (L - C) * B * hkv * rows * 2 * d * (2 if dtype == "bf16" else 4)
         want = mode == "pruned" and {None: step_bytes > LAST_LEVEL_CACHE_BYTES, "0": False, "1": True}[env]
-        assert info["kept_stream"] == int(want), (info, step_bytes)
+        assert info["stream_rows"] == int(want), (info, step_bytes)
         seen.add(want)
     assert seen == ({False} if env == "0" else {True, False})
 

@@ -17,8 +17,8 @@ import bench  # noqa: E402
 
 
 @pytest.mark.parametrize("name,cls", [
-    ("void fastocr::split_attn_kernel<unsigned short, 128, 0, 4, 2>(fastocr::SplitParams)", "full_split"),
-    ("void fastocr::split_attn_kernel<unsigned short, 128, 1, 4, 2>(fastocr::SplitParams)", "focal_split"),
+    ("void fastocr::split_attn_kernel<unsigned short, 128, 0, 4, 2, false>(fastocr::SplitParams)", "full_split"),
+    ("void fastocr::split_attn_kernel<unsigned short, 128, 1, 4, 2, true>(fastocr::SplitParams)", "focal_split"),
     ("void fastocr::kept_attn_kernel<unsigned short, 128, 4, 2, false>(fastocr::SplitParams)", "sparse_split"),
     ("void fastocr::merge_kernel<unsigned short, 128>(fastocr::MergeParams)", "merge"),
     ("void fastocr::kept_merge_kernel<float, 64, true>(fastocr::MergeParams)", "merge"),

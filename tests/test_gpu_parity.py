@@ -106,10 +106,10 @@ def test_topk_bit_exact(tau, n_cap):
 # workgroup per pair (no merge).  With batches of 4 (16 pairs) and 5 or 1
 # (pair grids padded to a multiple of 8) every kept-token kernel form runs.
 KEPT_VARIANTS = {
-    "kept": ({"FASTOCR_FOCAL_STAGE": "1", "FASTOCR_KEPT_STREAM": "1"},
-             dict(sparse_direct=0, focal_staged=1, kept_stream=1)),
-    "kept-few-splits": ({"FASTOCR_SPARSE_ROWS": "1024", "FASTOCR_FOCAL_STAGE": "0", "FASTOCR_KEPT_STREAM": "0"},
-                        dict(focal_staged=0, kept_stream=0)),
+    "kept": ({"FASTOCR_FOCAL_STAGE": "1", "FASTOCR_STREAM_ROWS": "1"},
+             dict(sparse_direct=0, focal_staged=1, stream_rows=1)),
+    "kept-few-splits": ({"FASTOCR_SPARSE_ROWS": "1024", "FASTOCR_FOCAL_STAGE": "0", "FASTOCR_STREAM_ROWS": "0"},
+                        dict(focal_staged=0, stream_rows=0)),
     "direct": ({"FASTOCR_SPARSE_ROWS": "16384"}, dict(sparse_direct=1)),
 }
 SPARSE_VARIANTS = pytest.mark.parametrize("rows", list(KEPT_VARIANTS), ids=list(KEPT_VARIANTS))
@@ -118,7 +118,7 @@ SPARSE_VARIANTS = pytest.mark.parametrize("rows", list(KEPT_VARIANTS), ids=list(
 def _sparse_variant(monkeypatch, rows):
     monkeypatch.delenv("FASTOCR_SPARSE_ROWS", raising=False)
     monkeypatch.delenv("FASTOCR_FOCAL_STAGE", raising=False)
-    monkeypatch.delenv("FASTOCR_KEPT_STREAM", raising=False)
+    monkeypatch.delenv("FASTOCR_STREAM_ROWS", raising=False)
     for k, v in KEPT_VARIANTS[rows][0].items():
         monkeypatch.setenv(k, v)
 
@@ -380,14 +380,14 @@ def test_trajectory_tiny_images(monkeypatch, rows):
 def test_trajectory_other_dtype_and_head_dim(monkeypatch, name, dtype, head_dim, steps, stream):
     # every kept-token kernel form: both dtypes and head sizes, plain and
     # non-temporal row loads
-    monkeypatch.setenv("FASTOCR_KEPT_STREAM", stream)
+    monkeypatch.setenv("FASTOCR_STREAM_ROWS", stream)
     wl = get_workload(name).with_overrides(dtype=dtype, head_dim=head_dim)
     if name == "7b-b1":
         wl = wl.with_overrides(num_layers=4, focal_band=(1, 2), num_focal=2, warmup_steps=2)
     up = upload(wl, steps=steps)
     T = up.wl.steps
     h = fo.fastocr_create(make_config(up))
-    assert fo.fastocr_get_info(h)["kept_stream"] == int(stream)
+    assert fo.fastocr_get_info(h)["stream_rows"] == int(stream)
     rec = run(up, h, T)
     assert rec.status == 0
     chk = Checker(up, rec)
