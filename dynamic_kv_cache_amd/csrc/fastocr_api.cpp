@@ -101,7 +101,7 @@ struct Plan {
   bool valu_full = false;        // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;   // a focal layer followed by a focal layer picks nothing
   bool focal_staged = false;     // focal passes stage a split's logits in LDS
-  bool stream_rows = false;      // kept-token and focal passes load K/V rows non-temporally
+  bool stream_rows = false;      // pruned steps' kept-token and focal-layer passes stream their rows
   int max_splits = 0;            // merge states per head the scratch holds
   // scratch arena: byte offsets of each array, and the total
   size_t o_pstat = 0, o_po = 0, o_logits = 0, o_mz = 0, o_scores = 0, o_warm = 0, o_tm = 0, o_sel = 0,
@@ -162,18 +162,19 @@ int make_plan(const fastocr_config& c, int num_cu, Plan& p) {
     P = std::min(std::max(P, 1), kMaxKeptSplits);
     p.sparse_splits = P;
     p.sparse_R = (int)align_up((size_t)((sparse_rows + P - 1) / P), kTileRows);
-    // Kept-token and focal passes load their K/V rows non-temporally when the
-    // kept rows of one step's non-focal layers (at the longest text) exceed
-    // the last-level cache: the next step would not find them there anyway,
-    // and streaming keeps the kept indices, the merge states and the focal
-    // logits cached.  Measured per step, streamed kept-token rows against
+    // In pruned steps the kept-token passes and the focal layers' passes load
+    // their K/V rows non-temporally when the kept rows of one step's
+    // non-focal layers (at the longest text) exceed the last-level cache: the
+    // next step would not find them there anyway, and streaming keeps the
+    // kept indices, the merge states and the focal logits cached.  Measured per step, streamed kept-token rows against
     // plain: 72B-like B=8 2115 against 2173-2178 us, 32B-like B=4 1396
     // against 1434, 7B-like B=16 500-501 against 505-506, but 7B-like B=1
     // (69 MB of kept rows a step) 259.3 against 257.6-258.3, where plain
-    // loads find the previous step's rows in that cache; streamed focal rows
-    // on top, with the cache scrubbed before every step: 72B-like 2053-2057
-    // against 2083-2084 us (the focal pass 84.8 against 91.7), the others
-    // unchanged.  FASTOCR_STREAM_ROWS=0|1 overrides.
+    // loads find the previous step's rows in that cache; streamed focal-layer
+    // rows on top, with the cache scrubbed before every step: 72B-like
+    // 2053-2057 against 2083-2084 us for the focal passes (84.8 against 91.7
+    // us each), 2020-2023 with the full passes of focal layers whose pick is
+    // unused too; the others unchanged.  FASTOCR_STREAM_ROWS=0|1 overrides.
     const int64_t row_bytes = 2 * (int64_t)c.head_dim * (c.dtype == FASTOCR_DTYPE_BF16 ? 2 : 4);
     const int64_t step_bytes = (int64_t)(c.num_layers - c.num_focal) * pairs * sparse_rows * row_bytes;
     const int stream_env = env_int("FASTOCR_STREAM_ROWS", -1);
@@ -244,7 +245,7 @@ struct fastocr_handle {
   bool valu_full = false;              // full passes run the VALU variant (measurement override)
   bool skip_dead_picks = true;         // a focal layer followed by a focal layer picks nothing
   bool focal_staged = false;           // focal passes stage a split's logits in LDS
-  bool stream_rows = false;            // kept-token and focal passes load K/V rows non-temporally
+  bool stream_rows = false;            // pruned steps' kept-token and focal-layer passes stream their rows
   Roctx roctx;                         // FASTOCR_TRACE=1: a named range per call
   const void* app_k = nullptr;         // fastocr_attend_append: the current token's K/V
   const void* app_v = nullptr;
@@ -342,7 +343,7 @@ SplitParams split_params(fastocr_handle* h, const void* q, const void* k, const 
   p.rows_per_split = sparse ? h->sparse_R : h->full_R;
   p.grid_splits = sparse ? h->sparse_splits : h->full_splits;
   p.sure_splits = sparse ? 0 : h->full_sure;
-  p.stream_rows = h->stream_rows ? 1 : 0;  // (kept-token and focal kinds only)
+  p.stream_rows = (sparse && h->stream_rows) ? 1 : 0;  // (full passes: set by run_full)
   p.scale_log2 = h->scale_log2;
   return p;
 }
@@ -382,12 +383,14 @@ MergeParams merge_params(fastocr_handle* h, const int32_t* lens, void* out, bool
 
 // Full attention of one layer: split pass, then the merge (and optionally
 // each head's text mass and, with `scores_dst`, the image-token scores),
-// then with `topk` the selection of the kept set from those scores.
+// then with `topk` the selection of the kept set from those scores.  With
+// `stream` the split pass loads its rows non-temporally.
 int run_full(fastocr_handle* h, const void* q, const void* k, const void* v, const int32_t* lens,
-             void* out, float* text_mass_dst, float* scores_dst, bool topk) {
+             void* out, float* text_mass_dst, float* scores_dst, bool topk, bool stream) {
   const fastocr_config& c = h->cfg;
   const bool focal = scores_dst != nullptr;
   SplitParams sp = split_params(h, q, k, v, lens, out, false);
+  sp.stream_rows = stream ? 1 : 0;
   sp.valu = (h->valu_full && !focal && !h->app_k) ? 1 : 0;
   sp.stage_logits = (focal && h->focal_staged) ? 1 : 0;
   int rc = timed(h, focal ? FASTOCR_KC_FOCAL_SPLIT : FASTOCR_KC_FULL_SPLIT, [&](const LaunchTiming& lt) {
@@ -748,14 +751,14 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
   TraceRange range(&h->roctx, label);
   switch (h->phase) {
     case PHASE_FULL:
-      rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
+      rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false, false);
       break;
     case PHASE_WARMUP: {
       float* tm = h->text_mass + ((size_t)layer * c.warmup_steps + h->warm_pos) * BH;
       float* sc = (h->warm_pos == c.warmup_steps - 1)
                       ? h->warm_scores + (size_t)layer * c.batch * h->n_stride
                       : nullptr;
-      rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc, false);
+      rc = run_full(h, q, k_cache, v_cache, lens, out, tm, sc, false, false);
       if (!rc && sc && layer == 0) {
         hipError_t e = hipMemcpyAsync(h->lens_shadow, lens, (size_t)c.batch * 2 * sizeof(int32_t),
                                       hipMemcpyDeviceToDevice, h->stream);
@@ -767,13 +770,13 @@ static int attend_impl(fastocr_handle* h, int32_t layer, const void* q, const vo
       if (h->is_focal[layer] && h->skip_dead_picks && layer + 1 < c.num_layers && h->is_focal[layer + 1]) {
         // the next layer is focal too and replaces this layer's pick before
         // any layer attends with it: the full pass alone gives every output
-        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false, h->stream_rows);
       } else if (h->is_focal[layer]) {
-        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores, true);
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, h->scores, true, h->stream_rows);
       } else if (h->keeps_all) {
         // tau = 1 keeps every image token: the kept set plus the text is the
         // whole sequence, which the full pass reads without the gather
-        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false);
+        rc = run_full(h, q, k_cache, v_cache, lens, out, nullptr, nullptr, false, false);
       } else {
         rc = run_sparse(h, q, k_cache, v_cache, lens, out);
       }

@@ -66,7 +66,7 @@ struct SplitParams {
   int32_t* status;
   int32_t B, Hq, Hkv, S, n_cap, n_stride, k_stride, max_splits, rows_per_split;
   int32_t grid_splits;    // workgroups launched per (sequence, KV head)
-  int32_t stream_rows;    // kept-token and focal kinds: load the K/V rows non-temporally
+  int32_t stream_rows;    // load the K/V rows non-temporally
   int32_t sure_splits;    // full pass: splits that hold rows for every accepted sequence
   const void* k_new;      // [B, Hkv, D] the current token's key and value, or null: when
   const void* v_new;      // set, cache row len-1 is read from here and written into the

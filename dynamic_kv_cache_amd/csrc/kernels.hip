@@ -549,9 +549,10 @@ __device__ __forceinline__ void topk_sequence(const float* scores, int n_cap, co
 // (sequence, KV head) pair in 128-row rounds, double-buffered (the next
 // round's loads are issued before the current round is computed), and
 // writes one merge state per split.
-// STREAM (focal kind only): the K/V rows are loaded non-temporally, which
-// the launch plan picks when one step's kept rows exceed the last-level
-// cache (the logits written here and read by the merge then stay cached).
+// STREAM: the K/V rows are loaded non-temporally, which pruned steps do when
+// one step's kept rows exceed the last-level cache (the logits written here
+// and read by the merge, and the kept indices and states of the layers
+// around, then stay cached).
 template <typename T, int D, int KIND, int NW, int TPW, bool STREAM>
 __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   constexpr bool BF = sizeof(T) == 2;
@@ -572,7 +573,6 @@ __global__ __launch_bounds__(NW * 64, 2) void split_attn_kernel(SplitParams p) {
   __shared__ __align__(16) float s_pool[POOL];
   float (*s_o)[HH][OST] = reinterpret_cast<float (*)[HH][OST]>(s_pool);
   static_assert(KIND == KIND_FULL || KIND == KIND_FOCAL, "kept-token passes run kept_attn_kernel");
-  static_assert(!STREAM || KIND == KIND_FOCAL, "full passes load their rows plainly");
 
   // x = split, y = (sequence, KV head) pair, so workgroups dispatched
   // together stream neighbouring rows
@@ -1960,6 +1960,8 @@ static hipError_t launch_split_t(SplitKind kind, const SplitParams& p, hipStream
     case KIND_FULL:
       if constexpr (sizeof(T) == 2 && D == 128)
         if (p.valu) return launch(split_valu_kernel<kValuMaxGroup>, grid, block, stream, timing, p);
+      if (p.stream_rows)
+        return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, TPW, true>, grid, block, stream, timing, p);
       return launch(split_attn_kernel<T, D, KIND_FULL, kSplitWaves, TPW, false>, grid, block, stream, timing, p);
     case KIND_FOCAL:
       if (p.stream_rows)

@@ -47,8 +47,9 @@
  *   FASTOCR_KEPT_ALL_AS_FULL=0|1  with tau = 1, non-focal layers run the full
  *                           pass (default 1) or the kept-token pass over
  *                           every image token (0)
- *   FASTOCR_STREAM_ROWS=0|1 kept-token and focal passes load their K/V rows
- *                           plainly (0) or non-temporally (1); default:
+ *   FASTOCR_STREAM_ROWS=0|1 pruned steps' kept-token passes and focal-layer
+ *                           passes load their K/V rows plainly (0) or
+ *                           non-temporally (1); default:
  *                           non-temporally when one step's kept rows of the
  *                           non-focal layers, at the longest text, exceed the
  *                           256 MiB last-level cache
@@ -147,8 +148,9 @@ typedef struct fastocr_info {
                              pair (no merge launch) */
   int32_t focal_staged;   /* 1: focal passes keep a split's image-token logits in LDS and write
                              them once its rows are done (0: as they are computed) */
-  int32_t stream_rows;    /* 1: kept-token and focal passes load their K/V rows non-temporally
-                             (one step's kept rows exceed the 256 MiB last-level cache) */
+  int32_t stream_rows;    /* 1: pruned steps' kept-token and focal-layer passes load their K/V
+                             rows non-temporally (one step's kept rows exceed the 256 MiB
+                             last-level cache) */
   int32_t profiles;       /* focal-set picks so far (first warm-up and re-selections) */
   int64_t scratch_bytes;  /* device bytes owned by the handle */
 } fastocr_info;
