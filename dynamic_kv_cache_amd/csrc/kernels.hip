@@ -21,12 +21,21 @@
 //                      the output (and the head's text-probability mass);
 //                      for focal layers, score workgroups compute the
 //                      head-summed probability of every image token.
+//   kept_merge_kernel  the merge of a kept-token pass (at most 64 states per
+//                      head, no text mass, no scores).
 //   topk_kernel        the k_b highest scores per sequence, ties to the lower
 //                      index, ascending output.
 //   pack_rows_kernel   one-time image-first gather of a multi-span cache.
 // Workgroups never wait on each other inside a kernel: on this GPU a device
 // fence plus an arrival atomic, or the same chain kept inside one XCD's L2,
 // costs as much as the next kernel launch or more.
+//
+// Placement and caching.  Block i runs on XCD i mod 8; the kept-token pass
+// and its merge pad their pair dimension to a multiple of 8, so a pair's
+// blocks and the merge of its heads share one XCD and its L2.  In pruned
+// steps the kept-token and focal-layer passes load their K/V rows
+// non-temporally when a step's kept rows exceed the last-level cache, which
+// then keeps the kept indices, merge states and focal logits instead.
 //
 // Matrix layout on the MFMA units.  A wave consumes 16 cache rows per tile.
 // The GQA query group of one KV head (up to 16 heads, zero padded) is the N
